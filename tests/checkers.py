@@ -1,0 +1,113 @@
+"""Comparison rules between a kernel's results and the oracle's.
+
+Test infrastructure.  Tolerances:
+* V4 logits: |g - o| <= 1e-4 * sum_h |w_h| |q_h . k| + 1e-6 inside the range,
+  the exact -inf bit pattern outside it.
+* Top-k (per row, tau = the largest logit tolerance in the row, theta = the
+  oracle's m-th best score): the indices are distinct, inside [ks, ke), m of
+  them, in ascending order, with exact (-1, -inf) padding; every key whose
+  oracle score exceeds theta + 2 tau is selected and every selected key's
+  oracle score is at least theta - 2 tau (so where the oracle's m-th and
+  (m+1)-th scores are more than 2 tau apart the set is the oracle's exactly);
+  the sorted selected scores match the oracle's sorted top-m within tau; each
+  returned score is within its own tolerance of the oracle's value.
+* V4.1 scores: within 2 bf16 ulp of the oracle, or inside the interval the
+  oracle derives for float32 accumulation in any order; -inf exactly where
+  hidden.
+"""
+
+import numpy as np
+
+NEG_INF_F32_BITS = np.uint32(0xFF800000)
+NEG_INF_BF16_BITS = np.uint16(0xFF80)
+
+
+def logits_tolerance(mag):
+    return 1e-4 * mag + 1e-6
+
+
+def check_logits(gpu, ora, mag, where=""):
+    """gpu: float32 array; ora/mag: float64 arrays of the same shape."""
+    gpu = np.asarray(gpu, dtype=np.float32)
+    valid = np.isfinite(ora)
+    gbits = gpu.view(np.uint32)
+    bad_mask = ~valid & (gbits != NEG_INF_F32_BITS)
+    assert not bad_mask.any(), f"{where}: {int(bad_mask.sum())} masked positions are not -inf"
+    g = gpu.astype(np.float64)
+    assert np.isfinite(g[valid]).all(), f"{where}: non-finite value inside the range"
+    err = np.abs(g[valid] - ora[valid])
+    tol = logits_tolerance(mag[valid])
+    if err.size:
+        worst = int(np.argmax(err - tol))
+        assert (err <= tol).all(), (f"{where}: {int((err > tol).sum())} logits out of tolerance; "
+                                    f"worst err {err[worst]:.3e} tol {tol[worst]:.3e}")
+
+
+def check_topk_rows(g_scores, g_idx, ora_row_scores, ora_row_mag, ks, ke, topk, where=""):
+    """Check one kernel top-k result per row against the oracle's full rows.
+
+    g_scores/g_idx: [R, topk]; ora_row_scores/mag: [R, Skv] float64 oracle
+    logits and magnitudes of those rows; ks/ke: [R].
+    Returns the number of rows where the oracle's boundary gap forced an
+    exact set (for reporting).
+    """
+    g_scores = np.asarray(g_scores, dtype=np.float32)
+    g_idx = np.asarray(g_idx, dtype=np.int64)
+    R, n_kv = ora_row_scores.shape
+    exact_rows = 0
+    for r in range(R):
+        lo = min(max(int(ks[r]), 0), n_kv)
+        hi = min(max(int(ke[r]), 0), n_kv)
+        n = max(0, hi - lo)
+        m = min(topk, n)
+        idx = g_idx[r]
+        sc = g_scores[r]
+        tag = f"{where} row {r}"
+        # padding
+        assert (idx[m:] == -1).all(), f"{tag}: padding indices wrong"
+        assert (sc[m:].view(np.uint32) == NEG_INF_F32_BITS).all(), f"{tag}: padding scores not -inf"
+        if m == 0:
+            continue
+        sel = idx[:m]
+        assert ((sel >= lo) & (sel < hi)).all(), f"{tag}: index outside [ks, ke)"
+        assert (np.diff(sel) > 0).all(), f"{tag}: indices not distinct and ascending"
+        o = ora_row_scores[r, lo:hi]
+        tol_row = logits_tolerance(ora_row_mag[r, lo:hi])
+        tau = float(tol_row.max())
+        # each returned score close to the oracle's value at that key
+        o_sel = ora_row_scores[r, sel]
+        tol_sel = logits_tolerance(ora_row_mag[r, sel])
+        err = np.abs(sc[:m].astype(np.float64) - o_sel)
+        assert (err <= tol_sel).all(), f"{tag}: selected score off by {err.max():.3e}"
+        if m == n:
+            continue
+        order = np.sort(o)[::-1]
+        theta = order[m - 1]
+        must = np.nonzero(o > theta + 2 * tau)[0] + lo
+        assert np.isin(must, sel).all(), f"{tag}: a key well above the threshold was not selected"
+        assert (o_sel >= theta - 2 * tau).all(), f"{tag}: a key well below the threshold was selected"
+        gs = np.sort(sc[:m].astype(np.float64))[::-1]
+        assert np.all(np.abs(gs - order[:m]) <= tau), f"{tag}: sorted top-m scores differ"
+        if order[m - 1] - order[m] > 2 * tau:
+            exact_rows += 1
+    return exact_rows
+
+
+def check_v41(gpu_bits, ora, lo, hi, where=""):
+    """gpu_bits: uint16 [.., G]; ora, lo, hi: float64 (bf16 values or -inf)."""
+    gpu_bits = np.asarray(gpu_bits, dtype=np.uint16)
+    g = (gpu_bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    hidden = ~np.isfinite(ora)
+    assert (gpu_bits[hidden] == NEG_INF_BF16_BITS).all(), f"{where}: hidden positions not bf16 -inf"
+    vis = ~hidden
+    gv, ov = g[vis], ora[vis]
+    assert np.isfinite(gv).all(), f"{where}: non-finite visible score"
+    _, e = np.frexp(np.abs(ov))
+    e = np.where(ov == 0.0, -125, e)
+    ulp = np.ldexp(1.0, np.maximum(e - 8, -133))
+    near = np.abs(gv - ov) <= 2 * ulp
+    inside = (gv >= lo[vis]) & (gv <= hi[vis])
+    ok = near | inside
+    assert ok.all(), (f"{where}: {int((~ok).sum())} V4.1 scores beyond 2 ulp and outside the "
+                      f"accumulation interval")
+    return int((~near & inside).sum())
