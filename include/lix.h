@@ -1,0 +1,167 @@
+/*
+ * lix.h - C ABI of the MI355X (gfx950) lightning-indexer library, liblix.so.
+ *
+ * The DeepSeek-V4 lightning indexer scores every (query t, compressed key s)
+ * pair as
+ *     logits[b,t,s] = sum_h w[t,b,h] * max(0, q[t,b,h,:] . k[s,b,:])
+ * (the DSA indexer form adapted to V4's SBHD layout and causal masking, page
+ * "nemo_automodel.components.models.deepseek_v4.kernels.tilelang_indexer",
+ * module header), keeps only keys inside the query's range and selects the
+ * per-query top-k.  The V4.1 variant rounds to BF16 at two points and takes
+ * a visibility mask (page "nemo_automodel.components.models.deepseek_v41.indexer").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.   Every tensor argument is a device pointer to dense, row-major
+ *           memory on the current HIP device, allocated and owned by the
+ *           caller.  The library allocates nothing, keeps no pointer after
+ *           the call returns and has no mutable global state.
+ * bf16.     bfloat16 tensors travel as raw 16-bit words (const void*).
+ * Alignment. q/k/queries/keys: 16 bytes; float and int32 tensors: 4 bytes;
+ *           bf16 weights and scores: 2 bytes.
+ * Streams.  Work is enqueued on `stream` (a hipStream_t; NULL is the null
+ *           stream) and is asynchronous: results are valid once the caller
+ *           synchronises with that stream.
+ * Ranges.   A query's visible keys are the half-open range [ks[t], ke[t]),
+ *           clamped to [0, Skv].  When ks and ke are both NULL the causal
+ *           range over compressed positions is used: ks = 0 and
+ *           ke = min(Skv, (t+1) / compress_ratio) (page
+ *           "...deepseek_v4.kernels.tilelang_indexer_fwd", section
+ *           _make_causal_cu_seqlens).  Given arrays are int32 [S], shared
+ *           by every batch element (section batched_indexer_fwd).
+ * Errors.   Arguments are validated synchronously before anything is
+ *           enqueued.  On failure the call returns a negative lix_status,
+ *           enqueues nothing and leaves every output untouched:
+ *             LIX_ERR_NULL        a required pointer is NULL;
+ *             LIX_ERR_SHAPE       a size <= 0, topk < 1 or topk > Skv,
+ *                                 compress_ratio < 1, or only one of ks/ke;
+ *             LIX_ERR_UNSUPPORTED heads not a power of two <= 128,
+ *                                 index_dim not a multiple of 16 or above
+ *                                 256, a misaligned pointer, a size whose
+ *                                 element count overflows int64 indexing
+ *                                 limits, or topk above the fused kernel's
+ *                                 on-chip capacity (2048);
+ *             LIX_ERR_DEVICE      a pointer that is not device memory of
+ *                                 the current device (page
+ *                                 "...deepseek_v41.indexer", indexer_scores:
+ *                                 all inputs on the same device);
+ *             LIX_ERR_LAUNCH      the kernel launch itself failed.
+ *           Faults during execution surface at the caller's synchronise.
+ */
+#ifndef LIX_H
+#define LIX_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LIX_OK = 0,
+    LIX_ERR_NULL = -1,
+    LIX_ERR_SHAPE = -2,
+    LIX_ERR_UNSUPPORTED = -3,
+    LIX_ERR_DEVICE = -4,
+    LIX_ERR_LAUNCH = -5
+} lix_status;
+
+/* Largest topk the fused scoring + top-k path (lix_topk with logits == NULL)
+ * keeps on chip. */
+#define LIX_FUSED_TOPK_MAX 2048
+
+/* Human-readable name of a status code; never NULL, static storage. */
+const char* lix_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int lix_version(void);
+
+/*
+ * lix_indexer_logits - masked indexer logits for every (query, key) pair.
+ *
+ * Pages: "...deepseek_v4.kernels.tilelang_indexer_fwd", sections
+ * batched_indexer_fwd (q [S,B,H,D] bf16, k [Skv,B,D] bf16, weights [S,B,H]
+ * fp32 -> [B,S,Skv] fp32; ranges [S] shared by the batch) and clean_logits_
+ * (positions outside a query's range are cleaned; here they hold -inf).
+ *
+ *   q       bf16 [S, B, H, D]      (SBHD)
+ *   k       bf16 [Skv, B, D]
+ *   w       fp32 [S, B, H]
+ *   ks, ke  int32 [S] each, or both NULL for the causal range of compress_ratio
+ *   logits  fp32 [B, S, Skv]  out: the score inside [ks,ke), -inf elsewhere
+ */
+int lix_indexer_logits(const void* q, const void* k, const float* w,
+                       int B, int S, int Skv, int H, int D, int compress_ratio,
+                       const int32_t* ks, const int32_t* ke,
+                       float* logits, hipStream_t stream);
+
+/*
+ * lix_topk - per-query top-k of the indexer scores.
+ *
+ * Page "...deepseek_v4.kernels.tilelang_indexer", sections v4_lighting_indexer
+ * and V4IndexerFunction.forward with topk_indices = None (topk = number of
+ * indices to select; [B,S,topk] fp32 scores; int32 indices).
+ *
+ * logits == NULL: fused path.  Scores are computed from q, k, w (layouts as
+ *   in lix_indexer_logits) and selected on chip; no [B,S,Skv] tensor is
+ *   written.  topk <= LIX_FUSED_TOPK_MAX.
+ * logits != NULL: selection from a caller-provided fp32 [B,S,Skv] tensor
+ *   (for instance the output of lix_indexer_logits); q, k, w, H and D are
+ *   ignored and may be NULL / 0.
+ *
+ * For each (b, t) with n = ke - ks visible keys, the m = min(topk, n) keys
+ * with the largest scores are selected; equal scores are ordered by key
+ * index, the lower index first.  They are written to slots [0, m) in
+ * ascending key-index order; slots [m, topk) hold index -1 and score -inf.
+ *
+ *   scores   fp32  [B, S, topk]  out
+ *   indices  int32 [B, S, topk]  out
+ */
+int lix_topk(const void* q, const void* k, const float* w, const float* logits,
+             int B, int S, int Skv, int H, int D, int compress_ratio,
+             const int32_t* ks, const int32_t* ke, int topk,
+             float* scores, int32_t* indices, hipStream_t stream);
+
+/*
+ * lix_topk_scores - scores at given key indices.
+ *
+ * Page "...deepseek_v4.kernels.tilelang_indexer", section
+ * pytorch_extract_topk_scores (gather along the last dimension) as used by
+ * v4_lighting_indexer with precomputed topk_indices [B,S,topk] int32.
+ *
+ *   logits   fp32  [B, S, Skv]
+ *   indices  int32 [B, S, topk]; an index outside [0, Skv) (such as the -1
+ *            padding of lix_topk) yields -inf
+ *   scores   fp32  [B, S, topk]  out
+ */
+int lix_topk_scores(const float* logits, const int32_t* indices,
+                    int B, int S, int Skv, int topk, float* scores,
+                    hipStream_t stream);
+
+/*
+ * lix_indexer_scores_v41 - V4.1 BF16-rounded scores with a visibility mask.
+ *
+ * Page "...deepseek_v41.indexer", module description (the GEMM output and
+ * each weighted head score are rounded to BF16 before the FP32 head
+ * reduction) and section indexer_scores (BSHD inputs, boolean `allowed`,
+ * BF16 scores; heads a power of two <= 128; index_dim a multiple of 16).
+ * Rounding is round-to-nearest-even.  For every visible (t, s):
+ *     out = bf16( sum_h bf16( w_h * max(0, bf16(q_h . k_s)) ) )
+ * with the sum in fp32; hidden positions hold bf16 -inf (0xFF80).
+ *
+ *   queries  bf16 [B, L, H, D]
+ *   keys     bf16 [B, G, D]
+ *   weights  bf16 [B, L, H]
+ *   allowed  uint8 [B, L, G], 0 = hidden, nonzero = visible
+ *   scores   bf16 [B, L, G]  out
+ */
+int lix_indexer_scores_v41(const void* queries, const void* keys, const void* weights,
+                           const uint8_t* allowed, int B, int L, int G, int H, int D,
+                           void* scores, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIX_H */

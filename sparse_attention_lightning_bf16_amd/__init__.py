@@ -1,0 +1,15 @@
+"""MI355X-native DeepSeek-V4 lightning indexer (forward).
+
+The arithmetic lives in hand-written gfx950 HIP kernels behind the C ABI of
+liblix.so (include/lix.h); this package only binds it.
+"""
+
+from ._lib import LixError, load, status_string, LIB_PATH, LIX_FUSED_TOPK_MAX  # noqa: F401
+from .ops import (  # noqa: F401
+    indexer_logits,
+    topk,
+    topk_from_logits,
+    topk_scores,
+    indexer_scores_v41,
+    v4_lighting_indexer,
+)

@@ -1,0 +1,150 @@
+// C ABI of liblix: argument validation and kernel dispatch.
+//
+// Validation happens on the host before any HIP call: a failing call returns
+// a negative status, enqueues nothing and writes no output.  The only HIP
+// calls made before a launch are the pointer-attribute queries of the
+// device check.
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/lix.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int kVersion = 100;   // 0.1.0
+
+bool is_pow2_le128(int h) { return h >= 1 && h <= 128 && (h & (h - 1)) == 0; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Element counts must stay far inside int64 and the kernels' 32-bit grid limits.
+bool fits(long long a, long long b, long long c = 1, long long d = 1) {
+    const long long lim = 1LL << 40;
+    long long x = a;
+    for (long long f : {b, c, d}) {
+        if (f <= 0 || x > lim / f) return false;
+        x *= f;
+    }
+    return true;
+}
+
+// One workgroup per row or per query block: the row count must fit a 1-D grid.
+bool rows_fit(int B, int S) { return (long long)B * S <= (1LL << 30); }
+
+int check_dims_v4(int B, int S, int Skv, int H, int D, int ratio, const int32_t* ks, const int32_t* ke) {
+    if (B <= 0 || S <= 0 || Skv <= 0 || H <= 0 || D <= 0 || ratio < 1) return LIX_ERR_SHAPE;
+    if ((ks == nullptr) != (ke == nullptr)) return LIX_ERR_SHAPE;
+    if (!is_pow2_le128(H) || D % 16 != 0 || D > 256) return LIX_ERR_UNSUPPORTED;
+    if (!fits(S, B, H, D) || !fits(B, S, Skv) || !fits(Skv, B, D) || !rows_fit(B, S)) return LIX_ERR_UNSUPPORTED;
+    return LIX_OK;
+}
+
+// Every pointer must be device (or managed) memory of the current device.
+int check_device(std::initializer_list<const void*> ptrs) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return LIX_ERR_DEVICE;
+    for (const void* p : ptrs) {
+        if (p == nullptr) continue;
+        hipPointerAttribute_t attr;
+        if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+            (void)hipGetLastError();
+            return LIX_ERR_DEVICE;
+        }
+        if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged) return LIX_ERR_DEVICE;
+        if (attr.device != dev) return LIX_ERR_DEVICE;
+    }
+    return LIX_OK;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? LIX_OK : LIX_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* lix_status_string(int status) {
+    switch (status) {
+        case LIX_OK: return "LIX_OK";
+        case LIX_ERR_NULL: return "LIX_ERR_NULL: a required pointer is NULL";
+        case LIX_ERR_SHAPE: return "LIX_ERR_SHAPE: invalid size, topk, compress_ratio or ks/ke pairing";
+        case LIX_ERR_UNSUPPORTED:
+            return "LIX_ERR_UNSUPPORTED: heads/index_dim/alignment/size/topk outside what the kernels support";
+        case LIX_ERR_DEVICE: return "LIX_ERR_DEVICE: a pointer is not device memory of the current device";
+        case LIX_ERR_LAUNCH: return "LIX_ERR_LAUNCH: kernel launch failed";
+        default: return "LIX_ERR_UNKNOWN";
+    }
+}
+
+int lix_version(void) { return kVersion; }
+
+int lix_indexer_logits(const void* q, const void* k, const float* w, int B, int S, int Skv, int H, int D,
+                       int compress_ratio, const int32_t* ks, const int32_t* ke, float* logits,
+                       hipStream_t stream) {
+    if (!q || !k || !w || !logits) return LIX_ERR_NULL;
+    int st = check_dims_v4(B, S, Skv, H, D, compress_ratio, ks, ke);
+    if (st != LIX_OK) return st;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(w, 4) || !aligned(logits, 4) || !aligned(ks, 4) ||
+        !aligned(ke, 4))
+        return LIX_ERR_UNSUPPORTED;
+    st = check_device({q, k, w, logits, ks, ke});
+    if (st != LIX_OK) return st;
+    lix::LogitsArgs a{q, k, w, B, S, Skv, H, D, compress_ratio, ks, ke, logits, stream};
+    return launch_status(lix::launch_v4_logits(a));
+}
+
+int lix_topk(const void* q, const void* k, const float* w, const float* logits, int B, int S, int Skv, int H,
+             int D, int compress_ratio, const int32_t* ks, const int32_t* ke, int topk, float* scores,
+             int32_t* indices, hipStream_t stream) {
+    if (!scores || !indices) return LIX_ERR_NULL;
+    if (logits == nullptr && (!q || !k || !w)) return LIX_ERR_NULL;
+    if (B <= 0 || S <= 0 || Skv <= 0 || compress_ratio < 1) return LIX_ERR_SHAPE;
+    if ((ks == nullptr) != (ke == nullptr)) return LIX_ERR_SHAPE;
+    if (topk < 1 || topk > Skv) return LIX_ERR_SHAPE;
+    if (!fits(B, S, Skv) || !fits(B, S, topk) || !rows_fit(B, S)) return LIX_ERR_UNSUPPORTED;
+    if (!aligned(scores, 4) || !aligned(indices, 4) || !aligned(ks, 4) || !aligned(ke, 4) || !aligned(logits, 4))
+        return LIX_ERR_UNSUPPORTED;
+    if (logits != nullptr) {
+        int st = check_device({logits, ks, ke, scores, indices});
+        if (st != LIX_OK) return st;
+        lix::TopkArgs a{logits, B, S, Skv, compress_ratio, topk, ks, ke, scores, indices, stream};
+        return launch_status(lix::launch_topk_rows(a));
+    }
+    int st = check_dims_v4(B, S, Skv, H, D, compress_ratio, ks, ke);
+    if (st != LIX_OK) return st;
+    if (topk > LIX_FUSED_TOPK_MAX || Skv > 65536 || !lix::fused_supported(H, D, topk)) return LIX_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(w, 4)) return LIX_ERR_UNSUPPORTED;
+    st = check_device({q, k, w, ks, ke, scores, indices});
+    if (st != LIX_OK) return st;
+    lix::FusedArgs a{q, k, w, B, S, Skv, H, D, compress_ratio, topk, ks, ke, scores, indices, stream};
+    return launch_status(lix::launch_fused_topk(a));
+}
+
+int lix_topk_scores(const float* logits, const int32_t* indices, int B, int S, int Skv, int topk, float* scores,
+                    hipStream_t stream) {
+    if (!logits || !indices || !scores) return LIX_ERR_NULL;
+    if (B <= 0 || S <= 0 || Skv <= 0 || topk < 1) return LIX_ERR_SHAPE;
+    if (!fits(B, S, Skv) || !fits(B, S, topk) || (long long)B * S * topk > (1LL << 38)) return LIX_ERR_UNSUPPORTED;
+    if (!aligned(logits, 4) || !aligned(indices, 4) || !aligned(scores, 4)) return LIX_ERR_UNSUPPORTED;
+    int st = check_device({logits, indices, scores});
+    if (st != LIX_OK) return st;
+    lix::GatherArgs a{logits, indices, B, S, Skv, topk, scores, stream};
+    return launch_status(lix::launch_gather(a));
+}
+
+int lix_indexer_scores_v41(const void* queries, const void* keys, const void* weights, const uint8_t* allowed,
+                           int B, int L, int G, int H, int D, void* scores, hipStream_t stream) {
+    if (!queries || !keys || !weights || !allowed || !scores) return LIX_ERR_NULL;
+    if (B <= 0 || L <= 0 || G <= 0 || H <= 0 || D <= 0) return LIX_ERR_SHAPE;
+    if (!is_pow2_le128(H) || D % 16 != 0 || D > 256) return LIX_ERR_UNSUPPORTED;
+    if (!fits(B, L, H, D) || !fits(B, L, G) || !fits(B, G, D) || !rows_fit(B, L)) return LIX_ERR_UNSUPPORTED;
+    if (!aligned(queries, 16) || !aligned(keys, 16) || !aligned(weights, 2) || !aligned(scores, 2))
+        return LIX_ERR_UNSUPPORTED;
+    int st = check_device({queries, keys, weights, allowed, scores});
+    if (st != LIX_OK) return st;
+    lix::V41Args a{queries, keys, weights, allowed, B, L, G, H, D, scores, stream};
+    return launch_status(lix::launch_v41_scores(a));
+}
+
+}  // extern "C"

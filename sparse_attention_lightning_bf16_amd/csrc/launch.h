@@ -1,0 +1,74 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernels.
+// Arguments have been validated by the caller; launchers only enqueue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lix {
+
+// index_dim rounded up to the compiled fragment depth (zero-padded in the kernels).
+inline int padded_dim(int D) { return D <= 32 ? 32 : D <= 64 ? 64 : D <= 128 ? 128 : 256; }
+
+struct LogitsArgs {
+    const void* q;
+    const void* k;
+    const float* w;
+    int B, S, Skv, H, D, ratio;
+    const int32_t* ks;
+    const int32_t* ke;
+    float* logits;
+    hipStream_t stream;
+};
+
+struct TopkArgs {
+    const float* logits;   // [B,S,Skv]
+    int B, S, Skv, ratio, topk;
+    const int32_t* ks;
+    const int32_t* ke;
+    float* scores;
+    int32_t* indices;
+    hipStream_t stream;
+};
+
+struct FusedArgs {
+    const void* q;
+    const void* k;
+    const float* w;
+    int B, S, Skv, H, D, ratio, topk;
+    const int32_t* ks;
+    const int32_t* ke;
+    float* scores;
+    int32_t* indices;
+    hipStream_t stream;
+};
+
+struct GatherArgs {
+    const float* logits;
+    const int32_t* indices;
+    int B, S, Skv, topk;
+    float* scores;
+    hipStream_t stream;
+};
+
+struct V41Args {
+    const void* queries;
+    const void* keys;
+    const void* weights;
+    const uint8_t* allowed;
+    int B, L, G, H, D;
+    void* scores;
+    hipStream_t stream;
+};
+
+hipError_t launch_v4_logits(const LogitsArgs& p);
+hipError_t launch_topk_rows(const TopkArgs& p);
+hipError_t launch_fused_topk(const FusedArgs& p);
+hipError_t launch_gather(const GatherArgs& p);
+hipError_t launch_v41_scores(const V41Args& p);
+
+// Nonzero when the fused kernel can hold topk candidates per query on chip
+// for this head count and index_dim.
+int fused_supported(int H, int D, int topk);
+
+}  // namespace lix

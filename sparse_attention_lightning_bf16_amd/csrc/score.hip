@@ -1,0 +1,333 @@
+// Scoring kernels: V4 masked fp32 logits (materialized) and V4.1 BF16 scores.
+//
+// V4 (page "...deepseek_v4.kernels.tilelang_indexer_fwd", batched_indexer_fwd
+// and clean_logits_):
+//     logits[b,t,s] = sum_h w[t,b,h] * max(0, q[t,b,h,:] . k[s,b,:])  for s in [ks,ke)
+//     logits[b,t,s] = -inf                                            otherwise
+// V4.1 (page "...deepseek_v41.indexer", module description, indexer_scores):
+//     out[b,t,s] = bf16( sum_h bf16( w[b,t,h] * max(0, bf16(q[b,t,h,:] . k[b,s,:])) ) )
+// where allowed[b,t,s], bf16 -inf elsewhere; the head sum is fp32.
+//
+// One workgroup = 4 waves = QB consecutive queries of one batch element.
+// Key stages [s0, s0+64) that lie outside every range of the workgroup are
+// never computed (causal tile skip); their logits are filled with -inf.
+#include "score_core.h"
+#include "launch.h"
+
+namespace lix {
+
+template <class T>
+__device__ __forceinline__ void load_weights_f32(float (&wr)[T::NRT][16], const float* __restrict__ w, long w_t,
+                                                 long w_b, int b, int tq0, int S, int lane) {
+    const int hf = lane >> 5;
+#pragma unroll
+    for (int r = 0; r < T::NRT; ++r)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int row = 32 * r + c_row(i, hf);
+            const int t = tq0 + row / T::H, h = row % T::H;
+            wr[r][i] = (t < S) ? w[(long)t * w_t + (long)b * w_b + h] : 0.0f;
+        }
+}
+
+// ---------------------------------------------------------------- V4 logits
+
+template <int H, int DP>
+__global__ __launch_bounds__(256) void v4_logits_kernel(InLayout L, const float* __restrict__ w, int B, int S,
+                                                        int skv, int ratio, const int32_t* __restrict__ ks,
+                                                        const int32_t* __restrict__ ke, float* __restrict__ out) {
+    using T = Tiling<H, DP>;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][T::STAGE_BYTES];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5;
+    const int nqb = (S + T::QB - 1) / T::QB;
+    const int b = blockIdx.x % B;
+    const int qb = nqb - 1 - (int)(blockIdx.x / B);      // longest causal rows first
+    const int t0 = qb * T::QB;
+    const int tq0 = t0 + wave * T::QW;                    // first query of this wave
+
+    // Key span of the workgroup, in whole stages.
+    int wg_lo = skv, wg_hi = 0;
+    for (int j = 0; j < T::QB; ++j) {
+        int lo, hi;
+        key_range(ks, ke, t0 + j, S, skv, ratio, lo, hi);
+        if (hi > lo) { wg_lo = min(wg_lo, lo); wg_hi = max(wg_hi, hi); }
+    }
+    const int tile_lo = (wg_hi > wg_lo) ? wg_lo / T::KT : 0;
+    const int tile_hi = (wg_hi > wg_lo) ? (wg_hi + T::KT - 1) / T::KT : 0;
+    const int span_lo = tile_lo * T::KT, span_hi = min(skv, tile_hi * T::KT);
+
+    // -inf outside the staged span (no query of the workgroup sees those keys).
+    for (int j = 0; j < T::QB; ++j) {
+        const int t = t0 + j;
+        if (t >= S) break;
+        float* row = out + ((long)b * S + t) * skv;
+        fill_neg_inf(row, span_lo, tid, T::THREADS);
+        fill_neg_inf(row + span_hi, skv - span_hi, tid, T::THREADS);
+    }
+    const int ntile = tile_hi - tile_lo;
+    if (ntile <= 0) return;
+
+    // This lane's queries: ranges per slot.
+    int lo_s[T::QW], hi_s[T::QW];
+    int wave_lo = skv, wave_hi = 0;
+#pragma unroll
+    for (int j = 0; j < T::QW; ++j) {
+        key_range(ks, ke, slot_query<T>(tq0, j, hf), S, skv, ratio, lo_s[j], hi_s[j]);
+    }
+    for (int j = 0; j < T::QW; ++j) {
+        int lo, hi;
+        key_range(ks, ke, tq0 + j, S, skv, ratio, lo, hi);
+        if (hi > lo) { wave_lo = min(wave_lo, lo); wave_hi = max(wave_hi, hi); }
+    }
+
+    bf16x8 a[T::NRT][T::NSTEP];
+    load_q_frags<T>(a, L, b, tq0, S, lane);
+    float wr[T::NRT][16];
+    load_weights_f32<T>(wr, w, (long)B * H, H, b, tq0, S, lane);
+
+    u32x4 pf[T::CPT];
+    load_k_stage<T>(pf, L, b, span_lo, skv, tid);
+    store_k_stage<T>(lds[0], pf, tid);
+    __syncthreads();
+
+    for (int it = 0; it < ntile; ++it) {
+        const int s0 = (tile_lo + it) * T::KT;
+        const bool more = it + 1 < ntile;
+        if (more) load_k_stage<T>(pf, L, b, s0 + T::KT, skv, tid);
+        const uint8_t* stage = lds[it & 1];
+        const bool active = (s0 < wave_hi) && (s0 + T::KT > wave_lo);
+
+        float part[T::NCB][T::QW];
+#pragma unroll
+        for (int cb = 0; cb < T::NCB; ++cb) {
+#pragma unroll
+            for (int j = 0; j < T::QW; ++j) part[cb][j] = 0.0f;
+            if (active) {
+                f32x16 acc[T::NRT];
+                mfma_block<T>(acc, a, stage, cb, lane);
+#pragma unroll
+                for (int r = 0; r < T::NRT; ++r)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int j = T::slot(r, i);
+                        part[cb][j] = fmaf(wr[r][i], fmaxf(acc[r][i], 0.0f), part[cb][j]);
+                    }
+                if constexpr (H >= 8) {
+#pragma unroll
+                    for (int j = 0; j < T::QW; ++j) part[cb][j] = xor32_add(part[cb][j]);
+                }
+            }
+        }
+
+        if constexpr (H >= 8) {
+            // Both halves hold full sums; the lower half writes column block 0,
+            // the upper half column block 1: 64 consecutive keys per query.
+            const int s = s0 + lane;
+#pragma unroll
+            for (int j = 0; j < T::QW; ++j) {
+                const int t = tq0 + j;
+                if (t < S && s < skv) {
+                    const float v = hf ? part[1][j] : part[0][j];
+                    out[((long)b * S + t) * skv + s] = (s >= lo_s[j] && s < hi_s[j]) ? v : neg_inf();
+                }
+            }
+        } else {
+#pragma unroll
+            for (int cb = 0; cb < T::NCB; ++cb) {
+                const int s = s0 + 32 * cb + (lane & 31);
+#pragma unroll
+                for (int j = 0; j < T::QW; ++j) {
+                    if ((j % (2 * T::half_step())) >= T::half_step()) continue;   // slot owned via hf
+                    const int t = slot_query<T>(tq0, j, hf);
+                    if (t < S && s < skv)
+                        out[((long)b * S + t) * skv + s] =
+                            (s >= lo_s[j] && s < hi_s[j]) ? part[cb][j] : neg_inf();
+                }
+            }
+        }
+
+        if (more) store_k_stage<T>(lds[(it + 1) & 1], pf, tid);
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------- V4.1 scores
+
+template <int H, int DP>
+__global__ __launch_bounds__(256) void v41_scores_kernel(InLayout L, const uint16_t* __restrict__ wts,
+                                                         const uint8_t* __restrict__ allowed, int B, int Lq,
+                                                         int G, uint16_t* __restrict__ out) {
+    using T = Tiling<H, DP>;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][T::STAGE_BYTES];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5;
+    const int nqb = (Lq + T::QB - 1) / T::QB;
+    const int b = blockIdx.x % B;
+    const int qb = nqb - 1 - (int)(blockIdx.x / B);
+    const int t0 = qb * T::QB;
+    const int tq0 = t0 + wave * T::QW;
+    const int ntile = (G + T::KT - 1) / T::KT;
+
+    bf16x8 a[T::NRT][T::NSTEP];
+    load_q_frags<T>(a, L, b, tq0, Lq, lane);
+    float wr[T::NRT][16];
+#pragma unroll
+    for (int r = 0; r < T::NRT; ++r)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int row = 32 * r + c_row(i, hf);
+            const int t = tq0 + row / H, h = row % H;
+            wr[r][i] = (t < Lq) ? bf16_to_f32(wts[((long)b * Lq + t) * H + h]) : 0.0f;
+        }
+
+    u32x4 pf[T::CPT];
+    load_k_stage<T>(pf, L, b, 0, G, tid);
+    store_k_stage<T>(lds[0], pf, tid);
+    __syncthreads();
+
+    const uint16_t kNegInfBf16 = 0xff80u;
+    for (int it = 0; it < ntile; ++it) {
+        const int s0 = it * T::KT;
+        const bool more = it + 1 < ntile;
+        if (more) load_k_stage<T>(pf, L, b, s0 + T::KT, G, tid);
+        const uint8_t* stage = lds[it & 1];
+
+        // Visibility of this lane's keys for each of its queries.
+        bool vis[T::NCB][T::QW];
+        bool any = false;
+#pragma unroll
+        for (int cb = 0; cb < T::NCB; ++cb) {
+            const int s = s0 + 32 * cb + (lane & 31);
+#pragma unroll
+            for (int j = 0; j < T::QW; ++j) {
+                const int t = slot_query<T>(tq0, j, hf);
+                vis[cb][j] = (t < Lq && s < G) ? (allowed[((long)b * Lq + t) * G + s] != 0) : false;
+                any |= vis[cb][j];
+            }
+        }
+        const bool active = __ballot(any) != 0ull;
+
+        float part[T::NCB][T::QW];
+#pragma unroll
+        for (int cb = 0; cb < T::NCB; ++cb) {
+#pragma unroll
+            for (int j = 0; j < T::QW; ++j) part[cb][j] = 0.0f;
+            if (active) {
+                f32x16 acc[T::NRT];
+                mfma_block<T>(acc, a, stage, cb, lane);
+#pragma unroll
+                for (int r = 0; r < T::NRT; ++r)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int j = T::slot(r, i);
+                        const float rr = round_bf16(fmaxf(acc[r][i], 0.0f));   // bf16(d), ReLU commutes
+                        part[cb][j] += round_bf16(wr[r][i] * rr);              // exact product, then bf16
+                    }
+                if constexpr (H >= 8) {
+#pragma unroll
+                    for (int j = 0; j < T::QW; ++j) part[cb][j] = xor32_add(part[cb][j]);
+                }
+            }
+        }
+
+#pragma unroll
+        for (int cb = 0; cb < T::NCB; ++cb) {
+            const int s = s0 + 32 * cb + (lane & 31);
+#pragma unroll
+            for (int j = 0; j < T::QW; ++j) {
+                if constexpr (H >= 8) {
+                    if (hf != cb) continue;            // lower half stores block 0, upper block 1
+                } else {
+                    if ((j % (2 * T::half_step())) >= T::half_step()) continue;
+                }
+                const int t = slot_query<T>(tq0, j, hf);
+                if (t < Lq && s < G) {
+                    out[((long)b * Lq + t) * G + s] = vis[cb][j] ? bf16_bits(part[cb][j]) : kNegInfBf16;
+                }
+            }
+        }
+
+        if (more) store_k_stage<T>(lds[(it + 1) & 1], pf, tid);
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------- launchers
+
+template <int H, int DP>
+static hipError_t launch_v4_logits_t(const LogitsArgs& p) {
+    using T = Tiling<H, DP>;
+    InLayout L{static_cast<const uint16_t*>(p.q), (long)p.B * H * p.D, (long)H * p.D,
+               static_cast<const uint16_t*>(p.k), (long)p.B * p.D, (long)p.D, p.D};
+    const int nqb = (p.S + T::QB - 1) / T::QB;
+    dim3 grid((unsigned)((long)nqb * p.B));
+    hipLaunchKernelGGL((v4_logits_kernel<H, DP>), grid, dim3(T::THREADS), 0, p.stream, L, p.w, p.B, p.S, p.Skv,
+                       p.ratio, p.ks, p.ke, p.logits);
+    return hipGetLastError();
+}
+
+template <int H, int DP>
+static hipError_t launch_v41_t(const V41Args& p) {
+    using T = Tiling<H, DP>;
+    InLayout L{static_cast<const uint16_t*>(p.queries), (long)H * p.D, (long)p.L * H * p.D,
+               static_cast<const uint16_t*>(p.keys), (long)p.D, (long)p.G * p.D, p.D};
+    const int nqb = (p.L + T::QB - 1) / T::QB;
+    dim3 grid((unsigned)((long)nqb * p.B));
+    hipLaunchKernelGGL((v41_scores_kernel<H, DP>), grid, dim3(T::THREADS), 0, p.stream, L,
+                       static_cast<const uint16_t*>(p.weights), p.allowed, p.B, p.L, p.G,
+                       static_cast<uint16_t*>(p.scores));
+    return hipGetLastError();
+}
+
+template <int H>
+static hipError_t dispatch_dp_logits(const LogitsArgs& p) {
+    switch (padded_dim(p.D)) {
+        case 32: return launch_v4_logits_t<H, 32>(p);
+        case 64: return launch_v4_logits_t<H, 64>(p);
+        case 128: return launch_v4_logits_t<H, 128>(p);
+        case 256: return launch_v4_logits_t<H, 256>(p);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int H>
+static hipError_t dispatch_dp_v41(const V41Args& p) {
+    switch (padded_dim(p.D)) {
+        case 32: return launch_v41_t<H, 32>(p);
+        case 64: return launch_v41_t<H, 64>(p);
+        case 128: return launch_v41_t<H, 128>(p);
+        case 256: return launch_v41_t<H, 256>(p);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_v4_logits(const LogitsArgs& p) {
+    switch (p.H) {
+        case 1: return dispatch_dp_logits<1>(p);
+        case 2: return dispatch_dp_logits<2>(p);
+        case 4: return dispatch_dp_logits<4>(p);
+        case 8: return dispatch_dp_logits<8>(p);
+        case 16: return dispatch_dp_logits<16>(p);
+        case 32: return dispatch_dp_logits<32>(p);
+        case 64: return dispatch_dp_logits<64>(p);
+        case 128: return dispatch_dp_logits<128>(p);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_v41_scores(const V41Args& p) {
+    switch (p.H) {
+        case 1: return dispatch_dp_v41<1>(p);
+        case 2: return dispatch_dp_v41<2>(p);
+        case 4: return dispatch_dp_v41<4>(p);
+        case 8: return dispatch_dp_v41<8>(p);
+        case 16: return dispatch_dp_v41<16>(p);
+        case 32: return dispatch_dp_v41<32>(p);
+        case 64: return dispatch_dp_v41<64>(p);
+        case 128: return dispatch_dp_v41<128>(p);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace lix

@@ -1,0 +1,161 @@
+"""Python face of liblix: the four C entry points plus the pages' entry point.
+
+Every function only checks and marshals arguments (shapes, dtypes,
+contiguity, output allocation, the current HIP stream) and calls the C ABI;
+all arithmetic runs in the HIP kernels.  Inputs must be contiguous tensors on
+the current GPU.
+"""
+
+import torch
+
+from . import _lib
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t, name, dtype, ndim):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ranges(ks, ke, S):
+    if (ks is None) != (ke is None):
+        raise ValueError("cu_seqlen_ks and cu_seqlen_ke must be given together")
+    if ks is not None:
+        _need(ks, "cu_seqlen_ks", torch.int32, 1)
+        _need(ke, "cu_seqlen_ke", torch.int32, 1)
+        if ks.shape[0] != S or ke.shape[0] != S:
+            raise ValueError("cu_seqlen_ks/ke must have seqlen entries")
+    return ks, ke
+
+
+def _v4_shapes(q, k, w):
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 3)
+    _need(w, "weights", torch.float32, 3)
+    S, B, H, D = q.shape
+    Skv = k.shape[0]
+    if k.shape[1] != B or k.shape[2] != D:
+        raise ValueError(f"k must be [seqlen_kv, {B}, {D}], got {tuple(k.shape)}")
+    if tuple(w.shape) != (S, B, H):
+        raise ValueError(f"weights must be [{S}, {B}, {H}], got {tuple(w.shape)}")
+    if k.device != q.device or w.device != q.device:
+        raise ValueError("q, k and weights must be on the same device")
+    return S, B, H, D, Skv
+
+
+def indexer_logits(q, k, weights, compress_ratio, cu_seqlen_ks=None, cu_seqlen_ke=None, out=None):
+    """lix_indexer_logits: q [S,B,H,D] bf16, k [Skv,B,D] bf16, weights [S,B,H] fp32 -> [B,S,Skv] fp32.
+
+    Positions outside [ks, ke) (causal [0, (t+1)//compress_ratio) when no
+    ranges are given) hold -inf.
+    """
+    S, B, H, D, Skv = _v4_shapes(q, k, weights)
+    ks, ke = _ranges(cu_seqlen_ks, cu_seqlen_ke, S)
+    if out is None:
+        out = torch.empty(B, S, Skv, dtype=torch.float32, device=q.device)
+    else:
+        _need(out, "out", torch.float32, 3)
+        if tuple(out.shape) != (B, S, Skv):
+            raise ValueError("out must be [B, S, Skv]")
+    st = _lib.load().lix_indexer_logits(q.data_ptr(), k.data_ptr(), weights.data_ptr(), B, S, Skv, H, D,
+                                        int(compress_ratio), _ptr(ks), _ptr(ke), out.data_ptr(),
+                                        _stream(q.device))
+    _lib.check(st, "lix_indexer_logits")
+    return out
+
+
+def topk(q, k, weights, compress_ratio, topk, logits=None, cu_seqlen_ks=None, cu_seqlen_ke=None):
+    """lix_topk.  With logits=None: fused scoring + top-k from q, k, weights.
+    With logits [B,S,Skv] fp32: top-k of the given logits (q, k, weights may
+    be None).  Ranges are causal for compress_ratio unless cu_seqlen_ks/ke
+    are given.
+
+    Returns (scores fp32 [B,S,topk], indices int32 [B,S,topk]); selected keys
+    in ascending index order, rows with fewer visible keys padded (-inf, -1).
+    """
+    if logits is not None:
+        _need(logits, "logits", torch.float32, 3)
+        B, S, Skv = logits.shape
+        H = D = 0
+        dev = logits.device
+        qp = kp = wp = None
+    else:
+        S, B, H, D, Skv = _v4_shapes(q, k, weights)
+        dev = q.device
+        qp, kp, wp = q.data_ptr(), k.data_ptr(), weights.data_ptr()
+    ks, ke = _ranges(cu_seqlen_ks, cu_seqlen_ke, S)
+    scores = torch.empty(B, S, topk, dtype=torch.float32, device=dev)
+    indices = torch.empty(B, S, topk, dtype=torch.int32, device=dev)
+    st = _lib.load().lix_topk(qp, kp, wp, None if logits is None else logits.data_ptr(), B, S, Skv, H, D,
+                              int(compress_ratio), _ptr(ks), _ptr(ke), int(topk), scores.data_ptr(),
+                              indices.data_ptr(), _stream(dev))
+    _lib.check(st, "lix_topk")
+    return scores, indices
+
+
+def topk_from_logits(logits, compress_ratio, k, cu_seqlen_ks=None, cu_seqlen_ke=None):
+    """lix_topk over materialized logits [B,S,Skv] fp32 (k = number of keys to select)."""
+    return topk(None, None, None, compress_ratio, k, logits=logits, cu_seqlen_ks=cu_seqlen_ks,
+                cu_seqlen_ke=cu_seqlen_ke)
+
+
+def topk_scores(logits, topk_indices):
+    """lix_topk_scores: logits [B,S,Skv] fp32 gathered at topk_indices [B,S,topk] int32 (-inf outside [0,Skv))."""
+    _need(logits, "logits", torch.float32, 3)
+    _need(topk_indices, "topk_indices", torch.int32, 3)
+    B, S, Skv = logits.shape
+    if topk_indices.shape[0] != B or topk_indices.shape[1] != S:
+        raise ValueError("topk_indices must be [B, S, topk]")
+    tk = topk_indices.shape[2]
+    out = torch.empty(B, S, tk, dtype=torch.float32, device=logits.device)
+    st = _lib.load().lix_topk_scores(logits.data_ptr(), topk_indices.data_ptr(), B, S, Skv, tk, out.data_ptr(),
+                                     _stream(logits.device))
+    _lib.check(st, "lix_topk_scores")
+    return out
+
+
+def indexer_scores_v41(queries, keys, weights, allowed):
+    """lix_indexer_scores_v41: queries [B,L,H,D], keys [B,G,D], weights [B,L,H] (bf16),
+    allowed [B,L,G] bool -> bf16 [B,L,G] (-inf where hidden)."""
+    _need(queries, "queries", torch.bfloat16, 4)
+    _need(keys, "keys", torch.bfloat16, 3)
+    _need(weights, "weights", torch.bfloat16, 3)
+    _need(allowed, "allowed", torch.bool, 3)
+    B, L, H, D = queries.shape
+    G = keys.shape[1]
+    if tuple(keys.shape) != (B, G, D) or tuple(weights.shape) != (B, L, H) or tuple(allowed.shape) != (B, L, G):
+        raise ValueError("shapes must be queries [B,L,H,D], keys [B,G,D], weights [B,L,H], allowed [B,L,G]")
+    out = torch.empty(B, L, G, dtype=torch.bfloat16, device=queries.device)
+    st = _lib.load().lix_indexer_scores_v41(queries.data_ptr(), keys.data_ptr(), weights.data_ptr(),
+                                            allowed.data_ptr(), B, L, G, H, D, out.data_ptr(),
+                                            _stream(queries.device))
+    _lib.check(st, "lix_indexer_scores_v41")
+    return out
+
+
+def v4_lighting_indexer(index_q, index_k, weights, compress_ratio, topk, topk_indices=None):
+    """The pages' main entry point (the misspelt name is the pages' own).
+
+    Without topk_indices: fused scoring + top-k, returns (scores, indices).
+    With topk_indices [B,S,topk] int32: the scores at those indices
+    (logits, then the gather), returns scores.
+    """
+    if topk_indices is None:
+        return globals()["topk"](index_q, index_k, weights, compress_ratio, topk)
+    logits = indexer_logits(index_q, index_k, weights, compress_ratio)
+    return topk_scores(logits, topk_indices)

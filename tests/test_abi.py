@@ -1,0 +1,120 @@
+"""The C ABI loads, exports what include/lix.h declares, and validates its
+arguments on the host (no GPU needed: every case here fails validation before
+any HIP call)."""
+
+import os
+import re
+
+import pytest
+
+import sparse_attention_lightning_bf16_amd as lx
+from sparse_attention_lightning_bf16_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "lix.h")
+
+NULL, SHAPE, UNSUP, DEVICE = -1, -2, -3, -4
+P = 1 << 20          # a fake, 16-byte aligned address: never dereferenced
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lix_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = lx.load()
+    names = declared_functions()
+    assert set(names) == {"lix_status_string", "lix_version", "lix_indexer_logits", "lix_topk",
+                          "lix_topk_scores", "lix_indexer_scores_v41"}
+    for name in names:
+        assert hasattr(lib, name), name
+        assert name in _lib.SIGNATURES
+
+
+def test_status_strings():
+    for code in (0, NULL, SHAPE, UNSUP, DEVICE, -5):
+        assert lx.status_string(code).startswith("LIX_")
+    assert "UNKNOWN" in lx.status_string(-99)
+    assert lx.load().lix_version() >= 100
+
+
+def logits_call(q=P, k=P, w=P, B=1, S=8, Skv=2, H=64, D=128, c=4, ks=None, ke=None, out=P):
+    return lx.load().lix_indexer_logits(q, k, w, B, S, Skv, H, D, c, ks, ke, out, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(w=None), NULL), (dict(out=None), NULL),
+    (dict(B=0), SHAPE), (dict(S=-1), SHAPE), (dict(Skv=0), SHAPE), (dict(H=0), SHAPE), (dict(D=0), SHAPE),
+    (dict(c=0), SHAPE), (dict(ks=P), SHAPE), (dict(ke=P), SHAPE),
+    (dict(H=3), UNSUP), (dict(H=256), UNSUP), (dict(H=96), UNSUP), (dict(D=24), UNSUP), (dict(D=272), UNSUP),
+    (dict(q=P + 8), UNSUP), (dict(k=P + 2), UNSUP), (dict(w=P + 2), UNSUP), (dict(out=P + 1), UNSUP),
+    (dict(ks=P + 1, ke=P), UNSUP),
+    (dict(B=1 << 16, S=1 << 16, Skv=1 << 16), UNSUP),
+])
+def test_indexer_logits_validation(kw, code):
+    assert logits_call(**kw) == code
+
+
+def topk_call(q=P, k=P, w=P, logits=None, B=1, S=8, Skv=4, H=64, D=128, c=4, ks=None, ke=None, topk=2,
+              scores=P, idx=P):
+    return lx.load().lix_topk(q, k, w, logits, B, S, Skv, H, D, c, ks, ke, topk, scores, idx, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(scores=None), NULL), (dict(idx=None), NULL), (dict(q=None), NULL),
+    (dict(q=None, k=None, w=None, logits=None), NULL),
+    (dict(topk=0), SHAPE), (dict(topk=5), SHAPE), (dict(c=0), SHAPE), (dict(S=0), SHAPE),
+    (dict(ks=P), SHAPE),
+    (dict(H=5), UNSUP), (dict(D=20), UNSUP),
+    (dict(Skv=4096, topk=4096), UNSUP),            # fused: above the on-chip capacity
+    (dict(H=4), UNSUP),                            # fused path needs heads >= 8
+    (dict(Skv=70000, topk=16), UNSUP),             # fused: index above 16 bits
+    (dict(scores=P + 2), UNSUP), (dict(q=P + 4), UNSUP),
+])
+def test_topk_validation(kw, code):
+    assert topk_call(**kw) == code
+
+
+def test_topk_from_logits_ignores_q_k_w_shapes():
+    # with logits given, q/k/w may be NULL and H/D are not checked; the call
+    # passes validation and stops at the device check (no GPU here, or a
+    # fake pointer on a GPU machine)
+    assert topk_call(q=None, k=None, w=None, logits=P, H=0, D=0) == DEVICE
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(logits=None), NULL), (dict(indices=None), NULL), (dict(scores=None), NULL),
+    (dict(B=0), SHAPE), (dict(topk=0), SHAPE), (dict(Skv=-3), SHAPE),
+    (dict(scores=P + 2), UNSUP),
+])
+def test_topk_scores_validation(kw, code):
+    a = dict(logits=P, indices=P, B=1, S=4, Skv=8, topk=2, scores=P)
+    a.update(kw)
+    assert lx.load().lix_topk_scores(a["logits"], a["indices"], a["B"], a["S"], a["Skv"], a["topk"],
+                                     a["scores"], None) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(queries=None), NULL), (dict(keys=None), NULL), (dict(weights=None), NULL),
+    (dict(allowed=None), NULL), (dict(scores=None), NULL),
+    (dict(B=0), SHAPE), (dict(L=0), SHAPE), (dict(G=0), SHAPE), (dict(H=0), SHAPE), (dict(D=-16), SHAPE),
+    (dict(H=6), UNSUP), (dict(H=256), UNSUP), (dict(D=40), UNSUP),
+    (dict(queries=P + 8), UNSUP), (dict(weights=P + 1), UNSUP), (dict(scores=P + 1), UNSUP),
+])
+def test_v41_validation(kw, code):
+    a = dict(queries=P, keys=P, weights=P, allowed=P, B=1, L=4, G=2, H=64, D=128, scores=P)
+    a.update(kw)
+    assert lx.load().lix_indexer_scores_v41(a["queries"], a["keys"], a["weights"], a["allowed"], a["B"], a["L"],
+                                            a["G"], a["H"], a["D"], a["scores"], None) == code
+
+
+def test_python_binding_rejects_bad_tensors_before_the_library():
+    import torch
+    q = torch.zeros(8, 1, 64, 128, dtype=torch.bfloat16)
+    k = torch.zeros(2, 1, 128, dtype=torch.bfloat16)
+    w = torch.zeros(8, 1, 64)
+    with pytest.raises(ValueError):          # CPU tensors are refused
+        lx.indexer_logits(q, k, w, 4)
+    with pytest.raises(TypeError):
+        lx.indexer_logits(q.float(), k, w, 4)

@@ -1,0 +1,372 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Every input comes from the seeded generators in synth/; the oracle sees the
+same bits.  Small cases are compared in full, the 32K/131K/V4.1 workloads on
+stratified row samples.  Tolerances are those of tests/checkers.py.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import sparse_attention_lightning_bf16_amd as lx
+from tests import checkers
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev(t):
+    return t.to(DEV)
+
+
+def v4_case(B, S, Skv, H, D, seed, exact=False, heavy_fraction=0.0):
+    gen = synth.v4_exact_inputs if exact else synth.v4_inputs
+    kw = dict(batch=B, seqlen=S, seqlen_kv=Skv, heads=H, index_dim=D, seed=seed)
+    if heavy_fraction:
+        kw["heavy_fraction"] = heavy_fraction
+    inp = gen(**kw)
+    return inp, {x: synth.bits(inp[x]) for x in "qkw"}
+
+
+def ranges(S, Skv, c, ks=None, ke=None):
+    if ks is None:
+        return oracle.causal_ranges(S, Skv, c)
+    return ks.cpu().numpy().astype(np.int64), ke.cpu().numpy().astype(np.int64)
+
+
+# ------------------------------------------------------------------ V4 logits
+
+@pytest.mark.parametrize("H,D,B,S,Skv,c", [
+    (64, 128, 1, 256, 64, 4),       # tiny workload shape
+    (64, 128, 3, 333, 100, 3),      # ragged tail in queries and keys
+    (128, 256, 2, 70, 40, 2),
+    (64, 48, 1, 129, 33, 4),        # index_dim padded inside the kernel
+    (32, 64, 2, 90, 70, 1),
+    (16, 128, 1, 77, 150, 1),
+    (8, 32, 2, 40, 50, 1),
+    (4, 16, 1, 61, 70, 1),
+    (2, 64, 1, 50, 45, 1),
+    (1, 128, 2, 70, 66, 1),
+])
+def test_logits_match_oracle(H, D, B, S, Skv, c):
+    log(f"logits H={H} D={D} B={B} S={S} Skv={Skv} c={c}")
+    inp, nb = v4_case(B, S, Skv, H, D, seed=100 + H + D)
+    got = lx.indexer_logits(dev(inp["q"]), dev(inp["k"]), dev(inp["w"]), c).cpu().numpy()
+    ks, ke = ranges(S, Skv, c)
+    ora, mag = oracle.indexer_logits(nb["q"], nb["k"], nb["w"], ks, ke, with_magnitude=True)
+    checkers.check_logits(got, ora, mag, f"H={H} D={D}")
+
+
+def test_logits_exact_inputs_are_bitwise_equal():
+    B, S, Skv, H, D, c = 2, 300, 75, 64, 128, 4
+    inp, nb = v4_case(B, S, Skv, H, D, seed=5, exact=True)
+    got = lx.indexer_logits(dev(inp["q"]), dev(inp["k"]), dev(inp["w"]), c).cpu().numpy()
+    ks, ke = ranges(S, Skv, c)
+    ora = oracle.indexer_logits(nb["q"], nb["k"], nb["w"], ks, ke)
+    assert np.array_equal(got.astype(np.float64), ora)
+
+
+def test_logits_given_ranges():
+    B, S, Skv, H, D = 2, 200, 150, 64, 128
+    inp, nb = v4_case(B, S, Skv, H, D, seed=6)
+    g = torch.Generator().manual_seed(7)
+    ks = torch.randint(-5, 160, (S,), generator=g, dtype=torch.int32)
+    ke = ks + torch.randint(-10, 120, (S,), generator=g, dtype=torch.int32)
+    ke[::17] = 10_000                                   # clamped to Skv
+    got = lx.indexer_logits(dev(inp["q"]), dev(inp["k"]), dev(inp["w"]), 1, dev(ks), dev(ke)).cpu().numpy()
+    ksn, ken = ranges(S, Skv, 1, ks, ke)
+    ora, mag = oracle.indexer_logits(nb["q"], nb["k"], nb["w"], ksn, ken, with_magnitude=True)
+    checkers.check_logits(got, ora, mag, "given ranges")
+
+
+def test_logits_4k_workload():
+    cfg = synth.WORKLOADS["4k"]
+    log("4k logits")
+    inp, nb = v4_case(cfg["batch"], cfg["seqlen"], cfg["seqlen_kv"], cfg["heads"], cfg["index_dim"], cfg["seed"])
+    got = lx.indexer_logits(dev(inp["q"]), dev(inp["k"]), dev(inp["w"]), cfg["compress_ratio"]).cpu().numpy()
+    ks, ke = oracle.causal_ranges(cfg["seqlen"], cfg["seqlen_kv"], cfg["compress_ratio"])
+    ora, mag = oracle.indexer_logits(nb["q"], nb["k"], nb["w"], ks, ke, with_magnitude=True)
+    checkers.check_logits(got, ora, mag, "4k")
+
+
+def test_logits_leave_memory_around_the_output_untouched():
+    B, S, Skv, H, D, c = 1, 64, 30, 64, 128, 4
+    inp, _ = v4_case(B, S, Skv, H, D, seed=8)
+    n = B * S * Skv
+    buf = torch.full((n + 2048,), 12345.0, dtype=torch.float32, device=DEV)
+    out = buf[1024:1024 + n].view(B, S, Skv)
+    lx.indexer_logits(dev(inp["q"]), dev(inp["k"]), dev(inp["w"]), c, out=out)
+    torch.cuda.synchronize()
+    assert bool((buf[:1024] == 12345.0).all()) and bool((buf[1024 + n:] == 12345.0).all())
+
+
+# ------------------------------------------------------------------ top-k
+
+def _check_topk_vs_oracle(sc, ix, nb, b, rows, ks, ke, topk, tag):
+    ora, mag = oracle.indexer_logits_rows(nb["q"], nb["k"], nb["w"], b, rows, ks, ke, with_magnitude=True)
+    return checkers.check_topk_rows(sc, ix, ora, mag, ks[rows], ke[rows], topk, tag)
+
+
+def _selection_of(logits_np, ks, ke, topk):
+    """The oracle's selection applied to the kernel's own fp32 logits."""
+    s, i = oracle.topk_select(logits_np.astype(np.float64), ks, ke, topk)
+    return s, i
+
+
+@pytest.mark.parametrize("topk", [1, 5, 16, 40, 64])
+def test_topk_tiny_workload_bitwise_on_kernel_logits(topk):
+    cfg = synth.WORKLOADS["tiny"]
+    inp, nb = v4_case(1, cfg["seqlen"], cfg["seqlen_kv"], 64, 128, cfg["seed"])
+    q, k, w = dev(inp["q"]), dev(inp["k"]), dev(inp["w"])
+    logits = lx.indexer_logits(q, k, w, 4)
+    sc_m, ix_m = lx.topk_from_logits(logits, 4, topk)
+    sc_f, ix_f = lx.topk(q, k, w, 4, topk)
+    lg = logits.cpu().numpy()
+    ks, ke = oracle.causal_ranges(cfg["seqlen"], cfg["seqlen_kv"], 4)
+    want_s, want_i = _selection_of(lg[0], ks, ke, topk)
+    for name, sc, ix in (("materialized", sc_m, ix_m), ("fused", sc_f, ix_f)):
+        sc, ix = sc.cpu().numpy(), ix.cpu().numpy()
+        assert np.array_equal(ix[0], want_i), name
+        assert np.array_equal(sc[0].astype(np.float64), want_s), name
+    _check_topk_vs_oracle(sc_f.cpu().numpy()[0], ix_f.cpu().numpy()[0], nb, 0, np.arange(cfg["seqlen"]),
+                          ks, ke, topk, "tiny fused")
+
+
+def test_topk_4k_workload_fused_and_materialized():
+    cfg = synth.WORKLOADS["4k"]
+    log("4k top-k")
+    B, S, Skv, tk = cfg["batch"], cfg["seqlen"], cfg["seqlen_kv"], cfg["topk"]
+    inp, nb = v4_case(B, S, Skv, 64, 128, cfg["seed"])
+    q, k, w = dev(inp["q"]), dev(inp["k"]), dev(inp["w"])
+    logits = lx.indexer_logits(q, k, w, 4)
+    sc_m, ix_m = lx.topk_from_logits(logits, 4, tk)
+    sc_f, ix_f = lx.topk(q, k, w, 4, tk)
+    assert torch.equal(ix_m, ix_f) and torch.equal(sc_m, sc_f)
+    ks, ke = oracle.causal_ranges(S, Skv, 4)
+    lg = logits.cpu().numpy()
+    sc, ix = sc_m.cpu().numpy(), ix_m.cpu().numpy()
+    rows = np.arange(0, S, 7)
+    for b in range(B):
+        want_s, want_i = _selection_of(lg[b][rows], ks[rows], ke[rows], tk)
+        assert np.array_equal(ix[b][rows], want_i)
+        exact = _check_topk_vs_oracle(sc[b][rows], ix[b][rows], nb, b, rows, ks, ke, tk, f"4k b={b}")
+        log(f"  batch {b}: rows with a forced exact set: {exact}/{len(rows)}")
+
+
+def test_topk_ties_and_padding_bitwise():
+    # scores drawn from a handful of values: heavy ties at every threshold
+    g = torch.Generator().manual_seed(9)
+    B, S, Skv = 2, 97, 300
+    lg = (torch.randint(0, 6, (B, S, Skv), generator=g).float() - 2.0) * 0.5
+    lg[:, :, 7] = -0.0                                   # signed zeros tie with +0
+    ks = torch.randint(0, 40, (S,), generator=g, dtype=torch.int32)
+    ke = ks + torch.randint(-3, 280, (S,), generator=g, dtype=torch.int32)
+    for tk in (1, 3, 50, 128, 300):
+        sc, ix = lx.topk_from_logits(dev(lg), 1, tk, dev(ks), dev(ke))
+        sc, ix = sc.cpu().numpy(), ix.cpu().numpy()
+        for b in range(B):
+            want_s, want_i = oracle.topk_select(lg[b].numpy().astype(np.float64), ks.numpy(), ke.numpy(), tk)
+            assert np.array_equal(ix[b], want_i), tk
+            assert np.array_equal(sc[b].astype(np.float64), want_s), tk
+
+
+def test_topk_long_rows_from_logits():
+    # rows longer than the register cache of the row kernel (re-read path)
+    g = torch.Generator().manual_seed(10)
+    B, S, Skv, tk = 1, 12, 20000, 700
+    lg = torch.randn(B, S, Skv, generator=g)
+    sc, ix = lx.topk_from_logits(dev(lg), 1, tk, dev(torch.zeros(S, dtype=torch.int32)),
+                                 dev(torch.arange(S, dtype=torch.int32) * 1800))
+    want_s, want_i = oracle.topk_select(lg[0].numpy().astype(np.float64), np.zeros(S, int), np.arange(S) * 1800, tk)
+    assert np.array_equal(ix.cpu().numpy()[0], want_i)
+    assert np.array_equal(sc.cpu().numpy()[0].astype(np.float64), want_s)
+
+
+@pytest.mark.parametrize("H,D,topk", [(64, 128, 2048), (128, 128, 256), (32, 64, 100), (16, 32, 33),
+                                      (8, 128, 64)])
+def test_fused_equals_materialized(H, D, topk):
+    B, S, Skv, c = 2, 3000, 2800, 1
+    log(f"fused vs materialized H={H} D={D} topk={topk}")
+    inp, _ = v4_case(B, S, Skv, H, D, seed=11 + H)
+    q, k, w = dev(inp["q"]), dev(inp["k"]), dev(inp["w"])
+    logits = lx.indexer_logits(q, k, w, c)
+    sc_m, ix_m = lx.topk_from_logits(logits, c, topk)
+    sc_f, ix_f = lx.topk(q, k, w, c, topk)
+    assert torch.equal(ix_m, ix_f)
+    assert torch.equal(sc_m, sc_f)
+
+
+def test_fused_exact_inputs_bitwise_vs_oracle():
+    B, S, Skv, H, D, c, tk = 1, 2000, 500, 64, 128, 4, 37
+    inp, nb = v4_case(B, S, Skv, H, D, seed=12, exact=True)
+    sc, ix = lx.topk(dev(inp["q"]), dev(inp["k"]), dev(inp["w"]), c, tk)
+    ks, ke = oracle.causal_ranges(S, Skv, c)
+    ora = oracle.indexer_logits(nb["q"], nb["k"], nb["w"], ks, ke)
+    want_s, want_i = oracle.topk_select(ora[0], ks, ke, tk)
+    assert np.array_equal(ix.cpu().numpy()[0], want_i)
+    assert np.array_equal(sc.cpu().numpy()[0].astype(np.float64), want_s)
+
+
+def test_topk_edges_select_all_and_single_key():
+    inp, nb = v4_case(1, 40, 9, 64, 128, seed=13)
+    q, k, w = dev(inp["q"]), dev(inp["k"]), dev(inp["w"])
+    for tk in (9, 1):
+        sc_f, ix_f = lx.topk(q, k, w, 1, tk)
+        logits = lx.indexer_logits(q, k, w, 1)
+        sc_m, ix_m = lx.topk_from_logits(logits, 1, tk)
+        assert torch.equal(ix_f, ix_m) and torch.equal(sc_f, sc_m)
+        want_s, want_i = oracle.topk_select(logits.cpu().numpy()[0].astype(np.float64),
+                                            *oracle.causal_ranges(40, 9, 1), tk)
+        assert np.array_equal(ix_f.cpu().numpy()[0], want_i)
+    with pytest.raises(lx.LixError):
+        lx.topk(q, k, w, 1, 10)                          # topk > Skv
+
+
+# ------------------------------------------------------------------ gather
+
+def test_gather_matches_oracle():
+    inp, _ = v4_case(2, 100, 50, 64, 128, seed=14)
+    logits = lx.indexer_logits(dev(inp["q"]), dev(inp["k"]), dev(inp["w"]), 2)
+    g = torch.Generator().manual_seed(15)
+    idx = torch.randint(-3, 60, (2, 100, 17), generator=g, dtype=torch.int32)
+    got = lx.topk_scores(logits, dev(idx)).cpu().numpy()
+    want = oracle.topk_scores_gather(logits.cpu().numpy().astype(np.float64), idx.numpy())
+    assert np.array_equal(got.astype(np.float64), want)
+
+
+def test_lighting_indexer_with_given_indices_round_trip():
+    inp, _ = v4_case(1, 300, 75, 64, 128, seed=16)
+    q, k, w = dev(inp["q"]), dev(inp["k"]), dev(inp["w"])
+    sc, ix = lx.v4_lighting_indexer(q, k, w, 4, 20)
+    again = lx.v4_lighting_indexer(q, k, w, 4, 20, topk_indices=ix)
+    assert torch.equal(sc, again)
+
+
+# ------------------------------------------------------------------ V4.1
+
+@pytest.mark.parametrize("H,D,B,L,G", [(64, 128, 1, 200, 60), (16, 32, 2, 70, 100), (128, 64, 1, 33, 20),
+                                       (1, 16, 1, 64, 70), (4, 48, 2, 50, 30)])
+def test_v41_matches_oracle(H, D, B, L, G):
+    log(f"v41 H={H} D={D} B={B} L={L} G={G}")
+    inp = synth.v41_inputs(batch=B, local_sequence=L, global_compressed=G, heads=H, index_dim=D, seed=20 + H,
+                           doc_min=10, doc_max=80)
+    nb = {x: synth.bits(inp[x]) for x in ("queries", "keys", "weights", "allowed")}
+    got = lx.indexer_scores_v41(*(dev(inp[x]) for x in ("queries", "keys", "weights", "allowed")))
+    got = got.cpu().view(torch.int16).numpy().view(np.uint16)
+    widened = 0
+    for b in range(B):
+        rows = np.arange(L)
+        o = oracle.indexer_scores_v41_rows(nb["queries"], nb["keys"], nb["weights"], nb["allowed"], b, rows)
+        lo, hi = oracle.indexer_scores_v41_bounds_rows(nb["queries"], nb["keys"], nb["weights"], nb["allowed"],
+                                                       b, rows)
+        widened += checkers.check_v41(got[b], o, lo, hi, f"v41 b={b}")
+    log(f"  outputs needing the accumulation interval: {widened}")
+
+
+def test_v41_exact_inputs_bitwise():
+    inp = synth.v41_exact_inputs(batch=2, local_sequence=90, global_compressed=70, heads=64, index_dim=128,
+                                 seed=21, density=0.4)
+    nb = {x: synth.bits(inp[x]) for x in ("queries", "keys", "weights", "allowed")}
+    got = lx.indexer_scores_v41(*(dev(inp[x]) for x in ("queries", "keys", "weights", "allowed")))
+    got = got.cpu().view(torch.int16).numpy().view(np.uint16)
+    want = oracle.f64_to_bf16_bits(oracle.indexer_scores_v41(nb["queries"], nb["keys"], nb["weights"],
+                                                             nb["allowed"]))
+    assert np.array_equal(got, want)
+
+
+def test_v41_golden_rounding_cases_on_gpu():
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "v41_rounding.json")))
+    D = g["index_dim"]
+    for case in g["cases"]:
+        H = len(case["heads"])
+        q = torch.zeros(1, 1, H, D)
+        w = torch.zeros(1, 1, H)
+        for h, hd in enumerate(case["heads"]):
+            q[0, 0, h, :len(hd["q"])] = torch.tensor(hd["q"], dtype=torch.float32)
+            w[0, 0, h] = hd["w"]
+        k = torch.zeros(1, 1, D)
+        k[0, 0, :len(case["k"])] = torch.tensor(case["k"], dtype=torch.float32)
+        al = torch.tensor([[[case["allowed"]]]])
+        out = lx.indexer_scores_v41(dev(q.bfloat16()), dev(k.bfloat16()), dev(w.bfloat16()), dev(al))
+        bits = int(out.cpu().view(torch.int16).item()) & 0xFFFF
+        assert bits == int(case["out_bits"], 16), case["name"]
+
+
+# ------------------------------------------------------------------ full-size workloads (sampled)
+
+def test_32k_workload_sampled_rows():
+    cfg = synth.WORKLOADS["32k"]
+    S, Skv, tk = cfg["seqlen"], cfg["seqlen_kv"], cfg["topk"]
+    log("32k: generating inputs")
+    inp, nb = v4_case(1, S, Skv, 64, 128, cfg["seed"])
+    q, k, w = dev(inp["q"]), dev(inp["k"]), dev(inp["w"])
+    log("32k: fused top-k")
+    sc_f, ix_f = lx.topk(q, k, w, 4, tk)
+    log("32k: materialized logits + top-k")
+    logits = lx.indexer_logits(q, k, w, 4)
+    sc_m, ix_m = lx.topk_from_logits(logits, 4, tk)
+    assert torch.equal(ix_f, ix_m) and torch.equal(sc_f, sc_m)
+    rows = np.arange(31, S, 64)
+    ks, ke = oracle.causal_ranges(S, Skv, 4)
+    ora, mag = oracle.indexer_logits_rows(nb["q"], nb["k"], nb["w"], 0, rows, ks, ke, with_magnitude=True)
+    checkers.check_logits(logits[0][torch.from_numpy(rows).to(DEV)].cpu().numpy(), ora, mag, "32k rows")
+    exact = checkers.check_topk_rows(sc_f[0].cpu().numpy()[rows], ix_f[0].cpu().numpy()[rows], ora, mag,
+                                     ks[rows], ke[rows], tk, "32k")
+    log(f"  32k: rows with a forced exact set: {exact}/{len(rows)}")
+
+
+def test_131k_workload_fused_sampled_rows():
+    cfg = synth.WORKLOADS["131k"]
+    S, Skv, tk = cfg["seqlen"], cfg["seqlen_kv"], cfg["topk"]
+    log("131k: generating inputs")
+    inp, nb = v4_case(1, S, Skv, 64, 128, cfg["seed"], heavy_fraction=cfg["heavy_fraction"])
+    q, k, w = dev(inp["q"]), dev(inp["k"]), dev(inp["w"])
+    log("131k: fused top-k")
+    sc, ix = lx.topk(q, k, w, 4, tk)
+    torch.cuda.synchronize()
+    rows = np.concatenate([np.arange(255, S, 256)[:400], np.arange(S - 64, S)])
+    ks, ke = oracle.causal_ranges(S, Skv, 4)
+    log("131k: oracle rows")
+    ora, mag = oracle.indexer_logits_rows(nb["q"], nb["k"], nb["w"], 0, rows, ks, ke, with_magnitude=True)
+    exact = checkers.check_topk_rows(sc[0].cpu().numpy()[rows], ix[0].cpu().numpy()[rows], ora, mag,
+                                     ks[rows], ke[rows], tk, "131k")
+    log(f"  131k: rows with a forced exact set: {exact}/{len(rows)}")
+
+
+def test_v41_workload_sampled_rows():
+    cfg = synth.WORKLOADS["v41"]
+    log("v41 workload: generating inputs")
+    inp = synth.v41_inputs(**cfg)
+    nb = {x: synth.bits(inp[x]) for x in ("queries", "keys", "weights", "allowed")}
+    got = lx.indexer_scores_v41(*(dev(inp[x]) for x in ("queries", "keys", "weights", "allowed")))
+    got = got.cpu().view(torch.int16).numpy().view(np.uint16)[0]
+    rows = np.arange(15, cfg["local_sequence"], 32)
+    o = oracle.indexer_scores_v41_rows(nb["queries"], nb["keys"], nb["weights"], nb["allowed"], 0, rows)
+    lo, hi = oracle.indexer_scores_v41_bounds_rows(nb["queries"], nb["keys"], nb["weights"], nb["allowed"], 0,
+                                                   rows)
+    widened = checkers.check_v41(got[rows], o, lo, hi, "v41 workload")
+    allowed_frac = float(inp["allowed"].float().mean())
+    log(f"  v41 workload: allowed fraction {allowed_frac:.4f}; outputs needing the interval: {widened}")
+
+
+def test_device_properties_logged():
+    p = torch.cuda.get_device_properties(0)
+    log(f"device: {p.name} gcn={getattr(p, 'gcnArchName', '?')} CUs={p.multi_processor_count} "
+        f"shared/block={getattr(p, 'shared_memory_per_block', '?')} "
+        f"shared/block optin={getattr(p, 'shared_memory_per_block_optin', '?')} "
+        f"L2={getattr(p, 'L2_cache_size', '?')} mem={p.total_memory >> 30} GiB")
+    assert "gfx950" in getattr(p, "gcnArchName", "gfx950")
