@@ -32,6 +32,8 @@ def common_flags():
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
             # keep packed fp32 VALU instructions out of the device code
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA accumulators in VGPRs: the epilogue reads them directly
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC,
             "-Wall", "-Wno-unused-result"]
 

@@ -48,6 +48,17 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_floa
 
 __device__ __forceinline__ float neg_inf() { return __uint_as_float(0xff800000u); }
 
+// max(0, x) as one integer max: a float with the sign bit set is a negative
+// int32, every other float is a non-negative one whose order matches.
+// (-0.0 becomes +0.0.)
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// c ? a : b on the bit patterns, so no select of addresses reaches the optimiser.
+__device__ __forceinline__ float pick(bool c, float a, float b) {
+    const int m = -(int)c;
+    return __int_as_float((__float_as_int(a) & m) | (__float_as_int(b) & ~m));
+}
+
 // Visible key range of query t: [ks, ke) clamped to [0, skv]; causal when ks_arr is null.
 __device__ __forceinline__ void key_range(const int32_t* __restrict__ ks_arr, const int32_t* __restrict__ ke_arr,
                                           int t, int S, int skv, int ratio, int& lo, int& hi) {

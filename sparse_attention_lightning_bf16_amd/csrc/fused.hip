@@ -197,7 +197,7 @@ __global__ __launch_bounds__(256) void v4_fused_topk_kernel(InLayout L, const fl
 #pragma unroll
                         for (int i = 0; i < 16; ++i) {
                             const int j = T::slot(r, i);
-                            part[cb][j] = fmaf(wr[r][i], fmaxf(acc[r][i], 0.0f), part[cb][j]);
+                            part[cb][j] = fmaf(wr[r][i], relu(acc[r][i]), part[cb][j]);
                         }
 #pragma unroll
                     for (int j = 0; j < T::QW; ++j) part[cb][j] = xor32_add(part[cb][j]);
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(256) void v4_fused_topk_kernel(InLayout L, const fl
                 const int s = s0 + lane;
 #pragma unroll
                 for (int j = 0; j < T::QW; ++j) {
-                    const float v = hf ? part[1][j] : part[0][j];
+                    const float v = pick(hf != 0, part[1][j], part[0][j]);
                     const uint32_t key = f32_to_key(v);
                     const bool in_range = (s >= lo_s[j]) && (s < hi_s[j]);
                     bool acc_ok = in_range && key > thr[j];

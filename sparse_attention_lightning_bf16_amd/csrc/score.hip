@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256) void v4_logits_kernel(InLayout L, const float*
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         const int j = T::slot(r, i);
-                        part[cb][j] = fmaf(wr[r][i], fmaxf(acc[r][i], 0.0f), part[cb][j]);
+                        part[cb][j] = fmaf(wr[r][i], relu(acc[r][i]), part[cb][j]);
                     }
                 if constexpr (H >= 8) {
 #pragma unroll
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(256) void v4_logits_kernel(InLayout L, const float*
             for (int j = 0; j < T::QW; ++j) {
                 const int t = tq0 + j;
                 if (t < S && s < skv) {
-                    const float v = hf ? part[1][j] : part[0][j];
+                    const float v = pick(hf != 0, part[1][j], part[0][j]);
                     out[((long)b * S + t) * skv + s] = (s >= lo_s[j] && s < hi_s[j]) ? v : neg_inf();
                 }
             }
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(256) void v41_scores_kernel(InLayout L, const uint1
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         const int j = T::slot(r, i);
-                        const float rr = round_bf16(fmaxf(acc[r][i], 0.0f));   // bf16(d), ReLU commutes
+                        const float rr = round_bf16(relu(acc[r][i]));   // bf16(d); ReLU commutes with rounding
                         part[cb][j] += round_bf16(wr[r][i] * rr);              // exact product, then bf16
                     }
                 if constexpr (H >= 8) {
