@@ -172,64 +172,51 @@ __global__ __launch_bounds__(256) void v4_fused_topk_kernel(InLayout L, const fl
                 wr[r][i] = (t < S) ? w[((long)t * B + b) * H + h] : 0.0f;
             }
 
-        u32x4 pf[T::CPT];
-        load_k_stage<T>(pf, L, b, tile_lo * T::KT, skv, tid);
-        store_k_stage<T>(lds[0], pf, tid);
-        __syncthreads();
-
-        for (int it = 0; it < ntile; ++it) {
+        stream_key_stages<T>(L, b, skv, tile_lo, ntile, lds, tid, [&](int it, const uint8_t* stage) {
             const int s0 = (tile_lo + it) * T::KT;
-            const bool more = it + 1 < ntile;
-            if (more) load_k_stage<T>(pf, L, b, s0 + T::KT, skv, tid);
-            const uint8_t* stage = lds[it & 1];
             const bool active = (s0 < wave_hi) && (s0 + T::KT > wave_lo);
-
-            if (active) {
-                float part[T::NCB][T::QW];
+            if (!active) return;
+            float part[T::NCB][T::QW];
 #pragma unroll
-                for (int cb = 0; cb < T::NCB; ++cb) {
+            for (int cb = 0; cb < T::NCB; ++cb) {
 #pragma unroll
-                    for (int j = 0; j < T::QW; ++j) part[cb][j] = 0.0f;
-                    f32x16 acc[T::NRT];
-                    mfma_block<T>(acc, a, stage, cb, lane);
+                for (int j = 0; j < T::QW; ++j) part[cb][j] = 0.0f;
+                f32x16 acc[T::NRT];
+                mfma_block<T>(acc, a, stage, cb, lane);
 #pragma unroll
-                    for (int r = 0; r < T::NRT; ++r)
+                for (int r = 0; r < T::NRT; ++r)
 #pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            const int j = T::slot(r, i);
-                            part[cb][j] = fmaf(wr[r][i], relu(acc[r][i]), part[cb][j]);
-                        }
-#pragma unroll
-                    for (int j = 0; j < T::QW; ++j) part[cb][j] = xor32_add(part[cb][j]);
-                }
-
-                // Lane l holds key s0 + l of each of its queries.
-                const int s = s0 + lane;
-#pragma unroll
-                for (int j = 0; j < T::QW; ++j) {
-                    const float v = pick(hf != 0, part[1][j], part[0][j]);
-                    const uint32_t key = f32_to_key(v);
-                    const bool in_range = (s >= lo_s[j]) && (s < hi_s[j]);
-                    bool acc_ok = in_range && key > thr[j];
-                    unsigned long long m = __ballot(acc_ok);
-                    if (m != 0ull && cnt[j] + __popcll(m) > cap) {
-                        thr[j] = wave_select<false>(bkey[j], bidx[j], cnt[j], topk, hist, lane, nullptr, nullptr);
-                        cnt[j] = topk;
-                        acc_ok = in_range && key > thr[j];
-                        m = __ballot(acc_ok);
+                    for (int i = 0; i < 16; ++i) {
+                        const int j = T::slot(r, i);
+                        part[cb][j] = fmaf(wr[r][i], relu(acc[r][i]), part[cb][j]);
                     }
-                    if (acc_ok) {
-                        const int pos = cnt[j] + lanes_below_f(m, lane);
-                        bkey[j][pos] = key;
-                        bidx[j][pos] = (uint16_t)s;
-                    }
-                    cnt[j] += __popcll(m);
-                }
+#pragma unroll
+                for (int j = 0; j < T::QW; ++j) part[cb][j] = xor32_add(part[cb][j]);
             }
 
-            if (more) store_k_stage<T>(lds[(it + 1) & 1], pf, tid);
-            __syncthreads();
-        }
+            // Lane l holds key s0 + l of each of its queries.
+            const int s = s0 + lane;
+#pragma unroll
+            for (int j = 0; j < T::QW; ++j) {
+                const float v = pick(hf != 0, part[1][j], part[0][j]);
+                const uint32_t key = f32_to_key(v);
+                const bool in_range = (s >= lo_s[j]) && (s < hi_s[j]);
+                bool acc_ok = in_range && key > thr[j];
+                unsigned long long m = __ballot(acc_ok);
+                if (m != 0ull && cnt[j] + __popcll(m) > cap) {
+                    thr[j] = wave_select<false>(bkey[j], bidx[j], cnt[j], topk, hist, lane, nullptr, nullptr);
+                    cnt[j] = topk;
+                    acc_ok = in_range && key > thr[j];
+                    m = __ballot(acc_ok);
+                }
+                if (acc_ok) {
+                    const int pos = cnt[j] + lanes_below_f(m, lane);
+                    bkey[j][pos] = key;
+                    bidx[j][pos] = (uint16_t)s;
+                }
+                cnt[j] += __popcll(m);
+            }
+        });
     }
 
     // Final selection per query, then padding.

@@ -26,7 +26,8 @@ __device__ __forceinline__ void load_weights_f32(float (&wr)[T::NRT][16], const 
         for (int i = 0; i < 16; ++i) {
             const int row = 32 * r + c_row(i, hf);
             const int t = tq0 + row / T::H, h = row % T::H;
-            wr[r][i] = (t < S) ? w[(long)t * w_t + (long)b * w_b + h] : 0.0f;
+            const float v = w[(long)min(t, S - 1) * w_t + (long)b * w_b + h];
+            wr[r][i] = (t < S) ? v : 0.0f;
         }
 }
 
@@ -41,114 +42,117 @@ __global__ __launch_bounds__(256) void v4_logits_kernel(InLayout L, const float*
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5;
     const int nqb = (S + T::QB - 1) / T::QB;
-    const int b = blockIdx.x % B;
-    const int qb = nqb - 1 - (int)(blockIdx.x / B);      // longest causal rows first
-    const int t0 = qb * T::QB;
-    const int tq0 = t0 + wave * T::QW;                    // first query of this wave
+    const int nblk = nqb * B;
+    const int G = gridDim.x;
+    // block j: batch j % B, query block nqb-1-j/B (longest causal rows first)
+    auto block_b = [&](int j) { return j % B; };
+    auto block_t0 = [&](int j) { return (nqb - 1 - j / B) * T::QB; };
 
-    // Key span of the workgroup, in whole stages.
-    int wg_lo = skv, wg_hi = 0;
-    for (int j = 0; j < T::QB; ++j) {
-        int lo, hi;
-        key_range(ks, ke, t0 + j, S, skv, ratio, lo, hi);
-        if (hi > lo) { wg_lo = min(wg_lo, lo); wg_hi = max(wg_hi, hi); }
-    }
-    const int tile_lo = (wg_hi > wg_lo) ? wg_lo / T::KT : 0;
-    const int tile_hi = (wg_hi > wg_lo) ? (wg_hi + T::KT - 1) / T::KT : 0;
-    const int span_lo = tile_lo * T::KT, span_hi = min(skv, tile_hi * T::KT);
+    for (int i = 0;; ++i) {
+        const int j = sched_block(blockIdx.x, G, i);
+        if (j >= nblk) break;
+        const int b = block_b(j), t0 = block_t0(j);
+        const int tq0 = t0 + wave * T::QW;
+        bf16x8 a[T::NRT][T::NSTEP];
+        load_q_frags<T>(a, L, b, tq0, S, lane);
+        float wr[T::NRT][16];
+        load_weights_f32<T>(wr, w, (long)B * H, H, b, tq0, S, lane);
 
-    // -inf outside the staged span (no query of the workgroup sees those keys).
-    for (int j = 0; j < T::QB; ++j) {
-        const int t = t0 + j;
-        if (t >= S) break;
-        float* row = out + ((long)b * S + t) * skv;
-        fill_neg_inf(row, span_lo, tid, T::THREADS);
-        fill_neg_inf(row + span_hi, skv - span_hi, tid, T::THREADS);
-    }
-    const int ntile = tile_hi - tile_lo;
-    if (ntile <= 0) return;
+        // Key span of the workgroup, in whole stages.
+        int wg_lo = skv, wg_hi = 0;
+        for (int q = 0; q < T::QB; ++q) {
+            int lo, hi;
+            key_range(ks, ke, t0 + q, S, skv, ratio, lo, hi);
+            if (hi > lo) { wg_lo = min(wg_lo, lo); wg_hi = max(wg_hi, hi); }
+        }
+        const int tile_lo = (wg_hi > wg_lo) ? wg_lo / T::KT : 0;
+        const int tile_hi = (wg_hi > wg_lo) ? (wg_hi + T::KT - 1) / T::KT : 0;
+        const int span_lo = tile_lo * T::KT, span_hi = min(skv, tile_hi * T::KT);
+        const int ntile = tile_hi - tile_lo;
 
-    // This lane's queries: ranges per slot.
-    int lo_s[T::QW], hi_s[T::QW];
-    int wave_lo = skv, wave_hi = 0;
+        int lo_s[T::QW], hi_s[T::QW];
+        int wave_lo = skv, wave_hi = 0;
 #pragma unroll
-    for (int j = 0; j < T::QW; ++j) {
-        key_range(ks, ke, slot_query<T>(tq0, j, hf), S, skv, ratio, lo_s[j], hi_s[j]);
-    }
-    for (int j = 0; j < T::QW; ++j) {
-        int lo, hi;
-        key_range(ks, ke, tq0 + j, S, skv, ratio, lo, hi);
-        if (hi > lo) { wave_lo = min(wave_lo, lo); wave_hi = max(wave_hi, hi); }
-    }
+        for (int q = 0; q < T::QW; ++q)
+            key_range(ks, ke, slot_query<T>(tq0, q, hf), S, skv, ratio, lo_s[q], hi_s[q]);
+        for (int q = 0; q < T::QW; ++q) {
+            int lo, hi;
+            key_range(ks, ke, tq0 + q, S, skv, ratio, lo, hi);
+            if (hi > lo) { wave_lo = min(wave_lo, lo); wave_hi = max(wave_hi, hi); }
+        }
 
-    bf16x8 a[T::NRT][T::NSTEP];
-    load_q_frags<T>(a, L, b, tq0, S, lane);
-    float wr[T::NRT][16];
-    load_weights_f32<T>(wr, w, (long)B * H, H, b, tq0, S, lane);
-
-    u32x4 pf[T::CPT];
-    load_k_stage<T>(pf, L, b, span_lo, skv, tid);
-    store_k_stage<T>(lds[0], pf, tid);
-    __syncthreads();
-
-    for (int it = 0; it < ntile; ++it) {
-        const int s0 = (tile_lo + it) * T::KT;
-        const bool more = it + 1 < ntile;
-        if (more) load_k_stage<T>(pf, L, b, s0 + T::KT, skv, tid);
-        const uint8_t* stage = lds[it & 1];
-        const bool active = (s0 < wave_hi) && (s0 + T::KT > wave_lo);
-
-        float part[T::NCB][T::QW];
+        float* out_b = out + (long)b * S * skv;
+        // Results of a stage are stored at the start of the next one (see
+        // stream_key_stages): pend[cb][q], first key of that stage pend_s0.
+        float pend[T::NCB][T::QW];
+        int pend_s0 = -1;
+        auto flush = [&]() {
+            if (pend_s0 < 0) return;
+            if constexpr (H >= 8) {
+                // Both halves hold full sums; the lower half writes column block 0,
+                // the upper half column block 1: 64 consecutive keys per query.
+                const int s = pend_s0 + lane;
 #pragma unroll
-        for (int cb = 0; cb < T::NCB; ++cb) {
-#pragma unroll
-            for (int j = 0; j < T::QW; ++j) part[cb][j] = 0.0f;
-            if (active) {
-                f32x16 acc[T::NRT];
-                mfma_block<T>(acc, a, stage, cb, lane);
-#pragma unroll
-                for (int r = 0; r < T::NRT; ++r)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int j = T::slot(r, i);
-                        part[cb][j] = fmaf(wr[r][i], relu(acc[r][i]), part[cb][j]);
+                for (int q = 0; q < T::QW; ++q) {
+                    const int t = tq0 + q;
+                    if (t < S && s < skv) {
+                        const float v = pick(hf != 0, pend[1][q], pend[0][q]);
+                        __builtin_nontemporal_store((s >= lo_s[q] && s < hi_s[q]) ? v : neg_inf(),
+                                                    out_b + (long)t * skv + s);
                     }
-                if constexpr (H >= 8) {
+                }
+            } else {
 #pragma unroll
-                    for (int j = 0; j < T::QW; ++j) part[cb][j] = xor32_add(part[cb][j]);
+                for (int cb = 0; cb < T::NCB; ++cb) {
+                    const int s = pend_s0 + 32 * cb + (lane & 31);
+#pragma unroll
+                    for (int q = 0; q < T::QW; ++q) {
+                        if ((q % (2 * T::half_step())) >= T::half_step()) continue;   // slot owned via hf
+                        const int t = slot_query<T>(tq0, q, hf);
+                        if (t < S && s < skv)
+                            __builtin_nontemporal_store((s >= lo_s[q] && s < hi_s[q]) ? pend[cb][q] : neg_inf(),
+                                                        out_b + (long)t * skv + s);
+                    }
                 }
             }
+        };
+        if (ntile > 0) {
+            stream_key_stages<T>(L, b, skv, tile_lo, ntile, lds, tid, [&](int it, const uint8_t* stage) {
+                flush();
+                const int s0 = (tile_lo + it) * T::KT;
+                const bool active = (s0 < wave_hi) && (s0 + T::KT > wave_lo);
+#pragma unroll
+                for (int cb = 0; cb < T::NCB; ++cb) {
+#pragma unroll
+                    for (int q = 0; q < T::QW; ++q) pend[cb][q] = 0.0f;
+                    if (active) {
+                        f32x16 acc[T::NRT];
+                        mfma_block<T>(acc, a, stage, cb, lane);
+#pragma unroll
+                        for (int r = 0; r < T::NRT; ++r)
+#pragma unroll
+                            for (int ii = 0; ii < 16; ++ii) {
+                                const int q = T::slot(r, ii);
+                                pend[cb][q] = fmaf(wr[r][ii], relu(acc[r][ii]), pend[cb][q]);
+                            }
+                        if constexpr (H >= 8) {
+#pragma unroll
+                            for (int q = 0; q < T::QW; ++q) pend[cb][q] = xor32_add(pend[cb][q]);
+                        }
+                    }
+                }
+                pend_s0 = s0;
+            });
+            flush();
         }
-
-        if constexpr (H >= 8) {
-            // Both halves hold full sums; the lower half writes column block 0,
-            // the upper half column block 1: 64 consecutive keys per query.
-            const int s = s0 + lane;
-#pragma unroll
-            for (int j = 0; j < T::QW; ++j) {
-                const int t = tq0 + j;
-                if (t < S && s < skv) {
-                    const float v = pick(hf != 0, part[1][j], part[0][j]);
-                    out[((long)b * S + t) * skv + s] = (s >= lo_s[j] && s < hi_s[j]) ? v : neg_inf();
-                }
-            }
-        } else {
-#pragma unroll
-            for (int cb = 0; cb < T::NCB; ++cb) {
-                const int s = s0 + 32 * cb + (lane & 31);
-#pragma unroll
-                for (int j = 0; j < T::QW; ++j) {
-                    if ((j % (2 * T::half_step())) >= T::half_step()) continue;   // slot owned via hf
-                    const int t = slot_query<T>(tq0, j, hf);
-                    if (t < S && s < skv)
-                        out[((long)b * S + t) * skv + s] =
-                            (s >= lo_s[j] && s < hi_s[j]) ? part[cb][j] : neg_inf();
-                }
-            }
+        // -inf outside the staged span: no query of the block sees those keys.
+        for (int q = 0; q < T::QB; ++q) {
+            const int t = t0 + q;
+            if (t >= S) break;
+            float* row = out_b + (long)t * skv;
+            fill_neg_inf(row, span_lo, tid, T::THREADS);
+            fill_neg_inf(row + span_hi, skv - span_hi, tid, T::THREADS);
         }
-
-        if (more) store_k_stage<T>(lds[(it + 1) & 1], pf, tid);
-        __syncthreads();
     }
 }
 
@@ -181,18 +185,9 @@ __global__ __launch_bounds__(256) void v41_scores_kernel(InLayout L, const uint1
             wr[r][i] = (t < Lq) ? bf16_to_f32(wts[((long)b * Lq + t) * H + h]) : 0.0f;
         }
 
-    u32x4 pf[T::CPT];
-    load_k_stage<T>(pf, L, b, 0, G, tid);
-    store_k_stage<T>(lds[0], pf, tid);
-    __syncthreads();
-
     const uint16_t kNegInfBf16 = 0xff80u;
-    for (int it = 0; it < ntile; ++it) {
+    stream_key_stages<T>(L, b, G, 0, ntile, lds, tid, [&](int it, const uint8_t* stage) {
         const int s0 = it * T::KT;
-        const bool more = it + 1 < ntile;
-        if (more) load_k_stage<T>(pf, L, b, s0 + T::KT, G, tid);
-        const uint8_t* stage = lds[it & 1];
-
         // Visibility of this lane's keys for each of its queries.
         bool vis[T::NCB][T::QW];
         bool any = false;
@@ -222,7 +217,7 @@ __global__ __launch_bounds__(256) void v41_scores_kernel(InLayout L, const uint1
                     for (int i = 0; i < 16; ++i) {
                         const int j = T::slot(r, i);
                         const float rr = round_bf16(relu(acc[r][i]));   // bf16(d); ReLU commutes with rounding
-                        part[cb][j] += round_bf16(wr[r][i] * rr);              // exact product, then bf16
+                        part[cb][j] += round_bf16(wr[r][i] * rr);       // exact product, then bf16
                     }
                 if constexpr (H >= 8) {
 #pragma unroll
@@ -242,15 +237,11 @@ __global__ __launch_bounds__(256) void v41_scores_kernel(InLayout L, const uint1
                     if ((j % (2 * T::half_step())) >= T::half_step()) continue;
                 }
                 const int t = slot_query<T>(tq0, j, hf);
-                if (t < Lq && s < G) {
+                if (t < Lq && s < G)
                     out[((long)b * Lq + t) * G + s] = vis[cb][j] ? bf16_bits(part[cb][j]) : kNegInfBf16;
-                }
             }
         }
-
-        if (more) store_k_stage<T>(lds[(it + 1) & 1], pf, tid);
-        __syncthreads();
-    }
+    });
 }
 
 // ---------------------------------------------------------------- launchers
@@ -260,8 +251,8 @@ static hipError_t launch_v4_logits_t(const LogitsArgs& p) {
     using T = Tiling<H, DP>;
     InLayout L{static_cast<const uint16_t*>(p.q), (long)p.B * H * p.D, (long)H * p.D,
                static_cast<const uint16_t*>(p.k), (long)p.B * p.D, (long)p.D, p.D};
-    const int nqb = (p.S + T::QB - 1) / T::QB;
-    dim3 grid((unsigned)((long)nqb * p.B));
+    const long nblk = (long)((p.S + T::QB - 1) / T::QB) * p.B;
+    dim3 grid((unsigned)nblk);                 // one block per workgroup (see sched_block)
     hipLaunchKernelGGL((v4_logits_kernel<H, DP>), grid, dim3(T::THREADS), 0, p.stream, L, p.w, p.B, p.S, p.Skv,
                        p.ratio, p.ks, p.ke, p.logits);
     return hipGetLastError();

@@ -54,7 +54,8 @@ struct InLayout {
 
 // Fragments of the wave's rows: a[r][st] holds rows 32r + (lane % 32),
 // index_dim entries 16 st + 8 (lane / 32) + 0..7.  Queries past S and
-// index_dim entries past D read as zero.
+// index_dim entries past D read as zero.  The addresses are clamped into q
+// and the zeroing is a select, so the loads issue without branches.
 template <class T>
 __device__ __forceinline__ void load_q_frags(bf16x8 (&a)[T::NRT][T::NSTEP], const InLayout& L, int b,
                                              int tq0, int S, int lane) {
@@ -64,15 +65,24 @@ __device__ __forceinline__ void load_q_frags(bf16x8 (&a)[T::NRT][T::NSTEP], cons
         const int row = 32 * r + r32;
         const int t = tq0 + row / T::H;
         const int h = row % T::H;
-        const uint16_t* base = L.q + (long)t * L.q_t + (long)b * L.q_b + (long)h * L.D;
+        const bool tv = t < S;
+        const uint16_t* base = L.q + (long)min(t, S - 1) * L.q_t + (long)b * L.q_b + (long)h * L.D;
 #pragma unroll
         for (int st = 0; st < T::NSTEP; ++st) {
             const int d0 = 16 * st + 8 * hf;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (t < S && d0 < L.D) v = *reinterpret_cast<const u32x4*>(base + d0);
+            const bool ok = tv && (d0 < L.D);
+            u32x4 v = *reinterpret_cast<const u32x4*>(base + min(d0, L.D - 8));
+            if (!ok) v = u32x4{0u, 0u, 0u, 0u};
             a[r][st] = as_bf16x8(v);
         }
     }
+}
+
+// Static schedule of a persistent grid of G workgroups over nblk blocks
+// ordered longest first: workgroup w takes blocks w, 2G-1-w, 2G+w, 4G-1-w, ...
+// so each workgroup's pair of consecutive blocks has about the same total work.
+__device__ __forceinline__ int sched_block(int w, int G, int i) {
+    return (i & 1) ? (i + 1) * G - 1 - w : i * G + w;
 }
 
 // LDS position of the 16-byte chunk (column block cb, k-step st, fragment
@@ -86,18 +96,23 @@ __device__ __forceinline__ int stage_offset(int cb, int st, int lp) {
 }
 
 // Global -> registers: this thread's chunks of the key stage starting at s0.
+// Branch-free: rows past skv are clamped to the last key and index_dim chunks
+// past D to the last real chunk, so every access stays inside k.  Clamped rows
+// only feed scores of keys >= skv, which are never stored or selected, and
+// clamped chunks meet zero query entries (load_q_frags), adding exact zeros.
 template <class T>
-__device__ __forceinline__ void load_k_stage(u32x4 (&pf)[T::CPT], const InLayout& L, int b, int s0,
+__device__ __forceinline__ void load_k_stage(u32x4 (&pf)[T::CPT], const InLayout& L, const uint16_t* kb, int s0,
                                              int skv, int tid) {
+    const int rowlim = skv - 1 - s0;                       // uniform
+    const int dlim = (L.D >> 3) - 1;
+    const uint16_t* base = kb + (long)s0 * L.k_s;          // uniform
 #pragma unroll
     for (int i = 0; i < T::CPT; ++i) {
         const int e = tid + i * T::THREADS;
-        const int sl = e / T::CPK, d8 = e % T::CPK;
-        const int s = s0 + sl;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (s < skv && 8 * d8 < L.D)
-            v = *reinterpret_cast<const u32x4*>(L.k + (long)s * L.k_s + (long)b * L.k_b + 8 * d8);
-        pf[i] = v;
+        const int sl = min(e / T::CPK, rowlim);
+        const int d8 = min(e % T::CPK, dlim);
+        const uint32_t off = __umul24((uint32_t)sl, (uint32_t)L.k_s) + 8u * (uint32_t)d8;
+        pf[i] = *reinterpret_cast<const u32x4*>(base + off);
     }
 }
 
@@ -110,6 +125,33 @@ __device__ __forceinline__ void store_k_stage(uint8_t* stage, const u32x4 (&pf)[
         const int sl = e / T::CPK, d8 = e % T::CPK;
         const int cb = sl >> 5, st = d8 >> 1, lp = (sl & 31) + 32 * (d8 & 1);
         *reinterpret_cast<u32x4*>(stage + stage_offset<T>(cb, st, lp)) = pf[i];
+    }
+}
+
+// Key stages tile_lo .. tile_lo+ntile-1 stream through two LDS buffers.
+// The global loads of stage it+1 are issued right after the barrier that
+// opens stage it and are written to the other buffer once stage it has been
+// computed, so they have a whole stage of MFMA work to land.  (The compiler
+// waits for every outstanding vector-memory operation before those LDS
+// writes, so results a body wants to store should be issued early in the
+// next stage, not at the end of this one.)  body(it, stage) computes stage
+// tile_lo+it from its LDS copy.  Every thread of the workgroup must call
+// this with the same arguments.
+template <class T, class Body>
+__device__ __forceinline__ void stream_key_stages(const InLayout& L, int b, int skv, int tile_lo, int ntile,
+                                                  uint8_t (*lds)[T::STAGE_BYTES], int tid, Body&& body) {
+    const uint16_t* kb = L.k + (long)b * L.k_b;
+    const int s_first = tile_lo * T::KT;
+    u32x4 pf[T::CPT];
+    load_k_stage<T>(pf, L, kb, s_first, skv, tid);
+    store_k_stage<T>(lds[0], pf, tid);
+    __syncthreads();
+    for (int it = 0; it < ntile; ++it) {
+        const bool more = it + 1 < ntile;
+        if (more) load_k_stage<T>(pf, L, kb, s_first + (it + 1) * T::KT, skv, tid);
+        body(it, lds[it & 1]);
+        if (more) store_k_stage<T>(lds[(it + 1) & 1], pf, tid);
+        __syncthreads();
     }
 }
 
