@@ -187,6 +187,336 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(const float* __
     });
 }
 
+
+// ---------------------------------------------------------------- register-resident row top-k
+//
+// Rows of at most 8192 visible keys.  WPR waves (1 or 2) select one row; the
+// row sits in their registers (wave w of the row holds elements
+// w*VEC*256 + 256*j + 4*lane + m in slot [j][m]; slots past the row hold NaN)
+// and the row has a private LDS histogram.  The m-th best element in the
+// order (score descending, key index ascending) is located in two steps: a
+// 2048-bin histogram linear in the score between the row's min and max gives
+// the bin holding it (NaN slots land in per-lane trash bins past the end);
+// inside that bin it is ranked exactly (pairwise when the bin has at most 64
+// elements, else radix on order-preserving keys plus an ordered count for
+// ties).  With that element (vT, iT), an element is selected iff its score is
+// above vT, or equal to it with index <= iT; one ordered pass writes the
+// selection in ascending index order.  Scores are copied bit for bit.
+
+constexpr int kBins = 2048;
+constexpr int kRowThreads = 256;                     // threads per workgroup
+
+template <int WPR>
+struct RowShared {
+    uint32_t hist[kBins + 64 * WPR];                 // + one trash bin per lane
+    float cand_val[64];
+    int cand_idx[64];
+    float wmin[WPR], wmax[WPR];
+    int wcnt[WPR];
+    float cut_v;
+    int cut_i;
+};
+
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+// Bin (0..nbins-1) holding the need-th largest of hist[0..nbins) and the rank
+// of that element inside it (1-based, counted from the top).  One wave; lane l
+// owns bins [l*nbins/64, (l+1)*nbins/64).
+__device__ __forceinline__ void wave_find_bin(const uint32_t* hist, int nbins, int need, int lane, int& bin,
+                                              int& rank) {
+    const int bpl = nbins >> 6;
+    const int base = lane * bpl;
+    int local = 0;
+    for (int i = 0; i < bpl; ++i) local += (int)hist[base + i];
+    int v = local;                                   // inclusive suffix sum over lanes >= this one
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int u = __shfl_down(v, off, 64);
+        if (lane + off < 64) v += u;
+    }
+    int above = v - local;
+    int b = -1, r = 0;
+    if (above < need && need <= above + local) {
+        for (int i = bpl - 1; i >= 0; --i) {
+            const int h = (int)hist[base + i];
+            if (need <= above + h) { b = base + i; r = need - above; break; }
+            above += h;
+        }
+    }
+    const unsigned long long found = __ballot(b >= 0);
+    const int src = found ? __ffsll((long long)found) - 1 : 0;
+    bin = __shfl(b, src, 64);
+    rank = __shfl(r, src, 64);
+    if (bin < 0) { bin = 0; rank = 1; }
+}
+
+template <int WPR>
+__device__ __forceinline__ void row_sync() {
+    if constexpr (WPR > 1) __syncthreads();
+}
+
+template <int VEC, int WPR, int MINB>
+__global__ __launch_bounds__(kRowThreads, MINB) void topk_rows_reg_kernel(
+    const float* __restrict__ logits, int B, int S, int skv, int ratio, const int32_t* __restrict__ ks,
+    const int32_t* __restrict__ ke, int topk, float* __restrict__ scores, int32_t* __restrict__ indices) {
+    constexpr int RPB = kRowThreads / (64 * WPR);            // rows per workgroup
+    constexpr int SPAN = VEC * 256;                           // elements per wave
+    __shared__ RowShared<WPR> shr[RPB];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int rw = wv / WPR, wr = wv % WPR;                   // row slot in the block, wave within the row
+    RowShared<WPR>& sh = shr[rw];
+    const long rid = (long)blockIdx.x * RPB + rw;
+    const bool live = rid < (long)B * S;
+    const int b = live ? (int)(rid % B) : 0;
+    const int t = live ? S - 1 - (int)(rid / B) : 0;         // longest causal rows first
+    int lo = 0, hi = 0;
+    if (live) key_range(ks, ke, t, S, skv, ratio, lo, hi);
+    const int n = hi - lo;
+    const float* row = logits + ((long)b * S + t) * skv + lo;
+    float* so = scores + ((long)b * S + t) * topk;
+    int32_t* io = indices + ((long)b * S + t) * topk;
+    // every wave of the block reaches every barrier: rows that need no
+    // selection (or do not exist) only skip the work between them
+    const bool work = live && n > topk;
+    if (live && !work && wr == 0) {
+        for (int i = lane; i < n; i += 64) { so[i] = row[i]; io[i] = lo + i; }
+        for (int i = n + lane; i < topk; i += 64) { so[i] = neg_inf(); io[i] = -1; }
+    }
+    if constexpr (WPR == 1) {
+        if (!work) return;
+    }
+
+    // ---- load this wave's part of the row
+    const float qnan = __uint_as_float(0x7fc00000u);
+    const int ebase = wr * SPAN;                              // first element of this wave
+    const int nloc = work ? max(0, min(n - ebase, SPAN)) : 0;
+    const int nch = (nloc + 255) >> 8;
+    const bool vec_ok = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
+    float x[VEC][4];
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) {
+        const int e0 = j * 256 + 4 * lane;
+        x[j][0] = x[j][1] = x[j][2] = x[j][3] = qnan;
+        if (j < nch) {
+            if (vec_ok && e0 + 3 < nloc) {
+                const float4 y = *reinterpret_cast<const float4*>(row + ebase + e0);
+                x[j][0] = y.x; x[j][1] = y.y; x[j][2] = y.z; x[j][3] = y.w;
+            } else {
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    if (e0 + m < nloc) x[j][m] = row[ebase + e0 + m];
+            }
+        }
+    }
+
+    // ---- row min / max (NaN slots are ignored)
+    float vmin = __uint_as_float(0x7f800000u), vmax = neg_inf();
+#pragma unroll
+    for (int j = 0; j < VEC; ++j)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) { vmin = fminf(vmin, x[j][m]); vmax = fmaxf(vmax, x[j][m]); }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        vmin = fminf(vmin, __shfl_xor(vmin, off, 64));
+        vmax = fmaxf(vmax, __shfl_xor(vmax, off, 64));
+    }
+    if constexpr (WPR > 1) {
+        if (lane == 0) { sh.wmin[wr] = vmin; sh.wmax[wr] = vmax; }
+        for (int i = wr * 64 + lane; i < kBins + 64 * WPR; i += 64 * WPR) sh.hist[i] = 0u;
+        row_sync<WPR>();                                      // (1)
+        vmin = sh.wmin[0]; vmax = sh.wmax[0];
+#pragma unroll
+        for (int w2 = 1; w2 < WPR; ++w2) { vmin = fminf(vmin, sh.wmin[w2]); vmax = fmaxf(vmax, sh.wmax[w2]); }
+    } else {
+        for (int i = lane; i < kBins + 64; i += 64) sh.hist[i] = 0u;
+    }
+    const float span = vmax - vmin;
+    const bool binned = span > 0.0f && span < 3.0e38f;       // finite, non-degenerate range
+    const float scale = binned ? (float)kBins / span : 0.0f;
+    const int trash = kBins + 64 * wr + lane;
+    auto bin_with = [&](float v, float org, float sc) -> int {
+        const float f = (v - org) * sc;                       // NaN for NaN slots
+        return f >= 0.0f ? min((int)f, kBins - 1) : trash;
+    };
+
+    int bstar = 0, rstar = topk;
+    int cb = 1 << 30;                                         // boundary bin size; huge -> radix path
+    if (binned) {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) atomicAdd(&sh.hist[bin_with(x[j][m], vmin, scale)], 1u);
+        row_sync<WPR>();                                      // (2)
+        if (work) {
+            wave_find_bin(sh.hist, kBins, topk, lane, bstar, rstar);
+            cb = (int)sh.hist[bstar];
+        }
+    }
+    // Later passes recompute bins from copies of (vmin, scale) that the compiler
+    // cannot tie to the first pass, so no per-element bin stays in a register.
+    const float vmin2 = __shfl(vmin, 0, 64), scale2 = __shfl(scale, 0, 64);
+    auto bin_of = [&](float v) -> int { return bin_with(v, vmin2, scale2); };
+    const int ecut_lo = ebase;                                // this wave's first element index
+
+    if (__builtin_amdgcn_readfirstlane(cb) <= 64) {
+        // ---- small boundary bin: gather it in index order and rank pairwise
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < VEC; ++j)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) cnt += bin_of(x[j][m]) == bstar ? 1 : 0;
+        int run = 0;
+        if constexpr (WPR > 1) {
+            int tot = cnt;
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off, 64);
+            if (lane == 0) sh.wcnt[wr] = tot;
+            row_sync<WPR>();                                  // (3)
+            for (int w2 = 0; w2 < wr; ++w2) run += sh.wcnt[w2];
+        }
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+            int c = 0;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) c += bin_of(x[j][m]) == bstar ? 1 : 0;
+            const int incl = wave_incl_scan(c, lane);
+            int pos = run + incl - c;
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                if (bin_of(x[j][m]) == bstar) {
+                    sh.cand_val[pos] = x[j][m];
+                    sh.cand_idx[pos] = ecut_lo + j * 256 + 4 * lane + m;
+                    ++pos;
+                }
+            run += __shfl(incl, 63, 64);
+        }
+        row_sync<WPR>();                                      // (4)
+        if (wr == 0 && work) {
+            float vi = 0.0f;
+            int ii = 0x7fffffff, rank = 1 << 30;
+            if (lane < cb) {
+                vi = sh.cand_val[lane];
+                ii = sh.cand_idx[lane];
+                rank = 0;
+                for (int jj = 0; jj < cb; ++jj) {
+                    const float vj = sh.cand_val[jj];
+                    const int ij = sh.cand_idx[jj];
+                    rank += (vj > vi) || (vj == vi && ij < ii);
+                }
+            }
+            if (rank == rstar - 1) { sh.cut_v = vi; sh.cut_i = ii; }
+        }
+    } else {
+        // ---- large boundary bin (or unbinned row): radix select on the keys
+        // of its elements, 8-bit digits ...
+        uint32_t prefix = 0, pmask = 0;
+        int need = rstar;
+        for (int shift = 24; shift >= 0; shift -= 8) {
+            row_sync<WPR>();
+            for (int i = wr * 64 + lane; i < 256; i += 64 * WPR) sh.hist[i] = 0u;
+            row_sync<WPR>();
+#pragma unroll
+            for (int j = 0; j < VEC; ++j)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const float v = x[j][m];
+                    const bool in = (v == v) && (!binned || bin_of(v) == bstar);
+                    const uint32_t k = f32_to_key(v);
+                    if (in && (k & pmask) == prefix) atomicAdd(&sh.hist[(k >> shift) & 255u], 1u);
+                }
+            row_sync<WPR>();
+            int bb = 0, rr = 1;
+            if (work) wave_find_bin(sh.hist, 256, need, lane, bb, rr);
+            prefix |= (uint32_t)bb << shift;
+            pmask |= 255u << shift;
+            need = rr;
+        }
+        const float vt = key_to_f32(prefix);
+        // ... then the need-th smallest index among scores equal to it
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < VEC; ++j)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) cnt += (x[j][m] == vt) ? 1 : 0;
+        int run = 0;
+        if constexpr (WPR > 1) {
+            int tot = cnt;
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off, 64);
+            if (lane == 0) sh.wcnt[wr] = tot;
+            row_sync<WPR>();
+            for (int w2 = 0; w2 < wr; ++w2) run += sh.wcnt[w2];
+        }
+        int found = -1;
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+            int c = 0;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) c += (x[j][m] == vt) ? 1 : 0;
+            const int incl = wave_incl_scan(c, lane);
+            int r = run + incl - c;
+            if (r < need && need <= r + c) {
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    if (x[j][m] == vt) {
+                        ++r;
+                        if (r == need) found = ecut_lo + j * 256 + 4 * lane + m;
+                    }
+            }
+            run += __shfl(incl, 63, 64);
+        }
+        if (found >= 0 && work) { sh.cut_v = vt; sh.cut_i = found; }
+    }
+    row_sync<WPR>();                                          // (5) cut visible
+    const float vT = sh.cut_v;
+    const int iT = sh.cut_i;
+
+    // ---- ordered write of the selection
+    auto sel = [&](int j, int m) {
+        const float v = x[j][m];
+        return v > vT || (v == vT && ecut_lo + j * 256 + 4 * lane + m <= iT);
+    };
+    int run = 0;
+    if constexpr (WPR > 1) {
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < VEC; ++j)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) cnt += sel(j, m) ? 1 : 0;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
+        row_sync<WPR>();
+        if (lane == 0) sh.wcnt[wr] = cnt;
+        row_sync<WPR>();                                      // (6)
+        for (int w2 = 0; w2 < wr; ++w2) run += sh.wcnt[w2];
+    }
+    if (!work) return;
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) {
+        bool f[4];
+        int c = 0;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) { f[m] = sel(j, m); c += f[m] ? 1 : 0; }
+        const int incl = wave_incl_scan(c, lane);
+        int pos = run + incl - c;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            if (f[m] && pos < topk) {
+                so[pos] = x[j][m];
+                io[pos] = lo + ecut_lo + j * 256 + 4 * lane + m;
+                ++pos;
+            }
+        run += __shfl(incl, 63, 64);
+    }
+}
+
 __global__ __launch_bounds__(256) void gather_kernel(const float* __restrict__ logits,
                                                      const int32_t* __restrict__ idx, long total, int skv,
                                                      int topk, float* __restrict__ out) {
@@ -197,15 +527,31 @@ __global__ __launch_bounds__(256) void gather_kernel(const float* __restrict__ l
     out[i] = (v >= 0 && v < skv) ? logits[row * skv + v] : neg_inf();
 }
 
+template <int VEC, int WPR, int MINB>
+static void launch_reg(const TopkArgs& p) {
+    constexpr int rpb = kRowThreads / (64 * WPR);
+    const long rows = (long)p.B * p.S;
+    dim3 grid((unsigned)((rows + rpb - 1) / rpb));
+    hipLaunchKernelGGL((topk_rows_reg_kernel<VEC, WPR, MINB>), grid, dim3(kRowThreads), 0, p.stream, p.logits, p.B,
+                       p.S, p.Skv, p.ratio, p.ks, p.ke, p.topk, p.scores, p.indices);
+}
+
 hipError_t launch_topk_rows(const TopkArgs& p) {
-    dim3 grid((unsigned)((long)p.B * p.S));
-    const int cw = ((p.Skv + 63) / 64 + kTopkWaves - 1) / kTopkWaves;
-    if (cw <= 32)
-        hipLaunchKernelGGL(topk_rows_kernel<32>, grid, dim3(kTopkThreads), 0, p.stream, p.logits, p.B, p.S, p.Skv,
-                           p.ratio, p.ks, p.ke, p.topk, p.scores, p.indices);
-    else
-        hipLaunchKernelGGL(topk_rows_kernel<0>, grid, dim3(kTopkThreads), 0, p.stream, p.logits, p.B, p.S, p.Skv,
-                           p.ratio, p.ks, p.ke, p.topk, p.scores, p.indices);
+    // Measured on MI355X: one register-resident wave per row wins for rows of
+    // up to 2048 keys; longer rows go to the workgroup-per-row radix kernel
+    // (register cache up to 8192 keys, re-reads beyond).  The two-wave
+    // register variant (WPR = 2) measured slower at 8192 keys and is not used.
+    if (p.Skv <= 2048) {
+        launch_reg<8, 1, 4>(p);
+    } else {
+        dim3 grid((unsigned)((long)p.B * p.S));
+        if (p.Skv <= 8192)
+            hipLaunchKernelGGL(topk_rows_kernel<32>, grid, dim3(kTopkThreads), 0, p.stream, p.logits, p.B, p.S,
+                               p.Skv, p.ratio, p.ks, p.ke, p.topk, p.scores, p.indices);
+        else
+            hipLaunchKernelGGL(topk_rows_kernel<0>, grid, dim3(kTopkThreads), 0, p.stream, p.logits, p.B, p.S,
+                               p.Skv, p.ratio, p.ks, p.ke, p.topk, p.scores, p.indices);
+    }
     return hipGetLastError();
 }
 

@@ -370,3 +370,32 @@ def test_device_properties_logged():
         f"shared/block optin={getattr(p, 'shared_memory_per_block_optin', '?')} "
         f"L2={getattr(p, 'L2_cache_size', '?')} mem={p.total_memory >> 30} GiB")
     assert "gfx950" in getattr(p, "gcnArchName", "gfx950")
+
+
+@pytest.mark.parametrize("Skv", [300, 2048, 3000, 4096, 6000, 8192])
+def test_topk_from_logits_edge_rows_bitwise(Skv):
+    # Every size class of the row kernel, with rows that stress each branch:
+    # all-equal scores (degenerate range), a few distinct values (large
+    # boundary bins), -inf inside the range (non-finite range), signed zeros,
+    # misaligned row starts (ks odd) and ragged ends.
+    g = torch.Generator().manual_seed(Skv)
+    B, S = 2, 24
+    lg = torch.randn(B, S, Skv, generator=g)
+    lg[:, 0] = 0.5                                       # all equal
+    lg[:, 1] = torch.randint(0, 3, (B, Skv), generator=g).float()
+    lg[:, 2, ::7] = float("-inf")
+    lg[:, 3, ::5] = -0.0
+    lg[:, 3, 1::5] = 0.0
+    lg[:, 4] = torch.randn(B, Skv, generator=g) * 1e-30     # tiny range
+    lg[:, 5] = torch.randn(B, Skv, generator=g) * 1e30      # huge range
+    ks = torch.randint(0, max(1, Skv // 5), (S,), generator=g, dtype=torch.int32)
+    ks[::3] |= 1
+    ke = torch.clamp(ks + torch.randint(Skv // 3, Skv + 10, (S,), generator=g, dtype=torch.int32), max=Skv)
+    for tk in (1, 17, min(1000, Skv // 3), min(2048, Skv // 2)):
+        log(f"Skv={Skv} topk={tk}")
+        sc, ix = lx.topk_from_logits(dev(lg), 1, tk, dev(ks), dev(ke))
+        sc, ix = sc.cpu().numpy(), ix.cpu().numpy()
+        for b in range(B):
+            want_s, want_i = oracle.topk_select(lg[b].numpy().astype(np.float64), ks.numpy(), ke.numpy(), tk)
+            assert np.array_equal(ix[b], want_i), (Skv, tk, b)
+            assert np.array_equal(sc[b].astype(np.float64), want_s), (Skv, tk, b)
