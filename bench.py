@@ -5,11 +5,13 @@
 A step is one forward of the V4 lightning indexer on the 32K workload
 (batch 1, seqlen 32768, seqlen_kv 8192, 64 heads, index_dim 128,
 compress_ratio 4, topk 2048): causally masked scoring of every valid
-(query, key) pair plus the per-query top-k, through lix_topk's fused path
-(no logits in HBM).  The same run also times, on the same inputs, the
-materialized path (lix_indexer_logits + lix_topk over the logits), the
-gather lix_topk_scores at the selected indices, and lix_indexer_scores_v41 on
-the V4.1 workload (batch 1, 16384 queries, 4096 keys, packed documents).
+(query, key) pair plus the per-query top-k.  Two routes compute it and both
+are timed on the same inputs: lix_topk's fused path (no logits in HBM) and
+the materialized path (lix_indexer_logits, then lix_topk over the logits);
+the step is the faster one, named in config.path.  The same run also times
+the gather lix_topk_scores at the selected indices and
+lix_indexer_scores_v41 on the V4.1 workload (batch 1, 16384 queries, 4096
+keys, packed documents).
 
 Prints one JSON line.  `value` is causally valid TFLOP/s (2*H*D per visible
 pair) over the whole step; queries/s are reported beside it.  Kernel
@@ -168,7 +170,7 @@ def main():
         profile_part(args, dev, q, k, w, cfg)
         return
     log("timing the fused step")
-    fused_ms, fused_wall = time_loop(lambda: lx.topk(q, k, w, c, tk), args.steps, args.warmup)
+    fused_ms, _ = time_loop(lambda: lx.topk(q, k, w, c, tk), args.steps, args.warmup)
     sc_f, ix_f = lx.topk(q, k, w, c, tk)
 
     parts = {"fused_topk_ms": fused_ms}
@@ -215,7 +217,15 @@ def main():
             "v41_allowed_tflops": 2.0 * H * D * allowed_pairs / v41_ms / 1e9,
         })
 
-    value = flop / fused_ms / 1e9
+    # The step is the faster of the two routes to the same forward; both are reported.
+    if args.part == "all" and parts["materialized_total_ms"] < fused_ms:
+        step_ms = parts["materialized_total_ms"]
+        path = "materialized: lix_indexer_logits then lix_topk over the logits"
+        roof_kernel = {"name": "v4_logits_kernel", "ms": parts["materialized_logits_ms"]}
+    else:
+        step_ms = fused_ms
+        path = "fused: lix_topk scoring and selecting on chip"
+    value = flop / step_ms / 1e9
     achieved = flop / roof_kernel["ms"] / 1e9
     result = {
         "metric": METRIC,
@@ -224,17 +234,16 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": fused_ms,
-        "wall_ms_per_step": fused_wall,
+        "ms_per_step": step_ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "32k lightning-indexer forward (fused scoring + top-k)", "batch": B,
+        "config": {"workload": "32k lightning-indexer forward (scoring + top-k)", "path": path, "batch": B,
                    "seqlen": S, "seqlen_kv": Skv, "heads": H, "index_dim": D, "compress_ratio": c,
                    "topk": tk, "causal_valid_pairs": pairs},
-        "queries_per_s": B * S / (fused_ms * 1e-3),
+        "queries_per_s": B * S / (step_ms * 1e-3),
         "roofline": {"bound": "mfma", "kernel": roof_kernel["name"], "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": None},
