@@ -116,7 +116,8 @@ __global__ __launch_bounds__(256) void v4_fused_topk_kernel(InLayout L, const fl
                                                             int32_t* __restrict__ indices) {
     using T = Tiling<H, DP>;
     static_assert(H >= 8, "the fused path keeps each query inside one lane pair");
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][T::STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t lds0[T::STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t lds1[T::STAGE_BYTES];
     __shared__ uint32_t hist_all[T::NWAVE][256];
     extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
 
@@ -172,27 +173,28 @@ __global__ __launch_bounds__(256) void v4_fused_topk_kernel(InLayout L, const fl
                 wr[r][i] = (t < S) ? w[((long)t * B + b) * H + h] : 0.0f;
             }
 
-        stream_key_stages<T>(L, b, skv, tile_lo, ntile, lds, tid, [&](int it, const uint8_t* stage) {
+        stream_key_stages<T>(L, b, skv, tile_lo, ntile, lds0, lds1, tid, [&](int it, const uint8_t* stage) {
             const int s0 = (tile_lo + it) * T::KT;
             const bool active = (s0 < wave_hi) && (s0 + T::KT > wave_lo);
             if (!active) return;
             float part[T::NCB][T::QW];
 #pragma unroll
-            for (int cb = 0; cb < T::NCB; ++cb) {
+            for (int cb = 0; cb < T::NCB; ++cb)
 #pragma unroll
                 for (int j = 0; j < T::QW; ++j) part[cb][j] = 0.0f;
-                f32x16 acc[T::NRT];
-                mfma_block<T>(acc, a, stage, cb, lane);
+            // same accumulation order as the materialized logits kernel
+            two_block_stage<T>(
+                a, stage, lane,
+                [&](const f32x16 (&acc)[T::NRT], int r, int i) {
+                    part[0][T::slot(r, i)] = fmaf(wr[r][i], relu(acc[r][i]), part[0][T::slot(r, i)]);
+                },
+                [&](const f32x16 (&acc)[T::NRT], int r, int i) {
+                    part[1][T::slot(r, i)] = fmaf(wr[r][i], relu(acc[r][i]), part[1][T::slot(r, i)]);
+                });
 #pragma unroll
-                for (int r = 0; r < T::NRT; ++r)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int j = T::slot(r, i);
-                        part[cb][j] = fmaf(wr[r][i], relu(acc[r][i]), part[cb][j]);
-                    }
+            for (int cb = 0; cb < T::NCB; ++cb)
 #pragma unroll
                 for (int j = 0; j < T::QW; ++j) part[cb][j] = xor32_add(part[cb][j]);
-            }
 
             // Lane l holds key s0 + l of each of its queries.
             const int s = s0 + lane;

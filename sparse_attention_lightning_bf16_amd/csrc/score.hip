@@ -38,7 +38,8 @@ __global__ __launch_bounds__(256) void v4_logits_kernel(InLayout L, const float*
                                                         int skv, int ratio, const int32_t* __restrict__ ks,
                                                         const int32_t* __restrict__ ke, float* __restrict__ out) {
     using T = Tiling<H, DP>;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][T::STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t lds0[T::STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t lds1[T::STAGE_BYTES];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5;
     const int nqb = (S + T::QB - 1) / T::QB;
@@ -117,28 +118,28 @@ __global__ __launch_bounds__(256) void v4_logits_kernel(InLayout L, const float*
             }
         };
         if (ntile > 0) {
-            stream_key_stages<T>(L, b, skv, tile_lo, ntile, lds, tid, [&](int it, const uint8_t* stage) {
+            stream_key_stages<T>(L, b, skv, tile_lo, ntile, lds0, lds1, tid, [&](int it, const uint8_t* stage) {
                 flush();
                 const int s0 = (tile_lo + it) * T::KT;
                 const bool active = (s0 < wave_hi) && (s0 + T::KT > wave_lo);
 #pragma unroll
-                for (int cb = 0; cb < T::NCB; ++cb) {
+                for (int cb = 0; cb < T::NCB; ++cb)
 #pragma unroll
                     for (int q = 0; q < T::QW; ++q) pend[cb][q] = 0.0f;
-                    if (active) {
-                        f32x16 acc[T::NRT];
-                        mfma_block<T>(acc, a, stage, cb, lane);
+                if (active) {
+                    two_block_stage<T>(
+                        a, stage, lane,
+                        [&](const f32x16 (&acc)[T::NRT], int r, int i) {
+                            pend[0][T::slot(r, i)] = fmaf(wr[r][i], relu(acc[r][i]), pend[0][T::slot(r, i)]);
+                        },
+                        [&](const f32x16 (&acc)[T::NRT], int r, int i) {
+                            pend[1][T::slot(r, i)] = fmaf(wr[r][i], relu(acc[r][i]), pend[1][T::slot(r, i)]);
+                        });
+                    if constexpr (H >= 8) {
 #pragma unroll
-                        for (int r = 0; r < T::NRT; ++r)
-#pragma unroll
-                            for (int ii = 0; ii < 16; ++ii) {
-                                const int q = T::slot(r, ii);
-                                pend[cb][q] = fmaf(wr[r][ii], relu(acc[r][ii]), pend[cb][q]);
-                            }
-                        if constexpr (H >= 8) {
+                        for (int cb = 0; cb < T::NCB; ++cb)
 #pragma unroll
                             for (int q = 0; q < T::QW; ++q) pend[cb][q] = xor32_add(pend[cb][q]);
-                        }
                     }
                 }
                 pend_s0 = s0;
@@ -163,7 +164,8 @@ __global__ __launch_bounds__(256) void v41_scores_kernel(InLayout L, const uint1
                                                          const uint8_t* __restrict__ allowed, int B, int Lq,
                                                          int G, uint16_t* __restrict__ out) {
     using T = Tiling<H, DP>;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][T::STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t lds0[T::STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t lds1[T::STAGE_BYTES];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5;
     const int nqb = (Lq + T::QB - 1) / T::QB;
@@ -186,7 +188,7 @@ __global__ __launch_bounds__(256) void v41_scores_kernel(InLayout L, const uint1
         }
 
     const uint16_t kNegInfBf16 = 0xff80u;
-    stream_key_stages<T>(L, b, G, 0, ntile, lds, tid, [&](int it, const uint8_t* stage) {
+    stream_key_stages<T>(L, b, G, 0, ntile, lds0, lds1, tid, [&](int it, const uint8_t* stage) {
         const int s0 = it * T::KT;
         // Visibility of this lane's keys for each of its queries.
         bool vis[T::NCB][T::QW];
@@ -205,24 +207,23 @@ __global__ __launch_bounds__(256) void v41_scores_kernel(InLayout L, const uint1
 
         float part[T::NCB][T::QW];
 #pragma unroll
-        for (int cb = 0; cb < T::NCB; ++cb) {
+        for (int cb = 0; cb < T::NCB; ++cb)
 #pragma unroll
             for (int j = 0; j < T::QW; ++j) part[cb][j] = 0.0f;
-            if (active) {
-                f32x16 acc[T::NRT];
-                mfma_block<T>(acc, a, stage, cb, lane);
+        if (active) {
+            auto term = [&](float acc_v, float w_v) {
+                const float rr = round_bf16(relu(acc_v));    // bf16(d); ReLU commutes with rounding
+                return round_bf16(w_v * rr);                  // exact product, then bf16
+            };
+            two_block_stage<T>(
+                a, stage, lane,
+                [&](const f32x16 (&acc)[T::NRT], int r, int i) { part[0][T::slot(r, i)] += term(acc[r][i], wr[r][i]); },
+                [&](const f32x16 (&acc)[T::NRT], int r, int i) { part[1][T::slot(r, i)] += term(acc[r][i], wr[r][i]); });
+            if constexpr (H >= 8) {
 #pragma unroll
-                for (int r = 0; r < T::NRT; ++r)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int j = T::slot(r, i);
-                        const float rr = round_bf16(relu(acc[r][i]));   // bf16(d); ReLU commutes with rounding
-                        part[cb][j] += round_bf16(wr[r][i] * rr);       // exact product, then bf16
-                    }
-                if constexpr (H >= 8) {
+                for (int cb = 0; cb < T::NCB; ++cb)
 #pragma unroll
                     for (int j = 0; j < T::QW; ++j) part[cb][j] = xor32_add(part[cb][j]);
-                }
             }
         }
 

@@ -86,71 +86,64 @@ __device__ __forceinline__ int sched_block(int w, int G, int i) {
 }
 
 // LDS position of the 16-byte chunk (column block cb, k-step st, fragment
-// lane lp).  Within each 1 KiB fragment block the lane slot is XOR-swizzled
-// so that the staging stores of 16 consecutive threads hit distinct banks;
-// the fragment reads of a wave stay a permutation of one 1 KiB block.
+// lane lp): 1 KiB blocks in fragment order, lane-linear inside a block, so a
+// wave's fragment read and a direct global->LDS load of one block both touch
+// one contiguous 1 KiB (no bank conflicts).
 template <class T>
 __device__ __forceinline__ int stage_offset(int cb, int st, int lp) {
-    const int sw = (2 * st + (lp >> 5)) & 15;
-    return ((cb * T::NSTEP + st) * kWave + (lp ^ sw)) * 16;
+    return ((cb * T::NSTEP + st) * kWave + lp) * 16;
 }
 
-// Global -> registers: this thread's chunks of the key stage starting at s0.
-// Branch-free: rows past skv are clamped to the last key and index_dim chunks
-// past D to the last real chunk, so every access stays inside k.  Clamped rows
-// only feed scores of keys >= skv, which are never stored or selected, and
-// clamped chunks meet zero query entries (load_q_frags), adding exact zeros.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Direct global->LDS loads of the key stage starting at s0: each of the stage's
+// NCB*NSTEP fragment blocks is one 64-lane load of 16 bytes per lane, written
+// by the hardware to block base + 16*lane; wave w issues blocks w, w+NWAVE, ...
+// Lane lp of block (cb, st) fetches key row s0 + 32cb + lp%32, index_dim chunk
+// 2st + lp/32.  Rows past skv are clamped to the last key and chunks past D to
+// the last real chunk, so every access stays inside k; clamped rows only feed
+// scores of keys >= skv, which are never stored or selected, and clamped chunks
+// meet zero query entries (load_q_frags), adding exact zeros.
 template <class T>
-__device__ __forceinline__ void load_k_stage(u32x4 (&pf)[T::CPT], const InLayout& L, const uint16_t* kb, int s0,
-                                             int skv, int tid) {
-    const int rowlim = skv - 1 - s0;                       // uniform
+__device__ __forceinline__ void dma_k_stage(uint8_t* stage, const InLayout& L, const uint16_t* kb, int s0, int skv,
+                                            int wave, int lane) {
+    const int rowlim = skv - 1 - s0;                      // uniform
     const int dlim = (L.D >> 3) - 1;
-    const uint16_t* base = kb + (long)s0 * L.k_s;          // uniform
+    const uint16_t* base = kb + (long)s0 * L.k_s;         // uniform
 #pragma unroll
-    for (int i = 0; i < T::CPT; ++i) {
-        const int e = tid + i * T::THREADS;
-        const int sl = min(e / T::CPK, rowlim);
-        const int d8 = min(e % T::CPK, dlim);
-        const uint32_t off = __umul24((uint32_t)sl, (uint32_t)L.k_s) + 8u * (uint32_t)d8;
-        pf[i] = *reinterpret_cast<const u32x4*>(base + off);
+    for (int blk = wave; blk < T::NCB * T::NSTEP; blk += T::NWAVE) {
+        const int cb = blk / T::NSTEP, st = blk % T::NSTEP;
+        const int row = min(32 * cb + (lane & 31), rowlim);
+        const int d8 = min(2 * st + (lane >> 5), dlim);
+        const uint32_t off = __umul24((uint32_t)row, (uint32_t)L.k_s) + 8u * (uint32_t)d8;
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base + off),
+                                         (lds_ptr_t)(stage + blk * kWave * 16), 16, 0, 0);
     }
 }
 
-// Registers -> LDS in fragment order.
-template <class T>
-__device__ __forceinline__ void store_k_stage(uint8_t* stage, const u32x4 (&pf)[T::CPT], int tid) {
-#pragma unroll
-    for (int i = 0; i < T::CPT; ++i) {
-        const int e = tid + i * T::THREADS;
-        const int sl = e / T::CPK, d8 = e % T::CPK;
-        const int cb = sl >> 5, st = d8 >> 1, lp = (sl & 31) + 32 * (d8 & 1);
-        *reinterpret_cast<u32x4*>(stage + stage_offset<T>(cb, st, lp)) = pf[i];
-    }
-}
-
-// Key stages tile_lo .. tile_lo+ntile-1 stream through two LDS buffers.
-// The global loads of stage it+1 are issued right after the barrier that
-// opens stage it and are written to the other buffer once stage it has been
-// computed, so they have a whole stage of MFMA work to land.  (The compiler
-// waits for every outstanding vector-memory operation before those LDS
-// writes, so results a body wants to store should be issued early in the
-// next stage, not at the end of this one.)  body(it, stage) computes stage
-// tile_lo+it from its LDS copy.  Every thread of the workgroup must call
-// this with the same arguments.
+// Key stages tile_lo .. tile_lo+ntile-1 stream through two LDS buffers (two
+// separate arrays, so the compiler can tell that loads into one never alias
+// reads of the other).  The loads of stage it+1 are issued right after the
+// barrier that opens stage it and land while stage it is computed; the
+// barrier's memory wait then covers them.  (That wait also covers every other
+// outstanding vector-memory operation, so results a body stores should be
+// issued early in the next stage.)  body(it, stage) computes stage
+// tile_lo+it.  Every thread of the workgroup calls this with the same arguments.
 template <class T, class Body>
 __device__ __forceinline__ void stream_key_stages(const InLayout& L, int b, int skv, int tile_lo, int ntile,
-                                                  uint8_t (*lds)[T::STAGE_BYTES], int tid, Body&& body) {
+                                                  uint8_t* lds0, uint8_t* lds1, int tid, Body&& body) {
     const uint16_t* kb = L.k + (long)b * L.k_b;
     const int s_first = tile_lo * T::KT;
-    u32x4 pf[T::CPT];
-    load_k_stage<T>(pf, L, kb, s_first, skv, tid);
-    store_k_stage<T>(lds[0], pf, tid);
+    const int wave = tid >> 6, lane = tid & 63;
+    dma_k_stage<T>(lds0, L, kb, s_first, skv, wave, lane);
     __syncthreads();
-    for (int it = 0; it < ntile; ++it) {
-        const bool more = it + 1 < ntile;
-        if (more) load_k_stage<T>(pf, L, kb, s_first + (it + 1) * T::KT, skv, tid);
-        body(it, lds[it & 1]);
-        if (more) store_k_stage<T>(lds[(it + 1) & 1], pf, tid);
+    for (int it = 0; it < ntile; it += 2) {
+        if (it + 1 < ntile) dma_k_stage<T>(lds1, L, kb, s_first + (it + 1) * T::KT, skv, wave, lane);
+        body(it, lds0);
+        __syncthreads();
+        if (it + 1 >= ntile) break;
+        if (it + 2 < ntile) dma_k_stage<T>(lds0, L, kb, s_first + (it + 2) * T::KT, skv, wave, lane);
+        body(it + 1, lds1);
         __syncthreads();
     }
 }
@@ -168,6 +161,47 @@ __device__ __forceinline__ void mfma_block(f32x16 (&acc)[T::NRT], const bf16x8 (
 #pragma unroll
         for (int r = 0; r < T::NRT; ++r) acc[r] = mfma_32x32x16(a[r][st], bfrag, acc[r]);
     }
+}
+
+// B fragment of column block cb, k-step st of a staged tile.
+template <class T>
+__device__ __forceinline__ bf16x8 b_frag(const uint8_t* stage, int cb, int st, int lane) {
+    return as_bf16x8(*reinterpret_cast<const u32x4*>(stage + stage_offset<T>(cb, st, lane)));
+}
+
+// One stage of two column blocks with the epilogue of block 0 interleaved,
+// by source order, with the MFMA chain of block 1: at each k-step of block 1
+// the wave issues that step's MFMAs and then epilogue work on one eighth of
+// block 0's accumulators, and a scheduling fence keeps the compiler from
+// regrouping them, so the matrix pipe and the VALU work at the same time
+// within the wave.  Block 1's epilogue follows.  epi(acc, r, i) handles
+// accumulator element i of row tile r of a finished chain.
+template <class T, class Epi0, class Epi1>
+__device__ __forceinline__ void two_block_stage(const bf16x8 (&a)[T::NRT][T::NSTEP], const uint8_t* stage,
+                                                int lane, Epi0&& epi0, Epi1&& epi1) {
+    static_assert(T::NCB == 2 && 16 % T::NSTEP == 0, "two column blocks, epilogue split over k-steps");
+    constexpr int PER = 16 / T::NSTEP;                    // accumulator elements per row tile per step
+    f32x16 acc0[T::NRT], acc1[T::NRT];
+    mfma_block<T>(acc0, a, stage, 0, lane);
+#pragma unroll
+    for (int r = 0; r < T::NRT; ++r) acc1[r] = f32x16{};
+    bf16x8 bn = b_frag<T>(stage, 1, 0, lane);
+#pragma unroll
+    for (int st = 0; st < T::NSTEP; ++st) {
+        const bf16x8 bc = bn;
+        if (st + 1 < T::NSTEP) bn = b_frag<T>(stage, 1, st + 1, lane);
+#pragma unroll
+        for (int r = 0; r < T::NRT; ++r) acc1[r] = mfma_32x32x16(a[r][st], bc, acc1[r]);
+#pragma unroll
+        for (int r = 0; r < T::NRT; ++r)
+#pragma unroll
+            for (int i = st * PER; i < (st + 1) * PER; ++i) epi0(acc0, r, i);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int r = 0; r < T::NRT; ++r)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) epi1(acc1, r, i);
 }
 
 // Query handled by slot j of this lane.
