@@ -73,8 +73,16 @@ __device__ __forceinline__ void key_range(const int32_t* __restrict__ ks_arr, co
     if (hi < lo) hi = lo;
 }
 
-// Wave-wide butterfly add across the two 32-lane halves.
-__device__ __forceinline__ float xor32_add(float v) { return v + __shfl_xor(v, 32, 64); }
+// v(lane) + v(lane ^ 32) in every lane.  v_permlane32_swap exchanges the
+// upper half of its first operand with the lower half of its second; with v
+// in both, the two results hold v's lower and upper halves in every lane, so
+// no LDS round trip is needed.  The sum is the same in both halves (fp add
+// commutes).
+__device__ __forceinline__ float xor32_add(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Fill p[0..n) with -inf using 16-byte stores where alignment allows.
 __device__ __forceinline__ void fill_neg_inf(float* __restrict__ p, long n, int tid, int nthreads) {

@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void v4_fused_topk_kernel(InLayout L, const fl
                                                             const int32_t* __restrict__ ke, int topk, int cap,
                                                             float* __restrict__ scores,
                                                             int32_t* __restrict__ indices) {
-    using T = Tiling<H, DP>;
+    using T = Tiling<H, DP, 64>;
     static_assert(H >= 8, "the fused path keeps each query inside one lane pair");
     __shared__ __attribute__((aligned(16))) uint8_t lds0[T::STAGE_BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t lds1[T::STAGE_BYTES];
@@ -183,14 +183,9 @@ __global__ __launch_bounds__(256) void v4_fused_topk_kernel(InLayout L, const fl
 #pragma unroll
                 for (int j = 0; j < T::QW; ++j) part[cb][j] = 0.0f;
             // same accumulation order as the materialized logits kernel
-            two_block_stage<T>(
-                a, stage, lane,
-                [&](const f32x16 (&acc)[T::NRT], int r, int i) {
-                    part[0][T::slot(r, i)] = fmaf(wr[r][i], relu(acc[r][i]), part[0][T::slot(r, i)]);
-                },
-                [&](const f32x16 (&acc)[T::NRT], int r, int i) {
-                    part[1][T::slot(r, i)] = fmaf(wr[r][i], relu(acc[r][i]), part[1][T::slot(r, i)]);
-                });
+            rolling_stage<T>(a, stage, lane, [&](int cb, const f32x16 (&acc)[T::NRT], int r, int i) {
+                part[cb][T::slot(r, i)] = fmaf(wr[r][i], relu(acc[r][i]), part[cb][T::slot(r, i)]);
+            });
 #pragma unroll
             for (int cb = 0; cb < T::NCB; ++cb)
 #pragma unroll
@@ -248,7 +243,7 @@ __global__ __launch_bounds__(256) void v4_fused_topk_kernel(InLayout L, const fl
 // Largest candidate capacity (multiple of 64) that fits next to the staging tiles.
 template <int H, int DP>
 static int fused_cap(int topk) {
-    using T = Tiling<H, DP>;
+    using T = Tiling<H, DP, 64>;
     const long fixed = 2L * T::STAGE_BYTES + T::NWAVE * 256 * 4;
     const long per_entry = (long)T::QB * 6;
     long max_cap = ((kFusedLdsBudget - fixed) / per_entry) & ~63L;
@@ -260,7 +255,7 @@ static int fused_cap(int topk) {
 
 template <int H, int DP>
 static hipError_t launch_fused_t(const FusedArgs& p) {
-    using T = Tiling<H, DP>;
+    using T = Tiling<H, DP, 64>;
     const int cap = fused_cap<H, DP>(p.topk);
     if (cap < 0) return hipErrorInvalidValue;
     const size_t dyn = (size_t)T::QB * cap * 6;

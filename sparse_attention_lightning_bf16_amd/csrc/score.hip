@@ -34,7 +34,7 @@ __device__ __forceinline__ void load_weights_f32(float (&wr)[T::NRT][16], const 
 // ---------------------------------------------------------------- V4 logits
 
 template <int H, int DP>
-__global__ __launch_bounds__(256) void v4_logits_kernel(InLayout L, const float* __restrict__ w, int B, int S,
+__global__ __launch_bounds__(256, stage_min_waves(H, DP)) void v4_logits_kernel(InLayout L, const float* __restrict__ w, int B, int S,
                                                         int skv, int ratio, const int32_t* __restrict__ ks,
                                                         const int32_t* __restrict__ ke, float* __restrict__ out) {
     using T = Tiling<H, DP>;
@@ -90,16 +90,20 @@ __global__ __launch_bounds__(256) void v4_logits_kernel(InLayout L, const float*
         auto flush = [&]() {
             if (pend_s0 < 0) return;
             if constexpr (H >= 8) {
-                // Both halves hold full sums; the lower half writes column block 0,
-                // the upper half column block 1: 64 consecutive keys per query.
-                const int s = pend_s0 + lane;
+                // Both halves hold full sums; per pair of column blocks the lower
+                // half writes the first and the upper half the second: 64
+                // consecutive keys per query and store.
 #pragma unroll
-                for (int q = 0; q < T::QW; ++q) {
-                    const int t = tq0 + q;
-                    if (t < S && s < skv) {
-                        const float v = pick(hf != 0, pend[1][q], pend[0][q]);
-                        __builtin_nontemporal_store((s >= lo_s[q] && s < hi_s[q]) ? v : neg_inf(),
-                                                    out_b + (long)t * skv + s);
+                for (int cp = 0; cp < T::NCB / 2; ++cp) {
+                    const int s = pend_s0 + 64 * cp + lane;
+#pragma unroll
+                    for (int q = 0; q < T::QW; ++q) {
+                        const int t = tq0 + q;
+                        if (t < S && s < skv) {
+                            const float v = pick(hf != 0, pend[2 * cp + 1][q], pend[2 * cp][q]);
+                            __builtin_nontemporal_store((s >= lo_s[q] && s < hi_s[q]) ? v : neg_inf(),
+                                                        out_b + (long)t * skv + s);
+                        }
                     }
                 }
             } else {
@@ -127,14 +131,9 @@ __global__ __launch_bounds__(256) void v4_logits_kernel(InLayout L, const float*
 #pragma unroll
                     for (int q = 0; q < T::QW; ++q) pend[cb][q] = 0.0f;
                 if (active) {
-                    two_block_stage<T>(
-                        a, stage, lane,
-                        [&](const f32x16 (&acc)[T::NRT], int r, int i) {
-                            pend[0][T::slot(r, i)] = fmaf(wr[r][i], relu(acc[r][i]), pend[0][T::slot(r, i)]);
-                        },
-                        [&](const f32x16 (&acc)[T::NRT], int r, int i) {
-                            pend[1][T::slot(r, i)] = fmaf(wr[r][i], relu(acc[r][i]), pend[1][T::slot(r, i)]);
-                        });
+                    rolling_stage<T>(a, stage, lane, [&](int cb, const f32x16 (&acc)[T::NRT], int r, int i) {
+                        pend[cb][T::slot(r, i)] = fmaf(wr[r][i], relu(acc[r][i]), pend[cb][T::slot(r, i)]);
+                    });
                     if constexpr (H >= 8) {
 #pragma unroll
                         for (int cb = 0; cb < T::NCB; ++cb)
@@ -160,7 +159,7 @@ __global__ __launch_bounds__(256) void v4_logits_kernel(InLayout L, const float*
 // ---------------------------------------------------------------- V4.1 scores
 
 template <int H, int DP>
-__global__ __launch_bounds__(256) void v41_scores_kernel(InLayout L, const uint16_t* __restrict__ wts,
+__global__ __launch_bounds__(256, stage_min_waves(H, DP)) void v41_scores_kernel(InLayout L, const uint16_t* __restrict__ wts,
                                                          const uint8_t* __restrict__ allowed, int B, int Lq,
                                                          int G, uint16_t* __restrict__ out) {
     using T = Tiling<H, DP>;
@@ -215,10 +214,9 @@ __global__ __launch_bounds__(256) void v41_scores_kernel(InLayout L, const uint1
                 const float rr = round_bf16(relu(acc_v));    // bf16(d); ReLU commutes with rounding
                 return round_bf16(w_v * rr);                  // exact product, then bf16
             };
-            two_block_stage<T>(
-                a, stage, lane,
-                [&](const f32x16 (&acc)[T::NRT], int r, int i) { part[0][T::slot(r, i)] += term(acc[r][i], wr[r][i]); },
-                [&](const f32x16 (&acc)[T::NRT], int r, int i) { part[1][T::slot(r, i)] += term(acc[r][i], wr[r][i]); });
+            rolling_stage<T>(a, stage, lane, [&](int cb, const f32x16 (&acc)[T::NRT], int r, int i) {
+                part[cb][T::slot(r, i)] += term(acc[r][i], wr[r][i]);
+            });
             if constexpr (H >= 8) {
 #pragma unroll
                 for (int cb = 0; cb < T::NCB; ++cb)
@@ -233,7 +231,7 @@ __global__ __launch_bounds__(256) void v41_scores_kernel(InLayout L, const uint1
 #pragma unroll
             for (int j = 0; j < T::QW; ++j) {
                 if constexpr (H >= 8) {
-                    if (hf != cb) continue;            // lower half stores block 0, upper block 1
+                    if (hf != (cb & 1)) continue;      // lower half stores even blocks, upper half odd
                 } else {
                     if ((j % (2 * T::half_step())) >= T::half_step()) continue;
                 }

@@ -16,7 +16,13 @@
 
 namespace lix {
 
-template <int H_, int DP_>
+// Keys per LDS stage: 128 where the rolling epilogue pipeline fits two
+// waves per SIMD (H <= 64, index_dim <= 128), else 64.
+constexpr int default_kt(int H, int DP) { return (H <= 64 && DP <= 128) ? 128 : 64; }
+// Waves per SIMD the register allocator is held to for those shapes.
+constexpr int stage_min_waves(int H, int DP) { return (H >= 16 && default_kt(H, DP) == 128) ? 2 : 1; }
+
+template <int H_, int DP_, int KT_ = default_kt(H_, DP_)>
 struct Tiling {
     static constexpr int H = H_;                    // heads (power of two, <= 128)
     static constexpr int DP = DP_;                  // index_dim padded up to 32/64/128/256
@@ -27,7 +33,7 @@ struct Tiling {
     static constexpr int NWAVE = 4;
     static constexpr int THREADS = NWAVE * kWave;
     static constexpr int QB = QW * NWAVE;           // queries per workgroup
-    static constexpr int KT = 64;                   // keys per LDS stage
+    static constexpr int KT = KT_;                  // keys per LDS stage
     static constexpr int NCB = KT / 32;             // 32-key column blocks per stage
     static constexpr int STAGE_BYTES = KT * DP * 2;
     static constexpr int CHUNKS = KT * DP / 8;      // 16-byte chunks per stage
@@ -169,39 +175,52 @@ __device__ __forceinline__ bf16x8 b_frag(const uint8_t* stage, int cb, int st, i
     return as_bf16x8(*reinterpret_cast<const u32x4*>(stage + stage_offset<T>(cb, st, lane)));
 }
 
-// One stage of two column blocks with the epilogue of block 0 interleaved,
-// by source order, with the MFMA chain of block 1: at each k-step of block 1
-// the wave issues that step's MFMAs and then epilogue work on one eighth of
-// block 0's accumulators, and a scheduling fence keeps the compiler from
-// regrouping them, so the matrix pipe and the VALU work at the same time
-// within the wave.  Block 1's epilogue follows.  epi(acc, r, i) handles
-// accumulator element i of row tile r of a finished chain.
-template <class T, class Epi0, class Epi1>
-__device__ __forceinline__ void two_block_stage(const bf16x8 (&a)[T::NRT][T::NSTEP], const uint8_t* stage,
-                                                int lane, Epi0&& epi0, Epi1&& epi1) {
-    static_assert(T::NCB == 2 && 16 % T::NSTEP == 0, "two column blocks, epilogue split over k-steps");
-    constexpr int PER = 16 / T::NSTEP;                    // accumulator elements per row tile per step
-    f32x16 acc0[T::NRT], acc1[T::NRT];
-    mfma_block<T>(acc0, a, stage, 0, lane);
+// One stage as a rolling pipeline over its NCB column blocks: each k-step of
+// block c issues its MFMAs and then a slice of the epilogue of block c-1, so
+// the VALU works on finished accumulators while the matrix pipe runs; only
+// the last block's epilogue runs alone.  B fragments are read one k-step
+// ahead, across block boundaries.  Scheduling fences keep this order (the
+// compiler would otherwise hoist the epilogue above the MFMAs and stall on
+// results still in flight, or wait for each read right after issuing it).
+// epi(cb, acc, r, i) handles element i of row tile r of block cb's finished
+// accumulators; within a block the elements are visited in a fixed order, so
+// every kernel that uses this stage sums a query's heads in the same order.
+template <class T, class Epi>
+__device__ __forceinline__ void rolling_stage(const bf16x8 (&a)[T::NRT][T::NSTEP], const uint8_t* stage, int lane,
+                                              Epi&& epi) {
+    static_assert(16 % T::NSTEP == 0, "the epilogue splits evenly over k-steps");
+    constexpr int PER = 16 / T::NSTEP;                    // elements per row tile per step
+    f32x16 accp[T::NRT], accc[T::NRT];
+    bf16x8 bn = b_frag<T>(stage, 0, 0, lane);
 #pragma unroll
-    for (int r = 0; r < T::NRT; ++r) acc1[r] = f32x16{};
-    bf16x8 bn = b_frag<T>(stage, 1, 0, lane);
+    for (int cb = 0; cb < T::NCB; ++cb) {
 #pragma unroll
-    for (int st = 0; st < T::NSTEP; ++st) {
-        const bf16x8 bc = bn;
-        if (st + 1 < T::NSTEP) bn = b_frag<T>(stage, 1, st + 1, lane);
+        for (int st = 0; st < T::NSTEP; ++st) {
+            const bf16x8 bc = bn;
+            if (st + 1 < T::NSTEP) bn = b_frag<T>(stage, cb, st + 1, lane);
+            else if (cb + 1 < T::NCB) bn = b_frag<T>(stage, cb + 1, 0, lane);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int r = 0; r < T::NRT; ++r) acc1[r] = mfma_32x32x16(a[r][st], bc, acc1[r]);
+            for (int r = 0; r < T::NRT; ++r) accc[r] = mfma_32x32x16(a[r][st], bc, st == 0 ? f32x16{} : accc[r]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (cb > 0) {
+#pragma unroll
+                for (int r = 0; r < T::NRT; ++r)
+#pragma unroll
+                    for (int i = st * PER; i < (st + 1) * PER; ++i) epi(cb - 1, accp, r, i);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < T::NRT; ++r) accp[r] = accc[r];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // Same element order as above: (k-step slice, row tile, element).
+#pragma unroll
+    for (int st = 0; st < T::NSTEP; ++st)
 #pragma unroll
         for (int r = 0; r < T::NRT; ++r)
 #pragma unroll
-            for (int i = st * PER; i < (st + 1) * PER; ++i) epi0(acc0, r, i);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int r = 0; r < T::NRT; ++r)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) epi1(acc1, r, i);
+            for (int i = st * PER; i < (st + 1) * PER; ++i) epi(T::NCB - 1, accp, r, i);
 }
 
 // Query handled by slot j of this lane.
