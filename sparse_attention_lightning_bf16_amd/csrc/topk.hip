@@ -109,10 +109,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(const float* __
 
     uint32_t cache[CACHE > 0 ? CACHE : 1];
     if constexpr (CACHE > 0) {
+        // Clamped addresses and a select instead of a guarded load: every load
+        // issues before the first wait (a guarded load would be waited for at
+        // its branch merge, serialising the row's loads).
+        // (The invalid slots are cleared with a mask, not a select, so the
+        // compiler cannot move a load under a branch.)
+        const int e_end = min(c_end * 64, n);
 #pragma unroll
         for (int j = 0; j < CACHE; ++j) {
             const int e = (c_begin + j) * 64 + lane;
-            cache[j] = (j < cw && c_begin + j < c_end && e < n) ? f32_to_key(row[e]) : 0u;
+            const float v = row[min(e, n - 1)];
+            cache[j] = f32_to_key(v) & (0u - (uint32_t)(e < e_end));
         }
     }
     auto key_at = [&](int j, int e) -> uint32_t {
@@ -297,22 +304,37 @@ __global__ __launch_bounds__(kRowThreads, MINB) void topk_rows_reg_kernel(
     const float qnan = __uint_as_float(0x7fc00000u);
     const int ebase = wr * SPAN;                              // first element of this wave
     const int nloc = work ? max(0, min(n - ebase, SPAN)) : 0;
-    const int nch = (nloc + 255) >> 8;
-    const bool vec_ok = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
+    // All loads issue before the first wait: addresses are clamped into the
+    // wave's part of the row and slots past it are set by a select.  16-byte
+    // loads need an aligned logits base, skv % 4 == 0 and lo % 4 == 0: then
+    // every row starts and the buffer ends on a 16-byte boundary, so the
+    // aligned group holding the row's last element lies inside the buffer.
+    const bool vec_ok = (reinterpret_cast<uintptr_t>(logits) & 15) == 0 && ((skv | lo) & 3) == 0;
     float x[VEC][4];
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) {
-        const int e0 = j * 256 + 4 * lane;
-        x[j][0] = x[j][1] = x[j][2] = x[j][3] = qnan;
-        if (j < nch) {
-            if (vec_ok && e0 + 3 < nloc) {
-                const float4 y = *reinterpret_cast<const float4*>(row + ebase + e0);
-                x[j][0] = y.x; x[j][1] = y.y; x[j][2] = y.z; x[j][3] = y.w;
-            } else {
+    for (int j = 0; j < VEC; ++j) x[j][0] = x[j][1] = x[j][2] = x[j][3] = qnan;
+    if (nloc > 0) {
+        const float* wrow = row + ebase;
+        if (vec_ok) {
+            const int last = (nloc - 1) & ~3;
 #pragma unroll
-                for (int m = 0; m < 4; ++m)
-                    if (e0 + m < nloc) x[j][m] = row[ebase + e0 + m];
+            for (int j = 0; j < VEC; ++j) {
+                const int e0 = j * 256 + 4 * lane;
+                const float4 y = *reinterpret_cast<const float4*>(wrow + min(e0, last));
+                x[j][0] = (e0 + 0 < nloc) ? y.x : qnan;
+                x[j][1] = (e0 + 1 < nloc) ? y.y : qnan;
+                x[j][2] = (e0 + 2 < nloc) ? y.z : qnan;
+                x[j][3] = (e0 + 3 < nloc) ? y.w : qnan;
             }
+        } else {
+#pragma unroll
+            for (int j = 0; j < VEC; ++j)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int e = j * 256 + 4 * lane + m;
+                    const float v = wrow[min(e, nloc - 1)];
+                    x[j][m] = (e < nloc) ? v : qnan;
+                }
         }
     }
 
@@ -517,6 +539,313 @@ __global__ __launch_bounds__(kRowThreads, MINB) void topk_rows_reg_kernel(
     }
 }
 
+// ---------------------------------------------------------------- binned workgroup row top-k
+//
+// Rows of at most 1024*VEC visible keys, one workgroup (four waves) per row.
+// The row sits in registers: wave w holds elements w*256*VEC + 256*j +
+// 4*lane + m in x[j][m]; slots past the row hold NaN.  The bin of a score is
+// a monotone function of it: u = 1 + 2^-12 + (v - vmin) * (1 - 2^-11) / span
+// lies in [1, 2), so the 11 leading mantissa bits of u are a linear bin in
+// 0..2047 (a subtract, an fma and a bit-field extract per element; the
+// margins keep u inside [1, 2) under rounding).  A 2048-bin LDS histogram
+// locates the bin holding the topk-th best element; that bin's elements
+// (a handful for smooth score distributions) are gathered and ranked exactly
+// by (score descending, key index ascending), which gives the cut element
+// (vT, iT).  A boundary bin of more than kBinCand elements, or a row whose
+// score range is zero or not finite, falls back to a radix select on
+// order-preserving keys.  The ordered write is that of the register-resident
+// kernel.
+constexpr int kBinCand = 256;
+constexpr int kBinThreads = 256;
+
+struct BinShared {
+    uint32_t hist[kBins];
+    float cand_v[kBinCand];
+    int cand_i[kBinCand];
+    float wmin[4], wmax[4];
+    int wtot[4];
+    int ncand;
+    int bstar, rstar;
+    float cut_v;
+    int cut_i;
+};
+
+// Bin of score v for a row with minimum vmin; sc = (1 - 2^-11) / span.
+__device__ __forceinline__ int score_bin(float v, float vmin, float sc) {
+    const float u = fmaf(v - vmin, sc, 1.000244140625f);          // 1 + 2^-12
+    return (int)((__float_as_uint(u) >> 12) & (uint32_t)(kBins - 1));
+}
+
+// Block-wide: the bin holding the need-th largest element of hist[0..NB) and
+// the element's 1-based rank inside it, counted from the top, into sh.bstar /
+// sh.rstar.  Thread tid owns bins [BPT*tid, BPT*tid + BPT), read rotated by
+// tid so a wave's reads spread over the LDS banks.  Every thread calls it;
+// it ends with a barrier.  Requires 1 <= need <= sum of hist.
+template <int NB>
+__device__ void block_find_bin(BinShared& sh, int need, int tid) {
+    constexpr int BPT = NB / kBinThreads;
+    const int lane = tid & 63, wv = tid >> 6;
+    const int base = BPT * tid;
+    int local = 0;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) local += (int)sh.hist[base + ((i + tid) & (BPT - 1))];
+    int v = local;                                   // inclusive suffix sum over lanes >= this one
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int u = __shfl_down(v, off, 64);
+        if (lane + off < 64) v += u;
+    }
+    if (lane == 0) sh.wtot[wv] = v;
+    __syncthreads();
+    int above = v - local;
+    for (int w2 = wv + 1; w2 < 4; ++w2) above += sh.wtot[w2];
+    if (above < need && need <= above + local) {
+        for (int i = BPT - 1; i >= 0; --i) {
+            const int h = (int)sh.hist[base + i];
+            if (need <= above + h) {
+                sh.bstar = base + i;
+                sh.rstar = need - above;
+                break;
+            }
+            above += h;
+        }
+    }
+    __syncthreads();
+}
+
+template <int VEC>
+__global__ __launch_bounds__(kBinThreads) void topk_rows_bin_kernel(const float* __restrict__ logits, int B, int S,
+                                                                    int skv, int ratio,
+                                                                    const int32_t* __restrict__ ks,
+                                                                    const int32_t* __restrict__ ke, int topk,
+                                                                    float* __restrict__ scores,
+                                                                    int32_t* __restrict__ indices) {
+    constexpr int SPAN = 256 * VEC;                           // elements per wave
+    __shared__ BinShared sh;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int b = blockIdx.x % B;
+    const int t = S - 1 - (int)(blockIdx.x / B);              // longest causal rows first
+    int lo, hi;
+    key_range(ks, ke, t, S, skv, ratio, lo, hi);
+    const int n = hi - lo;
+    const float* row = logits + ((long)b * S + t) * skv + lo;
+    float* so = scores + ((long)b * S + t) * topk;
+    int32_t* io = indices + ((long)b * S + t) * topk;
+
+    if (n <= topk) {                                          // everything is selected
+        for (int i0 = 0; i0 < n; i0 += 8 * kBinThreads) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = row[min(i0 + u * kBinThreads + tid, n - 1)];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = i0 + u * kBinThreads + tid;
+                if (i < n) { so[i] = v[u]; io[i] = lo + i; }
+            }
+        }
+        for (int i = n + tid; i < topk; i += kBinThreads) { so[i] = neg_inf(); io[i] = -1; }
+        return;
+    }
+
+    // ---- this wave's part of the row (every load issues before the first wait)
+    const float qnan = __uint_as_float(0x7fc00000u);
+    const int ebase = wv * SPAN;
+    const int nloc = max(0, min(n - ebase, SPAN));
+    const bool vec_ok = (reinterpret_cast<uintptr_t>(logits) & 15) == 0 && ((skv | lo) & 3) == 0;
+    float x[VEC][4];
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) x[j][0] = x[j][1] = x[j][2] = x[j][3] = qnan;
+    if (nloc > 0) {
+        const float* wrow = row + ebase;
+        if (vec_ok) {
+            const int last = (nloc - 1) & ~3;
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) {
+                const int e0 = j * 256 + 4 * lane;
+                const float4 y = *reinterpret_cast<const float4*>(wrow + min(e0, last));
+                x[j][0] = (e0 + 0 < nloc) ? y.x : qnan;
+                x[j][1] = (e0 + 1 < nloc) ? y.y : qnan;
+                x[j][2] = (e0 + 2 < nloc) ? y.z : qnan;
+                x[j][3] = (e0 + 3 < nloc) ? y.w : qnan;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < VEC; ++j)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int e = j * 256 + 4 * lane + m;
+                    const float v = wrow[min(e, nloc - 1)];
+                    x[j][m] = (e < nloc) ? v : qnan;
+                }
+        }
+    }
+
+    // ---- row min / max (NaN slots are ignored)
+    float vmin = __uint_as_float(0x7f800000u), vmax = neg_inf();
+#pragma unroll
+    for (int j = 0; j < VEC; ++j)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) { vmin = fminf(vmin, x[j][m]); vmax = fmaxf(vmax, x[j][m]); }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        vmin = fminf(vmin, __shfl_xor(vmin, off, 64));
+        vmax = fmaxf(vmax, __shfl_xor(vmax, off, 64));
+    }
+    if (lane == 0) { sh.wmin[wv] = vmin; sh.wmax[wv] = vmax; }
+    for (int i = tid; i < kBins; i += kBinThreads) sh.hist[i] = 0u;
+    if (tid == 0) sh.ncand = 0;
+    __syncthreads();
+    vmin = fminf(fminf(sh.wmin[0], sh.wmin[1]), fminf(sh.wmin[2], sh.wmin[3]));
+    vmax = fmaxf(fmaxf(sh.wmax[0], sh.wmax[1]), fmaxf(sh.wmax[2], sh.wmax[3]));
+    const float span = vmax - vmin;
+    // (A span below 1e-30 would overflow the scale; such rows take the radix path.)
+    const bool binned = span > 1.0e-30f && span < 3.0e38f;   // same in every thread
+    const float sc = binned ? 0.99951171875f / span : 0.0f;  // (1 - 2^-11) / span
+
+    int bstar = 0, rstar = topk, cb = 1 << 30;
+    if (binned) {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const float v = x[j][m];
+                if (v == v) atomicAdd(&sh.hist[score_bin(v, vmin, sc)], 1u);
+            }
+        __syncthreads();
+        block_find_bin<kBins>(sh, topk, tid);
+        bstar = sh.bstar;
+        rstar = sh.rstar;
+        cb = (int)sh.hist[bstar];
+    }
+
+    if (cb <= kBinCand) {
+        // ---- gather the boundary bin and rank it exactly
+#pragma unroll
+        for (int j = 0; j < VEC; ++j)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const float v = x[j][m];
+                const bool c = (v == v) && score_bin(v, vmin, sc) == bstar;
+                const unsigned long long mask = __ballot(c);
+                if (mask != 0ull) {
+                    int base = 0;
+                    if (lane == 0) base = atomicAdd(&sh.ncand, __popcll(mask));
+                    base = __shfl(base, 0, 64);
+                    if (c) {
+                        const int p = base + lanes_below(mask, lane);
+                        sh.cand_v[p] = v;
+                        sh.cand_i[p] = ebase + j * 256 + 4 * lane + m;
+                    }
+                }
+            }
+        __syncthreads();
+        if (tid < cb) {
+            const float vi = sh.cand_v[tid];
+            const int ii = sh.cand_i[tid];
+            int rank = 0;
+            for (int jj = 0; jj < cb; ++jj) {
+                const float vj = sh.cand_v[jj];
+                const int ij = sh.cand_i[jj];
+                rank += (vj > vi) || (vj == vi && ij < ii);
+            }
+            if (rank == rstar - 1) { sh.cut_v = vi; sh.cut_i = ii; }
+        }
+        __syncthreads();
+    } else {
+        // ---- radix select on the keys of the boundary bin (or of the whole
+        // row when it is not binned), 8-bit digits ...
+        uint32_t prefix = 0, pmask = 0;
+        int need = rstar;
+        for (int shift = 24; shift >= 0; shift -= 8) {
+            for (int i = tid; i < 256; i += kBinThreads) sh.hist[i] = 0u;
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < VEC; ++j)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const float v = x[j][m];
+                    const bool in = (v == v) && (!binned || score_bin(v, vmin, sc) == bstar);
+                    const uint32_t k = f32_to_key(v);
+                    if (in && (k & pmask) == prefix) atomicAdd(&sh.hist[(k >> shift) & 255u], 1u);
+                }
+            __syncthreads();
+            block_find_bin<256>(sh, need, tid);
+            prefix |= (uint32_t)sh.bstar << shift;
+            pmask |= 255u << shift;
+            need = sh.rstar;
+            __syncthreads();                                  // bstar / rstar read before reuse
+        }
+        // ... then the need-th smallest key index among the scores equal to it
+        const float vt = key_to_f32(prefix);
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < VEC; ++j)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) cnt += (x[j][m] == vt) ? 1 : 0;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
+        if (lane == 0) sh.wtot[wv] = cnt;
+        __syncthreads();
+        int run = 0;
+        for (int w2 = 0; w2 < wv; ++w2) run += sh.wtot[w2];
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+            int c = 0;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) c += (x[j][m] == vt) ? 1 : 0;
+            const int incl = wave_incl_scan(c, lane);
+            int r = run + incl - c;
+            if (r < need && need <= r + c) {
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    if (x[j][m] == vt) {
+                        ++r;
+                        if (r == need) { sh.cut_v = vt; sh.cut_i = ebase + j * 256 + 4 * lane + m; }
+                    }
+            }
+            run += __shfl(incl, 63, 64);
+        }
+        __syncthreads();
+    }
+    const float vT = sh.cut_v;
+    const int iT = sh.cut_i;
+
+    // ---- ordered write of the selection
+    auto sel = [&](int j, int m) {
+        const float v = x[j][m];
+        return v > vT || (v == vT && ebase + j * 256 + 4 * lane + m <= iT);
+    };
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < VEC; ++j)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) cnt += sel(j, m) ? 1 : 0;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
+    __syncthreads();                                          // wtot reads above are done
+    if (lane == 0) sh.wtot[wv] = cnt;
+    __syncthreads();
+    int run = 0;
+    for (int w2 = 0; w2 < wv; ++w2) run += sh.wtot[w2];
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) {
+        bool f[4];
+        int c = 0;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) { f[m] = sel(j, m); c += f[m] ? 1 : 0; }
+        const int incl = wave_incl_scan(c, lane);
+        int pos = run + incl - c;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            if (f[m] && pos < topk) {
+                so[pos] = x[j][m];
+                io[pos] = lo + ebase + j * 256 + 4 * lane + m;
+                ++pos;
+            }
+        run += __shfl(incl, 63, 64);
+    }
+}
+
 __global__ __launch_bounds__(256) void gather_kernel(const float* __restrict__ logits,
                                                      const int32_t* __restrict__ idx, long total, int skv,
                                                      int topk, float* __restrict__ out) {
@@ -546,7 +875,7 @@ hipError_t launch_topk_rows(const TopkArgs& p) {
     } else {
         dim3 grid((unsigned)((long)p.B * p.S));
         if (p.Skv <= 8192)
-            hipLaunchKernelGGL(topk_rows_kernel<32>, grid, dim3(kTopkThreads), 0, p.stream, p.logits, p.B, p.S,
+            hipLaunchKernelGGL(topk_rows_bin_kernel<8>, grid, dim3(kBinThreads), 0, p.stream, p.logits, p.B, p.S,
                                p.Skv, p.ratio, p.ks, p.ke, p.topk, p.scores, p.indices);
         else
             hipLaunchKernelGGL(topk_rows_kernel<0>, grid, dim3(kTopkThreads), 0, p.stream, p.logits, p.B, p.S,
