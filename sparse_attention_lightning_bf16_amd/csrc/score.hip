@@ -158,6 +158,58 @@ __global__ __launch_bounds__(256, stage_min_waves(H, DP)) void v4_logits_kernel(
 
 // ---------------------------------------------------------------- V4.1 scores
 
+// Span [lo, hi) of keys visible to any of the workgroup's rows t0..t0+nrows-1
+// (hi <= lo when none is): a scan of those rows of `allowed` by the whole
+// workgroup, 16 bytes per load where rows are 16-byte aligned.  Ends with a
+// barrier.
+__device__ __forceinline__ void allowed_span(const uint8_t* __restrict__ rows0, int nrows, int G, int tid,
+                                             int* sh_lo, int* sh_hi, int& lo, int& hi) {
+    if (tid == 0) { *sh_lo = G; *sh_hi = 0; }
+    __syncthreads();
+    int my_lo = G, my_hi = 0;
+    const bool vec = ((reinterpret_cast<uintptr_t>(rows0) | (uintptr_t)G) & 15) == 0;
+    if (vec) {
+        const int cpr = G >> 4;                                   // 16-byte chunks per row
+        for (int c = tid; c < nrows * cpr; c += 256) {
+            const int r = c / cpr, s0 = (c - r * cpr) << 4;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(rows0 + (long)r * G + s0);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (w[i] != 0u) {
+                    my_lo = min(my_lo, s0 + 4 * i + (__builtin_ctz(w[i]) >> 3));
+                    my_hi = max(my_hi, s0 + 4 * i + ((31 - __builtin_clz(w[i])) >> 3) + 1);
+                }
+            }
+        }
+    } else {
+        for (long e = tid; e < (long)nrows * G; e += 256) {
+            if (rows0[e] != 0) {
+                const int sidx = (int)(e % G);
+                my_lo = min(my_lo, sidx);
+                my_hi = max(my_hi, sidx + 1);
+            }
+        }
+    }
+    if (my_lo < my_hi) { atomicMin(sh_lo, my_lo); atomicMax(sh_hi, my_hi); }
+    __syncthreads();
+    lo = *sh_lo;
+    hi = *sh_hi;
+}
+
+// Fill p[0..n) of bf16 with -inf (0xFF80), 16 bytes per store where aligned.
+__device__ __forceinline__ void fill_bf16_neg_inf(uint16_t* __restrict__ p, long n, int tid, int nthreads) {
+    if (n <= 0) return;
+    long head = (long)(((16 - ((uintptr_t)p & 15)) & 15) >> 1);
+    if (head > n) head = n;
+    for (long i = tid; i < head; i += nthreads) p[i] = 0xff80u;
+    uint16_t* body = p + head;
+    const long nb = (n - head) >> 3;
+    const u32x4 v = {0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
+    for (long i = tid; i < nb; i += nthreads) reinterpret_cast<u32x4*>(body)[i] = v;
+    for (long i = head + 8 * nb + tid; i < n; i += nthreads) p[i] = 0xff80u;
+}
+
 template <int H, int DP>
 __global__ __launch_bounds__(256, stage_min_waves(H, DP)) void v41_scores_kernel(InLayout L, const uint16_t* __restrict__ wts,
                                                          const uint8_t* __restrict__ allowed, int B, int Lq,
@@ -165,6 +217,7 @@ __global__ __launch_bounds__(256, stage_min_waves(H, DP)) void v41_scores_kernel
     using T = Tiling<H, DP>;
     __shared__ __attribute__((aligned(16))) uint8_t lds0[T::STAGE_BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t lds1[T::STAGE_BYTES];
+    __shared__ int span_lo, span_hi;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5;
     const int nqb = (Lq + T::QB - 1) / T::QB;
@@ -172,75 +225,109 @@ __global__ __launch_bounds__(256, stage_min_waves(H, DP)) void v41_scores_kernel
     const int qb = nqb - 1 - (int)(blockIdx.x / B);
     const int t0 = qb * T::QB;
     const int tq0 = t0 + wave * T::QW;
-    const int ntile = (G + T::KT - 1) / T::KT;
+    const int nrows = min(T::QB, Lq - t0);
+    const uint8_t* al_b = allowed + (long)b * Lq * G;
+
+    // Keys visible to some row of the workgroup, in whole stages; the rest of
+    // the rows is hidden and filled with -inf below without being computed.
+    int vlo, vhi;
+    allowed_span(al_b + (long)t0 * G, nrows, G, tid, &span_lo, &span_hi, vlo, vhi);
+    const int tile_lo = (vhi > vlo) ? vlo / T::KT : 0;
+    const int tile_hi = (vhi > vlo) ? (vhi + T::KT - 1) / T::KT : 0;
+    const int ntile = tile_hi - tile_lo;
+    const int fill_lo = tile_lo * T::KT, fill_hi = min(G, tile_hi * T::KT);
 
     bf16x8 a[T::NRT][T::NSTEP];
-    load_q_frags<T>(a, L, b, tq0, Lq, lane);
     float wr[T::NRT][16];
-#pragma unroll
-    for (int r = 0; r < T::NRT; ++r)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int row = 32 * r + c_row(i, hf);
-            const int t = tq0 + row / H, h = row % H;
-            wr[r][i] = (t < Lq) ? bf16_to_f32(wts[((long)b * Lq + t) * H + h]) : 0.0f;
-        }
-
     const uint16_t kNegInfBf16 = 0xff80u;
-    stream_key_stages<T>(L, b, G, 0, ntile, lds0, lds1, tid, [&](int it, const uint8_t* stage) {
-        const int s0 = it * T::KT;
-        // Visibility of this lane's keys for each of its queries.
-        bool vis[T::NCB][T::QW];
-        bool any = false;
+    if (ntile > 0) {
+        load_q_frags<T>(a, L, b, tq0, Lq, lane);
 #pragma unroll
-        for (int cb = 0; cb < T::NCB; ++cb) {
-            const int s = s0 + 32 * cb + (lane & 31);
+        for (int r = 0; r < T::NRT; ++r)
 #pragma unroll
-            for (int j = 0; j < T::QW; ++j) {
-                const int t = slot_query<T>(tq0, j, hf);
-                vis[cb][j] = (t < Lq && s < G) ? (allowed[((long)b * Lq + t) * G + s] != 0) : false;
-                any |= vis[cb][j];
+            for (int i = 0; i < 16; ++i) {
+                const int row = 32 * r + c_row(i, hf);
+                const int t = tq0 + row / H, h = row % H;
+                const float v = bf16_to_f32(wts[((long)b * Lq + min(t, Lq - 1)) * H + h]);
+                wr[r][i] = (t < Lq) ? v : 0.0f;
             }
-        }
-        const bool active = __ballot(any) != 0ull;
 
-        float part[T::NCB][T::QW];
+        // Visibility bytes of this lane's keys, loaded one stage ahead (the
+        // barrier that opens a stage waits for them with the key tile).
+        uint8_t nxt[T::NCB][T::QW];
+        auto load_vis = [&](int s0) {
 #pragma unroll
-        for (int cb = 0; cb < T::NCB; ++cb)
+            for (int cb = 0; cb < T::NCB; ++cb) {
+                const int s = min(s0 + 32 * cb + (lane & 31), G - 1);
 #pragma unroll
-            for (int j = 0; j < T::QW; ++j) part[cb][j] = 0.0f;
-        if (active) {
-            auto term = [&](float acc_v, float w_v) {
-                const float rr = round_bf16(relu(acc_v));    // bf16(d); ReLU commutes with rounding
-                return round_bf16(w_v * rr);                  // exact product, then bf16
-            };
-            rolling_stage<T>(a, stage, lane, [&](int cb, const f32x16 (&acc)[T::NRT], int r, int i) {
-                part[cb][T::slot(r, i)] += term(acc[r][i], wr[r][i]);
-            });
-            if constexpr (H >= 8) {
-#pragma unroll
-                for (int cb = 0; cb < T::NCB; ++cb)
-#pragma unroll
-                    for (int j = 0; j < T::QW; ++j) part[cb][j] = xor32_add(part[cb][j]);
-            }
-        }
-
-#pragma unroll
-        for (int cb = 0; cb < T::NCB; ++cb) {
-            const int s = s0 + 32 * cb + (lane & 31);
-#pragma unroll
-            for (int j = 0; j < T::QW; ++j) {
-                if constexpr (H >= 8) {
-                    if (hf != (cb & 1)) continue;      // lower half stores even blocks, upper half odd
-                } else {
-                    if ((j % (2 * T::half_step())) >= T::half_step()) continue;
+                for (int j = 0; j < T::QW; ++j) {
+                    const int t = min(slot_query<T>(tq0, j, hf), Lq - 1);
+                    nxt[cb][j] = al_b[(long)t * G + s];
                 }
-                const int t = slot_query<T>(tq0, j, hf);
-                if (t < Lq && s < G)
-                    out[((long)b * Lq + t) * G + s] = vis[cb][j] ? bf16_bits(part[cb][j]) : kNegInfBf16;
             }
-        }
-    });
+        };
+        load_vis(fill_lo);
+        stream_key_stages<T>(L, b, G, tile_lo, ntile, lds0, lds1, tid, [&](int it, const uint8_t* stage) {
+            const int s0 = (tile_lo + it) * T::KT;
+            bool vis[T::NCB][T::QW];
+            bool any = false;
+#pragma unroll
+            for (int cb = 0; cb < T::NCB; ++cb) {
+                const int s = s0 + 32 * cb + (lane & 31);
+#pragma unroll
+                for (int j = 0; j < T::QW; ++j) {
+                    const int t = slot_query<T>(tq0, j, hf);
+                    vis[cb][j] = (t < Lq && s < G) && nxt[cb][j] != 0;
+                    any |= vis[cb][j];
+                }
+            }
+            if (it + 1 < ntile) load_vis(s0 + T::KT);
+            const bool active = __ballot(any) != 0ull;
+
+            float part[T::NCB][T::QW];
+#pragma unroll
+            for (int cb = 0; cb < T::NCB; ++cb)
+#pragma unroll
+                for (int j = 0; j < T::QW; ++j) part[cb][j] = 0.0f;
+            if (active) {
+                auto term = [&](float acc_v, float w_v) {
+                    const float rr = round_bf16(relu(acc_v));    // bf16(d); ReLU commutes with rounding
+                    return round_bf16(w_v * rr);                  // exact product, then bf16
+                };
+                rolling_stage<T>(a, stage, lane, [&](int cb, const f32x16 (&acc)[T::NRT], int r, int i) {
+                    part[cb][T::slot(r, i)] += term(acc[r][i], wr[r][i]);
+                });
+                if constexpr (H >= 8) {
+#pragma unroll
+                    for (int cb = 0; cb < T::NCB; ++cb)
+#pragma unroll
+                        for (int j = 0; j < T::QW; ++j) part[cb][j] = xor32_add(part[cb][j]);
+                }
+            }
+
+#pragma unroll
+            for (int cb = 0; cb < T::NCB; ++cb) {
+                const int s = s0 + 32 * cb + (lane & 31);
+#pragma unroll
+                for (int j = 0; j < T::QW; ++j) {
+                    if constexpr (H >= 8) {
+                        if (hf != (cb & 1)) continue;      // lower half stores even blocks, upper half odd
+                    } else {
+                        if ((j % (2 * T::half_step())) >= T::half_step()) continue;
+                    }
+                    const int t = slot_query<T>(tq0, j, hf);
+                    if (t < Lq && s < G)
+                        out[((long)b * Lq + t) * G + s] = vis[cb][j] ? bf16_bits(part[cb][j]) : kNegInfBf16;
+                }
+            }
+        });
+    }
+    // Hidden outside the streamed span.
+    for (int q = 0; q < nrows; ++q) {
+        uint16_t* orow = out + ((long)b * Lq + t0 + q) * G;
+        fill_bf16_neg_inf(orow, fill_lo, tid, T::THREADS);
+        fill_bf16_neg_inf(orow + fill_hi, G - fill_hi, tid, T::THREADS);
+    }
 }
 
 // ---------------------------------------------------------------- launchers
