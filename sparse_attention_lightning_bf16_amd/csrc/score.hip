@@ -169,16 +169,26 @@ __device__ __forceinline__ void allowed_span(const uint8_t* __restrict__ rows0, 
     int my_lo = G, my_hi = 0;
     const bool vec = ((reinterpret_cast<uintptr_t>(rows0) | (uintptr_t)G) & 15) == 0;
     if (vec) {
-        const int cpr = G >> 4;                                   // 16-byte chunks per row
-        for (int c = tid; c < nrows * cpr; c += 256) {
-            const int r = c / cpr, s0 = (c - r * cpr) << 4;
-            const u32x4 v = *reinterpret_cast<const u32x4*>(rows0 + (long)r * G + s0);
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        // Rows are contiguous, so chunk c covers bytes 16c .. 16c+15 of the
+        // rows' block; four clamped loads per thread are in flight at once.
+        const int nch = nrows * (G >> 4);
+        for (int c0 = 0; c0 < nch; c0 += 4 * 256) {
+            u32x4 v[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (w[i] != 0u) {
-                    my_lo = min(my_lo, s0 + 4 * i + (__builtin_ctz(w[i]) >> 3));
-                    my_hi = max(my_hi, s0 + 4 * i + ((31 - __builtin_clz(w[i])) >> 3) + 1);
+            for (int u = 0; u < 4; ++u)
+                v[u] = *reinterpret_cast<const u32x4*>(rows0 + 16L * min(c0 + u * 256 + tid, nch - 1));
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int c = c0 + u * 256 + tid;
+                if (c >= nch) continue;
+                const int s0 = (int)((16L * c) % G);
+                const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (w[i] != 0u) {
+                        my_lo = min(my_lo, s0 + 4 * i + (__builtin_ctz(w[i]) >> 3));
+                        my_hi = max(my_hi, s0 + 4 * i + ((31 - __builtin_clz(w[i])) >> 3) + 1);
+                    }
                 }
             }
         }
@@ -228,6 +238,21 @@ __global__ __launch_bounds__(256, stage_min_waves(H, DP)) void v41_scores_kernel
     const int nrows = min(T::QB, Lq - t0);
     const uint8_t* al_b = allowed + (long)b * Lq * G;
 
+    // Query fragments and weights are requested first so their latency
+    // overlaps the span scan.
+    bf16x8 a[T::NRT][T::NSTEP];
+    float wr[T::NRT][16];
+    load_q_frags<T>(a, L, b, tq0, Lq, lane);
+#pragma unroll
+    for (int r = 0; r < T::NRT; ++r)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int row = 32 * r + c_row(i, hf);
+            const int t = tq0 + row / H, h = row % H;
+            const float v = bf16_to_f32(wts[((long)b * Lq + min(t, Lq - 1)) * H + h]);
+            wr[r][i] = (t < Lq) ? v : 0.0f;
+        }
+
     // Keys visible to some row of the workgroup, in whole stages; the rest of
     // the rows is hidden and filled with -inf below without being computed.
     int vlo, vhi;
@@ -237,20 +262,8 @@ __global__ __launch_bounds__(256, stage_min_waves(H, DP)) void v41_scores_kernel
     const int ntile = tile_hi - tile_lo;
     const int fill_lo = tile_lo * T::KT, fill_hi = min(G, tile_hi * T::KT);
 
-    bf16x8 a[T::NRT][T::NSTEP];
-    float wr[T::NRT][16];
     const uint16_t kNegInfBf16 = 0xff80u;
     if (ntile > 0) {
-        load_q_frags<T>(a, L, b, tq0, Lq, lane);
-#pragma unroll
-        for (int r = 0; r < T::NRT; ++r)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int row = 32 * r + c_row(i, hf);
-                const int t = tq0 + row / H, h = row % H;
-                const float v = bf16_to_f32(wts[((long)b * Lq + min(t, Lq - 1)) * H + h]);
-                wr[r][i] = (t < Lq) ? v : 0.0f;
-            }
 
         // Visibility bytes of this lane's keys, loaded one stage ahead (the
         // barrier that opens a stage waits for them with the key tile).
