@@ -1,6 +1,6 @@
 """Benchmark of the lightning-indexer hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
 
 A step is one forward of the V4 lightning indexer on the 32K workload
 (batch 1, seqlen 32768, seqlen_kv 8192, 64 heads, index_dim 128,
@@ -9,9 +9,11 @@ compress_ratio 4, topk 2048): causally masked scoring of every valid
 are timed on the same inputs: lix_topk's fused path (no logits in HBM) and
 the materialized path (lix_indexer_logits, then lix_topk over the logits);
 the step is the faster one, named in config.path.  The same run also times
-the gather lix_topk_scores at the selected indices and
-lix_indexer_scores_v41 on the V4.1 workload (batch 1, 16384 queries, 4096
-keys, packed documents).
+the gather lix_topk_scores at the selected indices, the direct scoring at
+those indices (lix_indexer_scores_at) and lix_indexer_scores_v41 on the V4.1 workload (batch 1, 16384 queries, 4096
+keys, packed documents), a 1 GiB device copy (achievable HBM bandwidth), the
+4K workload cold (L2 and MALL flushed by a 1 GiB write before each call) and
+warm, and the fused step on the 131K workload.
 
 Prints one JSON line.  `value` is causally valid TFLOP/s (2*H*D per visible
 pair) over the whole step; queries/s are reported beside it.  Kernel
@@ -79,6 +81,61 @@ def time_loop(fn, steps, warmup):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - wall0) * 1e3 / steps
     return t.mean_ms(), wall
+
+
+def time_each(fn, steps, warmup, between=None):
+    """Mean per-call time with HIP events around each call; `between` runs untimed before each call."""
+    for _ in range(warmup):
+        if between is not None:
+            between()
+        fn()
+    torch.cuda.synchronize()
+    t = EventTimer()
+    for _ in range(steps):
+        if between is not None:
+            between()
+        with t:
+            fn()
+    return t.mean_ms()
+
+
+def extra_parts(dev, steps, warmup):
+    """Achievable copy bandwidth, the 4K materialized step cold and warm, the 131K fused step."""
+    out = {}
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    copy_ms = time_each(lambda: dst.copy_(src), steps, warmup)
+    out["copy_1gib_ms"] = copy_ms
+    out["copy_gbs"] = 2.0 * src.numel() * 4 / copy_ms / 1e6             # read + write
+    flush = lambda: dst.fill_(0.0)                                        # 1 GiB write: evicts L2 and MALL
+    del src
+
+    cfg = synth.WORKLOADS["4k"]
+    inp = synth.v4_inputs(**cfg)
+    q, k, w = (inp[x].to(dev) for x in "qkw")
+    c, tk = cfg["compress_ratio"], cfg["topk"]
+    logits = torch.empty(cfg["batch"], cfg["seqlen"], cfg["seqlen_kv"], dtype=torch.float32, device=dev)
+    def step4k():
+        lx.indexer_logits(q, k, w, c, out=logits)
+        return lx.topk_from_logits(logits, c, tk)
+    out["4k_materialized_warm_ms"] = time_each(step4k, steps, warmup)
+    out["4k_materialized_cold_ms"] = time_each(step4k, steps, warmup, between=flush)
+    out["4k_fused_warm_ms"] = time_each(lambda: lx.topk(q, k, w, c, tk), steps, warmup)
+    out["4k_fused_cold_ms"] = time_each(lambda: lx.topk(q, k, w, c, tk), steps, warmup, between=flush)
+    del q, k, w, logits, dst
+
+    log("timing the 131K fused step")
+    cfg = synth.WORKLOADS["131k"]
+    inp = synth.v4_inputs(**cfg)
+    q, k, w = (inp[x].to(dev) for x in "qkw")
+    del inp
+    c, tk = cfg["compress_ratio"], cfg["topk"]
+    ms = time_each(lambda: lx.topk(q, k, w, c, tk), max(3, steps // 4), 2)
+    pairs = cfg["batch"] * causal_valid_pairs(cfg["seqlen"], cfg["seqlen_kv"], c)
+    out["131k_fused_ms"] = ms
+    out["131k_fused_tflops"] = 2.0 * cfg["heads"] * cfg["index_dim"] * pairs / ms / 1e9
+    out["131k_queries_per_s"] = cfg["batch"] * cfg["seqlen"] / (ms * 1e-3)
+    return out
 
 
 def source_digest():
@@ -172,6 +229,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the copy-bandwidth, 4K cold/warm and 131K fused parts")
     ap.add_argument("--cpu-sample-every", type=int, default=3)
     ap.add_argument("--part", choices=["all", "fused", "logits", "topk", "v41", "copy"], default="all",
                     help="time one kernel only (for profiler runs); the JSON line then covers that part")
@@ -221,6 +280,10 @@ def main():
         sc_m, ix_m = lx.topk_from_logits(logits, c, tk)
         same = bool(torch.equal(ix_m, ix_f) and torch.equal(sc_m, sc_f))
         gather_ms, _ = time_loop(lambda: lx.topk_scores(logits, ix_f), args.steps, args.warmup)
+        # scores at given indices straight from q, k, w (the topk_indices branch of the pages' entry point)
+        at_ms, _ = time_loop(lambda: lx.indexer_scores_at(q, k, w, c, ix_f), args.steps, args.warmup)
+        at_same = bool(torch.equal(lx.indexer_scores_at(q, k, w, c, ix_f), sc_f))
+        at_pairs = int((ix_f >= 0).sum())
         # algorithmic bytes of the row top-k: read the visible logits, write scores+indices
         topk_bytes = 4.0 * pairs + 8.0 * B * S * tk
         logits_bytes = 4.0 * B * S * Skv + 2.0 * B * S * H * D + 4.0 * B * S * H
@@ -237,6 +300,10 @@ def main():
             "gather_ms": gather_ms,
             "gather_gbs": gather_bytes / gather_ms / 1e6,
             "fused_equals_materialized": same,
+            "scores_at_ms": at_ms,
+            "scores_at_tflops": 2.0 * H * D * at_pairs / at_ms / 1e9,
+            "scores_at_equals_topk_scores": at_same,
+            "logits_then_gather_ms": score_ms + gather_ms,
         })
         del logits
 
@@ -255,6 +322,10 @@ def main():
             "v41_allowed_fraction": allowed_pairs / (Lq * G),
             "v41_allowed_tflops": 2.0 * H * D * allowed_pairs / v41_ms / 1e9,
         })
+
+        if not args.no_extra:
+            log("timing copy bandwidth and the 4K workload")
+            parts.update(extra_parts(dev, args.steps, args.warmup))
 
     # The step is the faster of the two routes to the same forward; both are reported.
     if args.part == "all" and parts["materialized_step_ms"] < fused_ms:

@@ -140,6 +140,28 @@ int lix_topk_scores(const float* logits, const int32_t* indices,
                     hipStream_t stream);
 
 /*
+ * lix_indexer_scores_at - indexer scores at given key indices, from q, k, w.
+ *
+ * Page "...deepseek_v4.kernels.tilelang_indexer", sections
+ * v4_lighting_indexer with topk_indices given and
+ * pytorch_extract_topk_scores: the scores of the given indices, i.e. the
+ * cleaned logits gathered at them.  Only the given keys are scored; no
+ * [B,S,Skv] tensor exists.  For i = indices[b,t,j]:
+ *   scores[b,t,j] = sum_h w[t,b,h] * max(0, q[t,b,h,:] . k[i,b,:])  if ks[t] <= i < ke[t]
+ *   scores[b,t,j] = -inf                                            otherwise
+ * (ranges as for lix_indexer_logits; an index outside [0, Skv) is -inf).
+ * Each score equals lix_indexer_logits' value at that position bit for bit.
+ *
+ *   q, k, w  as in lix_indexer_logits
+ *   indices  int32 [B, S, topk]  (any values; duplicates allowed)
+ *   scores   fp32  [B, S, topk]  out
+ */
+int lix_indexer_scores_at(const void* q, const void* k, const float* w, const int32_t* indices,
+                          int B, int S, int Skv, int H, int D, int compress_ratio,
+                          const int32_t* ks, const int32_t* ke, int topk,
+                          float* scores, hipStream_t stream);
+
+/*
  * lix_indexer_scores_v41 - V4.1 BF16-rounded scores with a visibility mask.
  *
  * Page "...deepseek_v41.indexer", module description (the GEMM output and

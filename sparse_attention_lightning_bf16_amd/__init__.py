@@ -10,6 +10,7 @@ from .ops import (  # noqa: F401
     topk,
     topk_from_logits,
     topk_scores,
+    indexer_scores_at,
     indexer_scores_v41,
     v4_lighting_indexer,
 )

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblix.so")
-SOURCES = ["api.cpp", "score.hip", "topk.hip", "fused.hip"]
+SOURCES = ["api.cpp", "score.hip", "topk.hip", "fused.hip", "sparse.hip"]
 ARCH = "gfx950"
 
 

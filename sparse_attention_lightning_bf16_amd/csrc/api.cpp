@@ -146,6 +146,23 @@ int lix_topk_scores(const float* logits, const int32_t* indices, int B, int S, i
     return launch_status(lix::launch_gather(a));
 }
 
+int lix_indexer_scores_at(const void* q, const void* k, const float* w, const int32_t* indices, int B, int S,
+                          int Skv, int H, int D, int compress_ratio, const int32_t* ks, const int32_t* ke, int topk,
+                          float* scores, hipStream_t stream) {
+    if (!q || !k || !w || !indices || !scores) return LIX_ERR_NULL;
+    int st = check_dims_v4(B, S, Skv, H, D, compress_ratio, ks, ke);
+    if (st != LIX_OK) return st;
+    if (topk < 1) return LIX_ERR_SHAPE;
+    if (!fits(B, S, topk) || (long long)B * S * topk > (1LL << 38)) return LIX_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(w, 4) || !aligned(indices, 4) || !aligned(scores, 4) ||
+        !aligned(ks, 4) || !aligned(ke, 4))
+        return LIX_ERR_UNSUPPORTED;
+    st = check_device({q, k, w, indices, scores, ks, ke});
+    if (st != LIX_OK) return st;
+    lix::SparseArgs a{q, k, w, indices, B, S, Skv, H, D, compress_ratio, topk, ks, ke, scores, stream};
+    return launch_status(lix::launch_sparse_scores(a));
+}
+
 int lix_indexer_scores_v41(const void* queries, const void* keys, const void* weights, const uint8_t* allowed,
                            int B, int L, int G, int H, int D, void* scores, hipStream_t stream) {
     if (!queries || !keys || !weights || !allowed || !scores) return LIX_ERR_NULL;

@@ -65,7 +65,20 @@ struct V41Args {
     hipStream_t stream;
 };
 
+struct SparseArgs {
+    const void* q;
+    const void* k;
+    const float* w;
+    const int32_t* indices;   // [B,S,topk]
+    int B, S, Skv, H, D, ratio, topk;
+    const int32_t* ks;
+    const int32_t* ke;
+    float* scores;            // [B,S,topk]
+    hipStream_t stream;
+};
+
 hipError_t launch_v4_logits(const LogitsArgs& p);
+hipError_t launch_sparse_scores(const SparseArgs& p);
 hipError_t launch_topk_rows(const TopkArgs& p);
 hipError_t launch_fused_topk(const FusedArgs& p);
 hipError_t launch_gather(const GatherArgs& p);

@@ -1,4 +1,4 @@
-"""Python face of liblix: the four C entry points plus the pages' entry point.
+"""Python face of liblix: the C entry points plus the pages' entry point.
 
 Every function only checks and marshals arguments (shapes, dtypes,
 contiguity, output allocation, the current HIP stream) and calls the C ABI;
@@ -129,6 +129,26 @@ def topk_scores(logits, topk_indices):
     return out
 
 
+def indexer_scores_at(q, k, weights, compress_ratio, topk_indices, cu_seqlen_ks=None, cu_seqlen_ke=None):
+    """lix_indexer_scores_at: the indexer scores at topk_indices [B,S,topk] int32, from q, k, weights
+    (layouts as indexer_logits) without forming the logits; -inf where an index is outside the query's
+    range (causal for compress_ratio unless cu_seqlen_ks/ke are given) or outside [0, Skv)."""
+    S, B, H, D, Skv = _v4_shapes(q, k, weights)
+    ks, ke = _ranges(cu_seqlen_ks, cu_seqlen_ke, S)
+    _need(topk_indices, "topk_indices", torch.int32, 3)
+    if topk_indices.shape[0] != B or topk_indices.shape[1] != S:
+        raise ValueError("topk_indices must be [B, S, topk]")
+    if topk_indices.device != q.device:
+        raise ValueError("topk_indices must be on the device of q")
+    tk = topk_indices.shape[2]
+    out = torch.empty(B, S, tk, dtype=torch.float32, device=q.device)
+    st = _lib.load().lix_indexer_scores_at(q.data_ptr(), k.data_ptr(), weights.data_ptr(), topk_indices.data_ptr(),
+                                           B, S, Skv, H, D, int(compress_ratio), _ptr(ks), _ptr(ke), tk,
+                                           out.data_ptr(), _stream(q.device))
+    _lib.check(st, "lix_indexer_scores_at")
+    return out
+
+
 def indexer_scores_v41(queries, keys, weights, allowed):
     """lix_indexer_scores_v41: queries [B,L,H,D], keys [B,G,D], weights [B,L,H] (bf16),
     allowed [B,L,G] bool -> bf16 [B,L,G] (-inf where hidden)."""
@@ -152,10 +172,10 @@ def v4_lighting_indexer(index_q, index_k, weights, compress_ratio, topk, topk_in
     """The pages' main entry point (the misspelt name is the pages' own).
 
     Without topk_indices: fused scoring + top-k, returns (scores, indices).
-    With topk_indices [B,S,topk] int32: the scores at those indices
-    (logits, then the gather), returns scores.
+    With topk_indices [B,S,topk] int32: the scores at those indices, scored
+    directly (lix_indexer_scores_at; equal bit for bit to gathering the
+    materialized logits), returns scores.
     """
     if topk_indices is None:
         return globals()["topk"](index_q, index_k, weights, compress_ratio, topk)
-    logits = indexer_logits(index_q, index_k, weights, compress_ratio)
-    return topk_scores(logits, topk_indices)
+    return indexer_scores_at(index_q, index_k, weights, compress_ratio, topk_indices)

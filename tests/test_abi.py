@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function():
     lib = lx.load()
     names = declared_functions()
     assert set(names) == {"lix_status_string", "lix_version", "lix_indexer_logits", "lix_topk",
-                          "lix_topk_scores", "lix_indexer_scores_v41"}
+                          "lix_topk_scores", "lix_indexer_scores_v41", "lix_indexer_scores_at"}
     for name in names:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES
@@ -107,6 +107,24 @@ def test_v41_validation(kw, code):
     a.update(kw)
     assert lx.load().lix_indexer_scores_v41(a["queries"], a["keys"], a["weights"], a["allowed"], a["B"], a["L"],
                                             a["G"], a["H"], a["D"], a["scores"], None) == code
+
+
+def scores_at_call(q=P, k=P, w=P, idx=P, B=1, S=8, Skv=4, H=64, D=128, c=4, ks=None, ke=None, topk=2, out=P):
+    return lx.load().lix_indexer_scores_at(q, k, w, idx, B, S, Skv, H, D, c, ks, ke, topk, out, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(w=None), NULL), (dict(idx=None), NULL),
+    (dict(out=None), NULL),
+    (dict(B=0), SHAPE), (dict(S=0), SHAPE), (dict(Skv=-3), SHAPE), (dict(topk=0), SHAPE), (dict(c=0), SHAPE),
+    (dict(ks=P), SHAPE),
+    (dict(H=48), UNSUP), (dict(D=40), UNSUP), (dict(q=P + 4), UNSUP), (dict(k=P + 8), UNSUP),
+    (dict(idx=P + 2), UNSUP), (dict(out=P + 1), UNSUP),
+    (dict(B=1 << 16, S=1 << 16, topk=1 << 16), UNSUP),
+])
+def test_scores_at_validation(kw, code):
+    # topk may exceed Skv here (given indices need not be distinct)
+    assert scores_at_call(**kw) == code
 
 
 def test_python_binding_rejects_bad_tensors_before_the_library():

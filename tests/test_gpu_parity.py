@@ -254,6 +254,65 @@ def test_lighting_indexer_with_given_indices_round_trip():
     assert torch.equal(sc, again)
 
 
+# ------------------------------------------------------------------ scores at given indices
+
+@pytest.mark.parametrize("H,D,B,S,Skv,c,tk", [
+    (64, 128, 2, 300, 75, 4, 40),     # the workloads' heads and index_dim
+    (64, 128, 1, 130, 200, 1, 1),
+    (128, 256, 1, 70, 40, 2, 33),
+    (32, 64, 2, 90, 70, 1, 70),       # topk == Skv, every key
+    (16, 48, 1, 61, 50, 1, 100),      # topk > Skv (duplicated indices), index_dim padded
+    (8, 32, 2, 40, 50, 1, 65),
+    (4, 16, 1, 61, 70, 1, 31),
+    (1, 128, 2, 70, 66, 1, 17),
+])
+def test_scores_at_equals_gathered_logits_bitwise(H, D, B, S, Skv, c, tk):
+    # Given indices: a mix of in-range keys, keys outside the causal range,
+    # negative and past-the-end indices and duplicates.
+    log(f"scores_at H={H} D={D} B={B} S={S} Skv={Skv} c={c} topk={tk}")
+    inp, nb = v4_case(B, S, Skv, H, D, seed=200 + H + D)
+    q, k, w = dev(inp["q"]), dev(inp["k"]), dev(inp["w"])
+    g = torch.Generator().manual_seed(201 + H)
+    idx = torch.randint(-3, Skv + 3, (B, S, tk), generator=g, dtype=torch.int32)
+    idx[:, :, : min(tk, 5)] = idx[:, :, :1]                       # duplicates
+    logits = lx.indexer_logits(q, k, w, c)
+    want = lx.topk_scores(logits, dev(idx))
+    got = lx.indexer_scores_at(q, k, w, c, dev(idx))
+    assert torch.equal(got, want)
+    ks, ke = ranges(S, Skv, c)
+    ora, mag = oracle.indexer_logits(nb["q"], nb["k"], nb["w"], ks, ke, with_magnitude=True)
+    o = oracle.topk_scores_gather(ora, idx.numpy())
+    m = oracle.topk_scores_gather(mag, np.clip(idx.numpy(), 0, Skv - 1))
+    checkers.check_logits(got.cpu().numpy(), o, np.where(np.isfinite(o), m, 0.0), f"scores_at H={H}")
+
+
+def test_scores_at_given_ranges_and_exact_inputs():
+    B, S, Skv, H, D, tk = 2, 150, 90, 64, 128, 50
+    inp, nb = v4_case(B, S, Skv, H, D, seed=210, exact=True)
+    q, k, w = dev(inp["q"]), dev(inp["k"]), dev(inp["w"])
+    g = torch.Generator().manual_seed(211)
+    ks = torch.randint(0, 30, (S,), generator=g, dtype=torch.int32)
+    ke = ks + torch.randint(-5, 80, (S,), generator=g, dtype=torch.int32)
+    idx = torch.randint(-2, Skv + 2, (B, S, tk), generator=g, dtype=torch.int32)
+    got = lx.indexer_scores_at(q, k, w, 1, dev(idx), dev(ks), dev(ke)).cpu().numpy()
+    ora = oracle.indexer_logits(nb["q"], nb["k"], nb["w"], ks.numpy().astype(np.int64), ke.numpy().astype(np.int64))
+    want = oracle.topk_scores_gather(ora, idx.numpy())
+    assert np.array_equal(got.astype(np.float64), want)
+
+
+def test_scores_at_32k_fused_selection_bitwise():
+    # At full size, in the launch configuration the bench times: the scores at
+    # the fused top-k's own indices are the fused top-k's scores, bit for bit.
+    cfg = synth.WORKLOADS["32k"]
+    S, Skv, tk = cfg["seqlen"], cfg["seqlen_kv"], cfg["topk"]
+    inp, _ = v4_case(1, S, Skv, 64, 128, cfg["seed"])
+    q, k, w = dev(inp["q"]), dev(inp["k"]), dev(inp["w"])
+    log("32k: fused top-k, then scores at its indices")
+    sc, ix = lx.topk(q, k, w, 4, tk)
+    again = lx.indexer_scores_at(q, k, w, 4, ix)
+    assert torch.equal(sc, again)
+
+
 # ------------------------------------------------------------------ V4.1
 
 @pytest.mark.parametrize("H,D,B,L,G", [(64, 128, 1, 200, 60), (16, 32, 2, 70, 100), (128, 64, 1, 33, 20),
