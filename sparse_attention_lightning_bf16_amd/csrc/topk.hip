@@ -224,12 +224,17 @@ struct RowShared {
     int cut_i;
 };
 
-__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
+// Inclusive prefix sum over the 64 lanes with DPP moves (no LDS): shifts by
+// 1, 2, 4, 8 inside each row of 16 lanes, then the totals of rows 0 and 2
+// broadcast into rows 1 and 3 (row_bcast:15), then the total of rows 0-1 into
+// rows 2 and 3 (row_bcast:31).  Lanes without a source add the `old` value 0.
+__device__ __forceinline__ int wave_incl_scan(int x, int /*lane*/) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15 -> rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31 -> rows 2, 3
     return x;
 }
 
@@ -705,12 +710,18 @@ __global__ __launch_bounds__(kBinThreads) void topk_rows_bin_kernel(const float*
     int bstar = 0, rstar = topk, cb = 1 << 30;
     if (binned) {
 #pragma unroll
-        for (int j = 0; j < VEC; ++j)
+        for (int j = 0; j < VEC; ++j) {
+            if ((j + 1) * 256 <= nloc) {                      // whole chunk inside the row
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const float v = x[j][m];
-                if (v == v) atomicAdd(&sh.hist[score_bin(v, vmin, sc)], 1u);
+                for (int m = 0; m < 4; ++m) atomicAdd(&sh.hist[score_bin(x[j][m], vmin, sc)], 1u);
+            } else if (j * 256 < nloc) {
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const float v = x[j][m];
+                    if (v == v) atomicAdd(&sh.hist[score_bin(v, vmin, sc)], 1u);
+                }
             }
+        }
         __syncthreads();
         block_find_bin<kBins>(sh, topk, tid);
         bstar = sh.bstar;
@@ -810,39 +821,37 @@ __global__ __launch_bounds__(kBinThreads) void topk_rows_bin_kernel(const float*
     const float vT = sh.cut_v;
     const int iT = sh.cut_i;
 
-    // ---- ordered write of the selection
-    auto sel = [&](int j, int m) {
-        const float v = x[j][m];
-        return v > vT || (v == vT && ebase + j * 256 + 4 * lane + m <= iT);
-    };
-    int cnt = 0;
+    // ---- ordered write of the selection.  The selection is evaluated once,
+    // as a bit mask (bit 4j+m), for both the per-wave count and the write.
+    uint32_t selm = 0;
 #pragma unroll
     for (int j = 0; j < VEC; ++j)
 #pragma unroll
-        for (int m = 0; m < 4; ++m) cnt += sel(j, m) ? 1 : 0;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
+        for (int m = 0; m < 4; ++m) {
+            const float v = x[j][m];
+            const bool f = v > vT || (v == vT && ebase + j * 256 + 4 * lane + m <= iT);
+            selm |= f ? (1u << (4 * j + m)) : 0u;
+        }
+    const int wcnt = __builtin_amdgcn_readlane(wave_incl_scan(__popc(selm), lane), 63);
     __syncthreads();                                          // wtot reads above are done
-    if (lane == 0) sh.wtot[wv] = cnt;
+    if (lane == 0) sh.wtot[wv] = wcnt;
     __syncthreads();
     int run = 0;
     for (int w2 = 0; w2 < wv; ++w2) run += sh.wtot[w2];
 #pragma unroll
     for (int j = 0; j < VEC; ++j) {
-        bool f[4];
-        int c = 0;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) { f[m] = sel(j, m); c += f[m] ? 1 : 0; }
+        const uint32_t bits = (selm >> (4 * j)) & 15u;
+        const int c = __popc(bits);
         const int incl = wave_incl_scan(c, lane);
         int pos = run + incl - c;
 #pragma unroll
         for (int m = 0; m < 4; ++m)
-            if (f[m] && pos < topk) {
+            if (((bits >> m) & 1u) && pos < topk) {
                 so[pos] = x[j][m];
                 io[pos] = lo + ebase + j * 256 + 4 * lane + m;
                 ++pos;
             }
-        run += __shfl(incl, 63, 64);
+        run += __builtin_amdgcn_readlane(incl, 63);
     }
 }
 
