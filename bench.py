@@ -13,7 +13,8 @@ the gather lix_topk_scores at the selected indices, the direct scoring at
 those indices (lix_indexer_scores_at) and lix_indexer_scores_v41 on the V4.1 workload (batch 1, 16384 queries, 4096
 keys, packed documents), a 1 GiB device copy (achievable HBM bandwidth), the
 4K workload cold (L2 and MALL flushed by a 1 GiB write before each call) and
-warm, and the fused step on the 131K workload.
+warm, the fused step on the 131K workload, and a bf16 8192^3 GEMM through
+torch (hipBLASLt) as the achievable dense MFMA rate beside the published one.
 
 Prints one JSON line.  `value` is causally valid TFLOP/s (2*H*D per visible
 pair) over the whole step; queries/s are reported beside it.  Kernel
@@ -102,6 +103,13 @@ def time_each(fn, steps, warmup, between=None):
 def extra_parts(dev, steps, warmup):
     """Achievable copy bandwidth, the 4K materialized step cold and warm, the 131K fused step."""
     out = {}
+    # achievable dense bf16 rate on this box: a large library GEMM (hipBLASLt through torch)
+    a = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    bm = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    gemm_ms = time_each(lambda: torch.matmul(a, bm), steps, warmup)
+    out["gemm_bf16_8192_ms"] = gemm_ms
+    out["gemm_bf16_tflops"] = 2.0 * 8192 ** 3 / gemm_ms / 1e9
+    del a, bm
     src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
     dst = torch.empty_like(src)
     copy_ms = time_each(lambda: dst.copy_(src), steps, warmup)
@@ -297,6 +305,7 @@ def main():
             "materialized_logits_store_gbs": logits_bytes / score_ms / 1e6,
             "topk_from_logits_gbs": topk_bytes / topk_ms / 1e6,
             "topk_from_logits_hbm_frac": topk_bytes / topk_ms / 1e6 / PEAK_HBM_GBS,
+            "topk_bytes": topk_bytes,
             "gather_ms": gather_ms,
             "gather_gbs": gather_bytes / gather_ms / 1e6,
             "fused_equals_materialized": same,
@@ -324,8 +333,9 @@ def main():
         })
 
         if not args.no_extra:
-            log("timing copy bandwidth and the 4K workload")
+            log("timing a library GEMM, copy bandwidth and the 4K workload")
             parts.update(extra_parts(dev, args.steps, args.warmup))
+            parts["topk_frac_of_copy"] = topk_bytes / topk_ms / 1e6 / parts["copy_gbs"]
 
     # The step is the faster of the two routes to the same forward; both are reported.
     if args.part == "all" and parts["materialized_step_ms"] < fused_ms:
@@ -338,6 +348,10 @@ def main():
     value = flop / step_ms / 1e9
     achieved = flop / roof_kernel["ms"] / 1e9
     traffic = recorded_traffic(roof_kernel["name"])
+    measured = {}
+    if "gemm_bf16_tflops" in parts:
+        measured = {"gemm_bf16_tflops": parts["gemm_bf16_tflops"], "copy_gbs": parts["copy_gbs"],
+                    "frac_of_gemm": achieved / parts["gemm_bf16_tflops"]}
     result = {
         "metric": METRIC,
         "value": value,
@@ -357,7 +371,7 @@ def main():
         "queries_per_s": B * S / (step_ms * 1e-3),
         "roofline": {"bound": "mfma", "kernel": roof_kernel["name"], "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": traffic},
+                     "traffic": traffic, "measured_peaks": measured},
         "parts": parts,
     }
     if not args.no_cpu_baseline:
