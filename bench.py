@@ -10,7 +10,8 @@ are timed on the same inputs: lix_topk's fused path (no logits in HBM) and
 the materialized path (lix_indexer_logits, then lix_topk over the logits);
 the step is the faster one, named in config.path.  The same run also times
 the gather lix_topk_scores at the selected indices, the direct scoring at
-those indices (lix_indexer_scores_at) and lix_indexer_scores_v41 on the V4.1 workload (batch 1, 16384 queries, 4096
+those indices (lix_indexer_scores_at), lix_indexer_scores_v41 and a top-512 of its
+bf16 scores (lix_topk_bf16) on the V4.1 workload (batch 1, 16384 queries, 4096
 keys, packed documents), a 1 GiB device copy (achievable HBM bandwidth), the
 4K workload cold (L2 and MALL flushed by a 1 GiB write before each call) and
 warm, the fused step on the 131K workload, and a bf16 8192^3 GEMM through
@@ -321,6 +322,8 @@ def main():
         vin = synth.v41_inputs(**vcfg)
         vq, vk, vw, va = (vin[x].to(dev) for x in ("queries", "keys", "weights", "allowed"))
         v41_ms, _ = time_loop(lambda: lx.indexer_scores_v41(vq, vk, vw, va), args.steps, args.warmup)
+        v41_scores = lx.indexer_scores_v41(vq, vk, vw, va)
+        v41_topk_ms, _ = time_loop(lambda: lx.topk_bf16(v41_scores, 512), args.steps, args.warmup)
         Lq, G = vcfg["local_sequence"], vcfg["global_compressed"]
         v41_bytes = (2.0 * Lq * H * D + 2.0 * G * D + 2.0 * Lq * H + 1.0 * Lq * G + 2.0 * Lq * G)
         allowed_pairs = int(vin["allowed"].sum())
@@ -330,6 +333,8 @@ def main():
             "v41_hbm_frac": v41_bytes / v41_ms / 1e6 / PEAK_HBM_GBS,
             "v41_allowed_fraction": allowed_pairs / (Lq * G),
             "v41_allowed_tflops": 2.0 * H * D * allowed_pairs / v41_ms / 1e9,
+            "v41_topk512_ms": v41_topk_ms,
+            "v41_topk512_gbs": (2.0 * Lq * G + 6.0 * Lq * 512) / v41_topk_ms / 1e6,
         })
 
         if not args.no_extra:

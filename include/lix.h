@@ -182,6 +182,28 @@ int lix_indexer_scores_v41(const void* queries, const void* keys, const void* we
                            const uint8_t* allowed, int B, int L, int G, int H, int D,
                            void* scores, hipStream_t stream);
 
+/*
+ * lix_topk_bf16 - per-query top-k of V4.1 bf16 scores over the visible keys.
+ *
+ * Page "...deepseek_v41.indexer", module description: the scores of
+ * indexer_scores feed a top-k / candidate selection that runs after it; the
+ * selection rule is V4's (page "...deepseek_v4.kernels.tilelang_indexer",
+ * v4_lighting_indexer: select topk indices per query).  A key is visible when
+ * its score is not bf16 -inf (0xFF80, the value indexer_scores writes where
+ * `allowed` is false).  For each (b, t) the m = min(topk, visible keys) best
+ * visible keys are selected by score, descending, equal scores by key index,
+ * the lower first; they are written to slots [0, m) in ascending key-index
+ * order with their scores copied bit for bit; slots [m, topk) hold index -1
+ * and score bf16 -inf.
+ *
+ *   scores      bf16  [B, L, G]     (e.g. the output of lix_indexer_scores_v41)
+ *   out_scores  bf16  [B, L, topk]  out
+ *   indices     int32 [B, L, topk]  out
+ * Requires 1 <= topk <= G and G <= 8192 (LIX_ERR_SHAPE / LIX_ERR_UNSUPPORTED).
+ */
+int lix_topk_bf16(const void* scores, int B, int L, int G, int topk,
+                  void* out_scores, int32_t* indices, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

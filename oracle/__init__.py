@@ -20,6 +20,7 @@ from .indexer import (  # noqa: F401
     indexer_logits_rows,
     indexer_logits,
     topk_select,
+    topk_select_visible_bf16,
     topk_scores_gather,
     indexer_scores_v41_rows,
     indexer_scores_v41,

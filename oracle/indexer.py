@@ -18,6 +18,9 @@ What is computed, and from which passage of the pages:
   ``v4_lighting_indexer`` (topk = the number of indices to select; returns
   [B,S,topk] fp32 scores and int32 indices).
 * Gather at given indices.  Same page, section ``pytorch_extract_topk_scores``.
+* Top-k of V4.1 scores over the visible keys.  Page "deepseek_v41.indexer",
+  module description (candidate selection follows the scoring), with V4's
+  selection rule.
 * V4.1 scores.  Page "deepseek_v41.indexer", module description and section
   ``indexer_scores``: the GEMM output and each weighted head score are
   rounded to BF16 before the FP32 head reduction; ``allowed`` selects the
@@ -218,6 +221,36 @@ def topk_select(scores, ks, ke, topk):
         out_i[r, :m] = chosen
         out_s[r, :m] = scores[r, chosen]
     return out_s, out_i
+
+
+def topk_select_visible_bf16(score_bits, topk):
+    """Top-k of each row of V4.1 bf16 scores [R, G] over the row's visible keys.
+
+    Page "deepseek_v41.indexer", module description: the scores feed a top-k /
+    candidate selection that runs after ``indexer_scores``; positions the
+    ``allowed`` mask hides hold bf16 -inf (0xFF80), so a key is visible when
+    its score is anything else.  The selection rule is V4's (``topk_select``):
+    the m = min(topk, visible keys) best by score, descending, equal scores by
+    key index, ascending; returned in ascending key-index order, slots
+    m..topk-1 holding index -1 and score 0xFF80.  Scores are compared as the
+    exact values of their bit patterns (so -0 and +0 tie).
+    Returns (score bits uint16 [R, topk], indices int64 [R, topk]).
+    """
+    bits = np.asarray(score_bits, dtype=np.uint16)
+    vals = bf16_bits_to_f64(bits)
+    R = bits.shape[0]
+    out_b = np.full((R, topk), 0xFF80, dtype=np.uint16)
+    out_i = np.full((R, topk), -1, dtype=np.int64)
+    for r in range(R):
+        vis = np.nonzero(bits[r] != 0xFF80)[0]
+        if len(vis) == 0:
+            continue
+        order = np.lexsort((vis, -vals[r, vis]))
+        m = min(topk, len(vis))
+        chosen = np.sort(vis[order[:m]])
+        out_i[r, :m] = chosen
+        out_b[r, :m] = bits[r, chosen]
+    return out_b, out_i
 
 
 def topk_scores_gather(logits, indices):

@@ -12,5 +12,6 @@ from .ops import (  # noqa: F401
     topk_scores,
     indexer_scores_at,
     indexer_scores_v41,
+    topk_bf16,
     v4_lighting_indexer,
 )

@@ -163,6 +163,18 @@ int lix_indexer_scores_at(const void* q, const void* k, const float* w, const in
     return launch_status(lix::launch_sparse_scores(a));
 }
 
+int lix_topk_bf16(const void* scores, int B, int L, int G, int topk, void* out_scores, int32_t* indices,
+                  hipStream_t stream) {
+    if (!scores || !out_scores || !indices) return LIX_ERR_NULL;
+    if (B <= 0 || L <= 0 || G <= 0 || topk < 1 || topk > G) return LIX_ERR_SHAPE;
+    if (G > 8192 || !fits(B, L, G) || !fits(B, L, topk) || !rows_fit(B, L)) return LIX_ERR_UNSUPPORTED;
+    if (!aligned(scores, 2) || !aligned(out_scores, 2) || !aligned(indices, 4)) return LIX_ERR_UNSUPPORTED;
+    int st = check_device({scores, out_scores, indices});
+    if (st != LIX_OK) return st;
+    lix::TopkBf16Args a{scores, B, L, G, topk, out_scores, indices, stream};
+    return launch_status(lix::launch_topk_bf16(a));
+}
+
 int lix_indexer_scores_v41(const void* queries, const void* keys, const void* weights, const uint8_t* allowed,
                            int B, int L, int G, int H, int D, void* scores, hipStream_t stream) {
     if (!queries || !keys || !weights || !allowed || !scores) return LIX_ERR_NULL;

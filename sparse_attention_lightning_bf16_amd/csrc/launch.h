@@ -47,6 +47,14 @@ struct FusedArgs {
     hipStream_t stream;
 };
 
+struct TopkBf16Args {
+    const void* scores;       // bf16 [B,L,G]; bf16 -inf marks a hidden key
+    int B, L, G, topk;
+    void* out_scores;         // bf16 [B,L,topk]
+    int32_t* indices;         // int32 [B,L,topk]
+    hipStream_t stream;
+};
+
 struct GatherArgs {
     const float* logits;
     const int32_t* indices;
@@ -80,6 +88,7 @@ struct SparseArgs {
 hipError_t launch_v4_logits(const LogitsArgs& p);
 hipError_t launch_sparse_scores(const SparseArgs& p);
 hipError_t launch_topk_rows(const TopkArgs& p);
+hipError_t launch_topk_bf16(const TopkBf16Args& p);
 hipError_t launch_fused_topk(const FusedArgs& p);
 hipError_t launch_gather(const GatherArgs& p);
 hipError_t launch_v41_scores(const V41Args& p);

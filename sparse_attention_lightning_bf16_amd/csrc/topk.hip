@@ -13,6 +13,8 @@
 //
 // Gather (section pytorch_extract_topk_scores): out = logits[b,t,idx], or -inf
 // for an index outside [0, Skv).
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -618,38 +620,53 @@ __device__ void block_find_bin(BinShared& sh, int need, int tid) {
     __syncthreads();
 }
 
-template <int VEC>
-__global__ __launch_bounds__(kBinThreads) void topk_rows_bin_kernel(const float* __restrict__ logits, int B, int S,
+// BF16 = false: fp32 logits of the causal or given ranges (lix_topk).
+// BF16 = true: V4.1 bf16 scores over whole rows, where bf16 -inf (0xFF80)
+// marks a hidden key: hidden keys are loaded as NaN slots, so they are
+// never binned, ranked or selected; a row with at most topk visible keys
+// selects all of them and pads the rest with (-1, bf16 -inf).  Selected
+// values are written back in the input's type, bit for bit.
+template <int VEC, bool BF16>
+__global__ __launch_bounds__(kBinThreads) void topk_rows_bin_kernel(const void* __restrict__ logits_v, int B, int S,
                                                                     int skv, int ratio,
                                                                     const int32_t* __restrict__ ks,
                                                                     const int32_t* __restrict__ ke, int topk,
-                                                                    float* __restrict__ scores,
+                                                                    void* __restrict__ scores_v,
                                                                     int32_t* __restrict__ indices) {
+    using In = typename std::conditional<BF16, uint16_t, float>::type;
     constexpr int SPAN = 256 * VEC;                           // elements per wave
     __shared__ BinShared sh;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int b = blockIdx.x % B;
     const int t = S - 1 - (int)(blockIdx.x / B);              // longest causal rows first
-    int lo, hi;
-    key_range(ks, ke, t, S, skv, ratio, lo, hi);
+    int lo = 0, hi = skv;
+    if constexpr (!BF16) key_range(ks, ke, t, S, skv, ratio, lo, hi);
     const int n = hi - lo;
-    const float* row = logits + ((long)b * S + t) * skv + lo;
-    float* so = scores + ((long)b * S + t) * topk;
+    const In* logits = static_cast<const In*>(logits_v);
+    const In* row = logits + ((long)b * S + t) * skv + lo;
+    In* so = static_cast<In*>(scores_v) + ((long)b * S + t) * topk;
     int32_t* io = indices + ((long)b * S + t) * topk;
+    auto out_val = [](float v) -> In {
+        if constexpr (BF16) return bf16_bits(v);              // v holds a bf16 value: exact
+        else return v;
+    };
+    const In pad_val = out_val(neg_inf());
 
-    if (n <= topk) {                                          // everything is selected
-        for (int i0 = 0; i0 < n; i0 += 8 * kBinThreads) {
-            float v[8];
+    if constexpr (!BF16) {
+        if (n <= topk) {                                      // everything is selected
+            for (int i0 = 0; i0 < n; i0 += 8 * kBinThreads) {
+                float v[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = row[min(i0 + u * kBinThreads + tid, n - 1)];
+                for (int u = 0; u < 8; ++u) v[u] = row[min(i0 + u * kBinThreads + tid, n - 1)];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int i = i0 + u * kBinThreads + tid;
-                if (i < n) { so[i] = v[u]; io[i] = lo + i; }
+                for (int u = 0; u < 8; ++u) {
+                    const int i = i0 + u * kBinThreads + tid;
+                    if (i < n) { so[i] = v[u]; io[i] = lo + i; }
+                }
             }
+            for (int i = n + tid; i < topk; i += kBinThreads) { so[i] = pad_val; io[i] = -1; }
+            return;
         }
-        for (int i = n + tid; i < topk; i += kBinThreads) { so[i] = neg_inf(); io[i] = -1; }
-        return;
     }
 
     // ---- this wave's part of the row (every load issues before the first wait)
@@ -657,21 +674,31 @@ __global__ __launch_bounds__(kBinThreads) void topk_rows_bin_kernel(const float*
     const int ebase = wv * SPAN;
     const int nloc = max(0, min(n - ebase, SPAN));
     const bool vec_ok = (reinterpret_cast<uintptr_t>(logits) & 15) == 0 && ((skv | lo) & 3) == 0;
+    auto cvt = [&](In raw) -> float {
+        if constexpr (BF16) return raw == (uint16_t)0xff80u ? qnan : bf16_to_f32(raw);
+        else return raw;
+    };
     float x[VEC][4];
 #pragma unroll
     for (int j = 0; j < VEC; ++j) x[j][0] = x[j][1] = x[j][2] = x[j][3] = qnan;
     if (nloc > 0) {
-        const float* wrow = row + ebase;
+        const In* wrow = row + ebase;
         if (vec_ok) {
             const int last = (nloc - 1) & ~3;
 #pragma unroll
             for (int j = 0; j < VEC; ++j) {
                 const int e0 = j * 256 + 4 * lane;
-                const float4 y = *reinterpret_cast<const float4*>(wrow + min(e0, last));
-                x[j][0] = (e0 + 0 < nloc) ? y.x : qnan;
-                x[j][1] = (e0 + 1 < nloc) ? y.y : qnan;
-                x[j][2] = (e0 + 2 < nloc) ? y.z : qnan;
-                x[j][3] = (e0 + 3 < nloc) ? y.w : qnan;
+                In y[4];
+                if constexpr (BF16) {
+                    const uint2 r = *reinterpret_cast<const uint2*>(wrow + min(e0, last));
+                    y[0] = (uint16_t)(r.x & 0xffffu); y[1] = (uint16_t)(r.x >> 16);
+                    y[2] = (uint16_t)(r.y & 0xffffu); y[3] = (uint16_t)(r.y >> 16);
+                } else {
+                    const float4 r = *reinterpret_cast<const float4*>(wrow + min(e0, last));
+                    y[0] = r.x; y[1] = r.y; y[2] = r.z; y[3] = r.w;
+                }
+#pragma unroll
+                for (int m = 0; m < 4; ++m) x[j][m] = (e0 + m < nloc) ? cvt(y[m]) : qnan;
             }
         } else {
 #pragma unroll
@@ -679,11 +706,27 @@ __global__ __launch_bounds__(kBinThreads) void topk_rows_bin_kernel(const float*
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const int e = j * 256 + 4 * lane + m;
-                    const float v = wrow[min(e, nloc - 1)];
-                    x[j][m] = (e < nloc) ? v : qnan;
+                    const In v = wrow[min(e, nloc - 1)];
+                    x[j][m] = (e < nloc) ? cvt(v) : qnan;
                 }
         }
     }
+
+    // ---- bf16 rows: count the visible keys; at most topk of them means all
+    int visible = n;
+    if constexpr (BF16) {
+        int c = 0;
+#pragma unroll
+        for (int j = 0; j < VEC; ++j)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) c += (x[j][m] == x[j][m]) ? 1 : 0;
+        c = __builtin_amdgcn_readlane(wave_incl_scan(c, lane), 63);
+        if (lane == 0) sh.wtot[wv] = c;
+        __syncthreads();
+        visible = sh.wtot[0] + sh.wtot[1] + sh.wtot[2] + sh.wtot[3];
+        __syncthreads();                                      // wtot is reused below
+    }
+    const bool take_all = visible <= topk;                    // same in every thread
 
     // ---- row min / max (NaN slots are ignored)
     float vmin = __uint_as_float(0x7f800000u), vmax = neg_inf();
@@ -708,10 +751,10 @@ __global__ __launch_bounds__(kBinThreads) void topk_rows_bin_kernel(const float*
     const float sc = binned ? 0.99951171875f / span : 0.0f;  // (1 - 2^-11) / span
 
     int bstar = 0, rstar = topk, cb = 1 << 30;
-    if (binned) {
+    if (binned && !take_all) {
 #pragma unroll
         for (int j = 0; j < VEC; ++j) {
-            if ((j + 1) * 256 <= nloc) {                      // whole chunk inside the row
+            if (!BF16 && (j + 1) * 256 <= nloc) {             // whole chunk inside the row (no NaN slots)
 #pragma unroll
                 for (int m = 0; m < 4; ++m) atomicAdd(&sh.hist[score_bin(x[j][m], vmin, sc)], 1u);
             } else if (j * 256 < nloc) {
@@ -729,7 +772,11 @@ __global__ __launch_bounds__(kBinThreads) void topk_rows_bin_kernel(const float*
         cb = (int)sh.hist[bstar];
     }
 
-    if (cb <= kBinCand) {
+    if (take_all) {
+        // ---- at most topk visible keys: every visible key is selected
+        if (tid == 0) { sh.cut_v = neg_inf(); sh.cut_i = 0x7fffffff; }
+        __syncthreads();
+    } else if (cb <= kBinCand) {
         // ---- gather the boundary bin and rank it exactly
 #pragma unroll
         for (int j = 0; j < VEC; ++j)
@@ -847,11 +894,15 @@ __global__ __launch_bounds__(kBinThreads) void topk_rows_bin_kernel(const float*
 #pragma unroll
         for (int m = 0; m < 4; ++m)
             if (((bits >> m) & 1u) && pos < topk) {
-                so[pos] = x[j][m];
+                so[pos] = out_val(x[j][m]);
                 io[pos] = lo + ebase + j * 256 + 4 * lane + m;
                 ++pos;
             }
         run += __builtin_amdgcn_readlane(incl, 63);
+    }
+    if constexpr (BF16) {
+        const int total = sh.wtot[0] + sh.wtot[1] + sh.wtot[2] + sh.wtot[3];
+        for (int i = total + tid; i < topk; i += kBinThreads) { so[i] = pad_val; io[i] = -1; }
     }
 }
 
@@ -884,12 +935,20 @@ hipError_t launch_topk_rows(const TopkArgs& p) {
     } else {
         dim3 grid((unsigned)((long)p.B * p.S));
         if (p.Skv <= 8192)
-            hipLaunchKernelGGL(topk_rows_bin_kernel<8>, grid, dim3(kBinThreads), 0, p.stream, p.logits, p.B, p.S,
-                               p.Skv, p.ratio, p.ks, p.ke, p.topk, p.scores, p.indices);
+            hipLaunchKernelGGL((topk_rows_bin_kernel<8, false>), grid, dim3(kBinThreads), 0, p.stream,
+                               static_cast<const void*>(p.logits), p.B, p.S, p.Skv, p.ratio, p.ks, p.ke, p.topk,
+                               static_cast<void*>(p.scores), p.indices);
         else
             hipLaunchKernelGGL(topk_rows_kernel<0>, grid, dim3(kTopkThreads), 0, p.stream, p.logits, p.B, p.S,
                                p.Skv, p.ratio, p.ks, p.ke, p.topk, p.scores, p.indices);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_topk_bf16(const TopkBf16Args& p) {
+    dim3 grid((unsigned)((long)p.B * p.L));
+    hipLaunchKernelGGL((topk_rows_bin_kernel<8, true>), grid, dim3(kBinThreads), 0, p.stream, p.scores, p.B, p.L,
+                       p.G, 1, nullptr, nullptr, p.topk, p.out_scores, p.indices);
     return hipGetLastError();
 }
 

@@ -168,6 +168,20 @@ def indexer_scores_v41(queries, keys, weights, allowed):
     return out
 
 
+def topk_bf16(scores, topk):
+    """lix_topk_bf16: per-row top-k of V4.1 bf16 scores [B,L,G] over the visible keys (score != bf16 -inf).
+    Returns (scores bf16 [B,L,topk], indices int32 [B,L,topk]); selected keys in ascending index order,
+    rows with fewer visible keys padded (-inf, -1)."""
+    _need(scores, "scores", torch.bfloat16, 3)
+    B, L, G = scores.shape
+    out = torch.empty(B, L, topk, dtype=torch.bfloat16, device=scores.device)
+    idx = torch.empty(B, L, topk, dtype=torch.int32, device=scores.device)
+    st = _lib.load().lix_topk_bf16(scores.data_ptr(), B, L, G, int(topk), out.data_ptr(), idx.data_ptr(),
+                                   _stream(scores.device))
+    _lib.check(st, "lix_topk_bf16")
+    return out, idx
+
+
 def v4_lighting_indexer(index_q, index_k, weights, compress_ratio, topk, topk_indices=None):
     """The pages' main entry point (the misspelt name is the pages' own).
 

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function():
     lib = lx.load()
     names = declared_functions()
     assert set(names) == {"lix_status_string", "lix_version", "lix_indexer_logits", "lix_topk",
-                          "lix_topk_scores", "lix_indexer_scores_v41", "lix_indexer_scores_at"}
+                          "lix_topk_scores", "lix_indexer_scores_v41", "lix_indexer_scores_at", "lix_topk_bf16"}
     for name in names:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES
@@ -125,6 +125,19 @@ def scores_at_call(q=P, k=P, w=P, idx=P, B=1, S=8, Skv=4, H=64, D=128, c=4, ks=N
 def test_scores_at_validation(kw, code):
     # topk may exceed Skv here (given indices need not be distinct)
     assert scores_at_call(**kw) == code
+
+
+def topk_bf16_call(sc=P, B=1, L=8, G=16, topk=4, out=P, idx=P):
+    return lx.load().lix_topk_bf16(sc, B, L, G, topk, out, idx, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(sc=None), NULL), (dict(out=None), NULL), (dict(idx=None), NULL),
+    (dict(B=0), SHAPE), (dict(L=-1), SHAPE), (dict(G=0), SHAPE), (dict(topk=0), SHAPE), (dict(topk=17), SHAPE),
+    (dict(G=8193, topk=4), UNSUP), (dict(sc=P + 1), UNSUP), (dict(out=P + 1), UNSUP), (dict(idx=P + 2), UNSUP),
+])
+def test_topk_bf16_validation(kw, code):
+    assert topk_bf16_call(**kw) == code
 
 
 def test_python_binding_rejects_bad_tensors_before_the_library():

@@ -422,6 +422,52 @@ def test_v41_workload_sampled_rows():
     log(f"  v41 workload: allowed fraction {allowed_frac:.4f}; outputs needing the interval: {widened}")
 
 
+# ------------------------------------------------------------------ V4.1 top-k over bf16 scores
+
+def _bf16_rows(g, B, L, G, hidden_frac):
+    pool = torch.tensor([0x3F80, 0xBF80, 0x0000, 0x8000, 0x4000, 0x3F00, 0xC040, 0x3E80, 0x4040],
+                        dtype=torch.int32)
+    bits = pool[torch.randint(0, len(pool), (B, L, G), generator=g)]
+    noise = torch.randint(0, 0x7F80, (B, L, G), generator=g, dtype=torch.int32)     # finite magnitudes
+    noise = noise | (torch.randint(0, 2, (B, L, G), generator=g, dtype=torch.int32) << 15)   # either sign
+    dense = torch.rand(B, L, G, generator=g) < 0.5
+    bits = torch.where(dense, noise, bits)                 # half from a small pool (ties), half arbitrary finite
+    bits[torch.rand(B, L, G, generator=g) < hidden_frac] = 0xFF80
+    return bits.to(torch.int16)
+
+
+@pytest.mark.parametrize("G", [100, 2048, 4096, 6000, 8192])
+def test_topk_bf16_matches_oracle_bitwise(G):
+    g = torch.Generator().manual_seed(300 + G)
+    B, L = 2, 12
+    bits = _bf16_rows(g, B, L, G, 0.4)
+    bits[0, 0] = 0xFF80 - 0x10000                          # nothing visible
+    bits[0, 1, 5:] = 0xFF80 - 0x10000                      # 5 visible keys
+    bits[1, 2] = 0x3F80                                    # all equal
+    scores = bits.view(torch.bfloat16)
+    for tk in (1, 17, max(1, G // 3), G):
+        log(f"topk_bf16 G={G} topk={tk}")
+        sc, ix = lx.topk_bf16(dev(scores), tk)
+        sc = sc.cpu().view(torch.int16).numpy().view(np.uint16)
+        ix = ix.cpu().numpy()
+        for b in range(B):
+            want_b, want_i = oracle.topk_select_visible_bf16(bits[b].numpy().view(np.uint16), tk)
+            assert np.array_equal(ix[b], want_i), (G, tk, b)
+            assert np.array_equal(sc[b], want_b), (G, tk, b)
+
+
+def test_topk_bf16_after_v41_workload_sampled_rows():
+    cfg = synth.WORKLOADS["v41"]
+    inp = synth.v41_inputs(**cfg)
+    got = lx.indexer_scores_v41(*(dev(inp[x]) for x in ("queries", "keys", "weights", "allowed")))
+    sc, ix = lx.topk_bf16(got, 512)
+    rows = np.arange(7, cfg["local_sequence"], 97)
+    bits = got[0].cpu().view(torch.int16).numpy().view(np.uint16)[rows]
+    want_b, want_i = oracle.topk_select_visible_bf16(bits, 512)
+    assert np.array_equal(ix[0].cpu().numpy()[rows], want_i)
+    assert np.array_equal(sc[0].cpu().view(torch.int16).numpy().view(np.uint16)[rows], want_b)
+
+
 def test_device_properties_logged():
     p = torch.cuda.get_device_properties(0)
     log(f"device: {p.name} gcn={getattr(p, 'gcnArchName', '?')} CUs={p.multi_processor_count} "

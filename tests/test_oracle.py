@@ -289,6 +289,26 @@ def test_topk_padding_and_empty_rows():
     assert list(i[1]) == [3, 4, -1, -1] and list(s[1][:2]) == [9.0, 10.0]
 
 
+def test_topk_visible_bf16_brute_force():
+    # Rows drawn from a handful of bf16 values (heavy ties, both zeros) with
+    # hidden keys; the expected selection is a plain Python sort.
+    rng = np.random.default_rng(12)
+    pool = np.array([0x3F80, 0xBF80, 0x0000, 0x8000, 0x4000, 0x3F00, 0xC040], dtype=np.uint16)
+    value = {0x3F80: 1.0, 0xBF80: -1.0, 0x0000: 0.0, 0x8000: 0.0, 0x4000: 2.0, 0x3F00: 0.5, 0xC040: -3.0}
+    bits = pool[rng.integers(0, len(pool), size=(30, 40))]
+    bits[rng.random((30, 40)) < 0.35] = 0xFF80          # hidden
+    bits[5] = 0xFF80                                    # a row with nothing visible
+    for tk in (1, 3, 11, 40):
+        got_b, got_i = oracle.topk_select_visible_bf16(bits, tk)
+        for r in range(30):
+            vis = [j for j in range(40) if bits[r, j] != 0xFF80]
+            best = sorted(sorted(vis, key=lambda j: (-value[int(bits[r, j])], j))[:tk])
+            m = len(best)
+            assert list(got_i[r, :m]) == best, (tk, r)
+            assert list(got_b[r, :m]) == [bits[r, j] for j in best]
+            assert (got_i[r, m:] == -1).all() and (got_b[r, m:] == 0xFF80).all()
+
+
 def test_gather_brute_force():
     rng = np.random.default_rng(11)
     lg = rng.standard_normal((2, 5, 9))
