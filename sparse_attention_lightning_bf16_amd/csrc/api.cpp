@@ -62,19 +62,6 @@ int launch_status(hipError_t e) { return e == hipSuccess ? LIX_OK : LIX_ERR_LAUN
 
 }  // namespace
 
-namespace lix {
-
-long persistent_slots(const void* kernel, int threads, size_t dyn_lds) {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 1;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, dyn_lds) != hipSuccess || per_cu < 1)
-        per_cu = 1;
-    return (long)cus * per_cu;
-}
-
-}  // namespace lix
-
 extern "C" {
 
 const char* lix_status_string(int status) {

@@ -7,10 +7,6 @@
 
 namespace lix {
 
-// Workgroups of `kernel` that fit on the current device at once (CUs times
-// resident workgroups per CU): the grid size of a persistent launch.
-long persistent_slots(const void* kernel, int threads, size_t dyn_lds);
-
 // index_dim rounded up to the compiled fragment depth (zero-padded in the kernels).
 inline int padded_dim(int D) { return D <= 32 ? 32 : D <= 64 ? 64 : D <= 128 ? 128 : 256; }
 

@@ -9,7 +9,7 @@
 // where allowed[b,t,s], bf16 -inf elsewhere; the head sum is fp32.
 //
 // One workgroup = 4 waves = QB consecutive queries of one batch element.
-// Key stages [s0, s0+64) that lie outside every range of the workgroup are
+// Key stages [s0, s0+KT) that lie outside every range of the workgroup are
 // never computed (causal tile skip); their logits are filled with -inf.
 #include "score_core.h"
 #include "launch.h"

@@ -154,21 +154,6 @@ __device__ __forceinline__ void stream_key_stages(const InLayout& L, int b, int 
     }
 }
 
-// d for the wave's rows against the 32 keys of column block cb of a staged tile.
-template <class T>
-__device__ __forceinline__ void mfma_block(f32x16 (&acc)[T::NRT], const bf16x8 (&a)[T::NRT][T::NSTEP],
-                                           const uint8_t* stage, int cb, int lane) {
-#pragma unroll
-    for (int r = 0; r < T::NRT; ++r) acc[r] = f32x16{};
-#pragma unroll
-    for (int st = 0; st < T::NSTEP; ++st) {
-        const u32x4 bv = *reinterpret_cast<const u32x4*>(stage + stage_offset<T>(cb, st, lane));
-        const bf16x8 bfrag = as_bf16x8(bv);
-#pragma unroll
-        for (int r = 0; r < T::NRT; ++r) acc[r] = mfma_32x32x16(a[r][st], bfrag, acc[r]);
-    }
-}
-
 // B fragment of column block cb, k-step st of a staged tile.
 template <class T>
 __device__ __forceinline__ bf16x8 b_frag(const uint8_t* stage, int cb, int st, int lane) {
