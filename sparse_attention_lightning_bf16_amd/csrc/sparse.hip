@@ -10,12 +10,14 @@
 // One wave (one workgroup) per (b, t).  Its MFMA rows are the query's heads,
 // padded with zero rows of zero weight up to whole 32-row tiles; its columns
 // walk the indices in blocks of 32.  A block's key rows are gathered by
-// direct global->LDS loads (one 64-lane load of 16 bytes per lane for each
-// k-step) into the wave's own LDS buffer in B-fragment order, double
-// buffered, so no barrier is needed.  The MFMA chain and the epilogue visit
-// a score's terms in the same order as the scoring stage of the logits
-// kernel (padded rows add exact zeros), so each score equals the
-// materialized logit bit for bit.
+// direct global->LDS loads into the wave's own LDS buffer, double buffered,
+// so no barrier is needed.  Each load moves whole row segments of up to 128
+// bytes (one cache line) per group of lanes, not one 16-byte chunk of 32
+// different rows, and places the chunks with an XOR swizzle so that the
+// B-fragment reads stay free of bank conflicts (BlockMap).  The MFMA chain
+// and the epilogue visit a score's terms in the same order as the scoring
+// stage of the logits kernel (padded rows add exact zeros), so each score
+// equals the materialized logit bit for bit.
 #include "score_core.h"
 #include "launch.h"
 
@@ -35,6 +37,33 @@ struct SparseTiling {
     static constexpr int BLOCK_BYTES = NSTEP * 1024;    // one 32-key block in LDS
 };
 
+// LDS placement of one gathered 32-key block (NLOAD loads of 64 lanes x 16
+// bytes).  Load ld, lane L carries row segment p = RPI*ld + L/SEG, i.e. key
+// row p % 32, chunks SEG*(p/32) .. +SEG-1, and within the segment the chunk
+// (L % SEG) ^ swz(ld, L/SEG): consecutive lanes read one contiguous piece of
+// a key row.  The swizzle makes the 16 (and each 8) consecutive lanes of a
+// B-fragment read hit distinct 16-byte bank groups.
+template <int DP>
+struct BlockMap {
+    static constexpr int CPK = DP / 8;                  // 16-byte chunks per key row
+    static constexpr int SEG = CPK < 8 ? CPK : 8;       // chunks per row segment
+    static constexpr int RPI = 64 / SEG;                // row segments per load
+    static constexpr int NLOAD = 32 * CPK / 64;         // loads per block
+    static constexpr int NSTEP = DP / 16;
+    static constexpr int KR = SEG == 8 ? 4 : NSTEP;     // distinct per-lane read offsets
+    static_assert(SEG == 4 || SEG == 8, "row segments of 4 or 8 chunks");
+    __device__ static constexpr int swz(int ld, int m) {
+        return SEG == 8 ? (m ^ (ld & 1)) : (((m >> 1) ^ (m >> 3)) & (SEG - 1));
+    }
+    // Byte offset of this lane's B fragment for k-step st: key row lane % 32,
+    // chunk 2 st + lane / 32.  Equals frag_off(st % KR) + 4096 (st / KR).
+    __device__ static constexpr int frag_off(int st, int lane) {
+        const int r = lane & 31, c = 2 * st + (lane >> 5);
+        const int p = 32 * (c / SEG) + r, ld = p / RPI, m = p % RPI;
+        return 1024 * ld + 16 * (SEG * m + ((c % SEG) ^ swz(ld, m)));
+    }
+};
+
 template <int H, int DP>
 __global__ __launch_bounds__(64, H >= 128 ? 1 : 2) void sparse_scores_kernel(InLayout L, const float* __restrict__ w,
                                                               const int32_t* __restrict__ indices, int B, int S,
@@ -42,6 +71,7 @@ __global__ __launch_bounds__(64, H >= 128 ? 1 : 2) void sparse_scores_kernel(InL
                                                               const int32_t* __restrict__ ke, int topk,
                                                               float* __restrict__ out) {
     using T = SparseTiling<H, DP>;
+    using M = BlockMap<DP>;
     __shared__ __attribute__((aligned(16))) uint8_t buf0[T::BLOCK_BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t buf1[T::BLOCK_BYTES];
 
@@ -88,15 +118,28 @@ __global__ __launch_bounds__(64, H >= 128 ? 1 : 2) void sparse_scores_kernel(InL
     auto load_idx = [&](int blk) { return ib[min(32 * blk + (lane & 31), topk - 1)]; };
     auto visible = [&](int idx, int blk) { return 32 * blk + (lane & 31) < topk && idx >= lo && idx < hi; };
     // Gather the 32 key rows of a block (invalid entries fetch key row 0).
+    // The row of each load's lane comes from the lane that holds that entry.
+    constexpr int NR = (32 / M::RPI) < M::NLOAD ? (32 / M::RPI) : M::NLOAD;
     auto gather = [&](uint8_t* buf, int idx, int blk) {
         const int s = visible(idx, blk) ? idx : 0;
-        const uint16_t* row = kb + (long)s * L.k_s;
+        const int m = lane / M::SEG, cp = lane % M::SEG;
+        int rows[NR];
 #pragma unroll
-        for (int st = 0; st < T::NSTEP; ++st) {
-            const int d8 = min(2 * st + hf, dlim);
-            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(row + 8 * d8),
-                                             (lds_ptr_t)(buf + st * kWave * 16), 16, 0, 0);
+        for (int j = 0; j < NR; ++j) rows[j] = __shfl(s, (M::RPI * j + m) & 31);
+#pragma unroll
+        for (int ld = 0; ld < M::NLOAD; ++ld) {
+            const int p = M::RPI * ld + m;
+            const int d8 = min(M::SEG * (p >> 5) + (cp ^ M::swz(ld, m)), dlim);
+            const uint16_t* src = kb + (long)rows[ld % NR] * L.k_s + 8 * d8;
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                             (lds_ptr_t)(buf + ld * kWave * 16), 16, 0, 0);
         }
+    };
+    int fofs[M::KR];
+#pragma unroll
+    for (int k = 0; k < M::KR; ++k) fofs[k] = M::frag_off(k, lane);
+    auto bfrag = [&](const uint8_t* buf, int st) {
+        return as_bf16x8(*reinterpret_cast<const u32x4*>(buf + fofs[st % M::KR] + 4096 * (st / M::KR)));
     };
     // Score block blk from buf: the MFMA chain, then the epilogue in the
     // scoring stage's element order, then the half-wave sum.
@@ -104,12 +147,11 @@ __global__ __launch_bounds__(64, H >= 128 ? 1 : 2) void sparse_scores_kernel(InL
         float res = neg_inf();
         if (active) {
             f32x16 acc[T::NRT];
-            bf16x8 bn = as_bf16x8(*reinterpret_cast<const u32x4*>(buf + 16 * lane));
+            bf16x8 bn = bfrag(buf, 0);
 #pragma unroll
             for (int st = 0; st < T::NSTEP; ++st) {
                 const bf16x8 bc = bn;
-                if (st + 1 < T::NSTEP)
-                    bn = as_bf16x8(*reinterpret_cast<const u32x4*>(buf + (st + 1) * 1024 + 16 * lane));
+                if (st + 1 < T::NSTEP) bn = bfrag(buf, st + 1);
 #pragma unroll
                 for (int r = 0; r < T::NRT; ++r)
                     acc[r] = mfma_32x32x16(a[r][st], bc, st == 0 ? f32x16{} : acc[r]);
