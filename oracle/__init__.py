@@ -6,7 +6,8 @@ CPU-baseline leg are the only code allowed to import it.  The product path
 this package never imports the product path: the two share no code.
 
 Everything is NumPy float64, with bfloat16 rounding emulated from its
-definition where the V4.1 page fixes rounding points.
+definition where the V4.1 page fixes rounding points.  ``indexer_grad``
+holds the backward pass (gradients of the selected scores).
 """
 
 from .indexer import (  # noqa: F401
@@ -26,3 +27,4 @@ from .indexer import (  # noqa: F401
     indexer_scores_v41,
     indexer_scores_v41_bounds_rows,
 )
+from .indexer_grad import indexer_backward  # noqa: F401

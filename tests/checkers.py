@@ -14,6 +14,12 @@ Test infrastructure.  Tolerances:
 * V4.1 scores: within 2 bf16 ulp of the oracle, or inside the interval the
   oracle derives for float32 accumulation in any order; -inf exactly where
   hidden.
+* Backward (dq, dk, dw): |g - o| <= 2**-8 * mag + amb + 1e-6, with mag and
+  amb from the oracle: the kernel's gradient GEMMs take one bfloat16-rounded
+  factor per term (g_j for dq, w_h for dk: relative error <= 2**-9) and add
+  in float32 (<= 2**-24 per addition, far below 2**-9 for the term counts
+  here); amb covers (head, key) pairs whose dot product a float32 sum may put
+  on the other side of 0.
 """
 
 import numpy as np
@@ -111,3 +117,22 @@ def check_v41(gpu_bits, ora, lo, hi, where=""):
     assert ok.all(), (f"{where}: {int((~ok).sum())} V4.1 scores beyond 2 ulp and outside the "
                       f"accumulation interval")
     return int((~near & inside).sum())
+
+
+BACKWARD_REL = 2.0 ** -8
+
+
+def check_backward(got, grads, bounds, where=""):
+    """got: dict name -> float32 array for "dq", "dk", "dw"; grads: the
+    oracle's (dq, dk, dw); bounds: its with_bounds dict."""
+    for name, ora in zip(("dq", "dk", "dw"), grads):
+        g = np.asarray(got[name], dtype=np.float64)
+        assert g.shape == ora.shape, (name, g.shape, ora.shape)
+        mag, amb = bounds[name]
+        tol = BACKWARD_REL * mag + amb + 1e-6
+        err = np.abs(g - ora)
+        bad = ~(err <= tol)
+        if bad.any():
+            i = tuple(int(x) for x in np.argwhere(bad)[0])
+            raise AssertionError(f"{where} {name}: {int(bad.sum())} of {bad.size} outside tolerance; first at {i}: "
+                                 f"got {g[i]!r} oracle {ora[i]!r} tol {tol[i]!r}")

@@ -425,3 +425,184 @@ def test_topk_checker_accepts_oracle_and_rejects_planted_errors():
     bad_pad[0, 0] = 0
     with pytest.raises(AssertionError):
         checkers.check_topk_rows(s.astype(np.float32), bad_pad, lg[0], mag[0], ks, ke, 4)
+
+
+# ---------------------------------------------------------------------------
+# Backward: gradients of the selected scores with respect to q, k and w
+# ---------------------------------------------------------------------------
+
+def _bw_case(seed, S=6, B=2, Skv=9, H=4, D=8, topk=5, ratio=1, nonneg=False):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((S, B, H, D))
+    k = rng.standard_normal((Skv, B, D))
+    w = rng.standard_normal((S, B, H))
+    if nonneg:
+        q, k = np.abs(q) + 0.1, np.abs(k) + 0.1
+    ks, ke = oracle.causal_ranges(S, Skv, ratio)
+    idx = rng.integers(-2, Skv + 2, size=(B, S, topk))     # -2, -1, Skv, Skv+1 are invalid
+    g = rng.standard_normal((B, S, topk))
+    return q, k, w, ks, ke, idx, g
+
+
+def _selected_loss(q, k, w, idx, g, ks, ke):
+    """sum of g * score over the valid entries, with the scores taken from the
+    forward oracle (full logits, then the gather at the indices)."""
+    sc = oracle.topk_scores_gather(oracle.indexer_logits(q, k, w, ks, ke), idx)
+    return float(np.sum(np.where(np.isfinite(sc), sc * g, 0.0)))
+
+
+def _valid_mask(k, idx, ks, ke):
+    S = len(ks)
+    t = np.arange(S)[None, :, None]
+    lo = np.clip(np.asarray(ks)[t], 0, k.shape[0])
+    hi = np.clip(np.asarray(ke)[t], 0, k.shape[0])
+    return (idx >= lo) & (idx < hi)
+
+
+@pytest.mark.parametrize("ratio", [1, 2])
+def test_backward_matches_central_differences_of_the_forward(ratio):
+    # The loss is piecewise linear along any direction in q, k or w (d is
+    # linear in each, the ReLU piecewise linear), so a central difference
+    # with a small step equals the directional derivative up to rounding.
+    q, k, w, ks, ke, idx, g = _bw_case(10 + ratio, ratio=ratio)
+    grads = dict(zip("qkw", oracle.indexer_backward(q, k, w, idx, g, ks, ke)))
+    rng = np.random.default_rng(7)
+    eps = 1e-6
+    for name in "qkw":
+        for _ in range(3):
+            v = rng.standard_normal(grads[name].shape)
+
+            def loss(step):
+                args = {"q": q, "k": k, "w": w}
+                args[name] = args[name] + step * v
+                return _selected_loss(args["q"], args["k"], args["w"], idx, g, ks, ke)
+
+            fd = (loss(eps) - loss(-eps)) / (2 * eps)
+            assert fd == pytest.approx(float(np.sum(grads[name] * v)), rel=1e-6, abs=1e-8), name
+
+
+def test_backward_coordinate_differences():
+    q, k, w, ks, ke, idx, g = _bw_case(20, S=4, Skv=5, H=2, D=4, topk=4)
+    dq, dk, dw = oracle.indexer_backward(q, k, w, idx, g, ks, ke)
+    eps = 1e-6
+    for name, x, grad in (("q", q, dq), ("k", k, dk), ("w", w, dw)):
+        for pos in np.ndindex(x.shape):
+            e = np.zeros_like(x)
+            e[pos] = eps
+            args_p = {"q": q, "k": k, "w": w}
+            args_m = dict(args_p)
+            args_p[name], args_m[name] = x + e, x - e
+            fd = (_selected_loss(args_p["q"], args_p["k"], args_p["w"], idx, g, ks, ke)
+                  - _selected_loss(args_m["q"], args_m["k"], args_m["w"], idx, g, ks, ke)) / (2 * eps)
+            assert fd == pytest.approx(grad[pos], rel=1e-6, abs=1e-8), (name, pos)
+
+
+def test_backward_nonnegative_operands_closed_form():
+    # q, k > 0 puts every d above 0: the score is k_s . u with u = sum_h w_h q_h,
+    # so dq_h = w_h sum_j g_j k_j, dk_s = sum_(t,j) g_j u_t, dw_h = sum_j g_j q_h . k_j.
+    q, k, w, ks, ke, idx, g = _bw_case(30, nonneg=True)
+    dq, dk, dw = oracle.indexer_backward(q, k, w, idx, g, ks, ke)
+    S, B, H, D = q.shape
+    e_dq, e_dk, e_dw = np.zeros_like(q), np.zeros_like(k), np.zeros_like(w)
+    for b in range(B):
+        for t in range(S):
+            u = w[t, b] @ q[t, b]
+            for j in range(idx.shape[2]):
+                s = idx[b, t, j]
+                if not (ks[t] <= s < min(ke[t], k.shape[0])):
+                    continue
+                e_dq[t, b] += g[b, t, j] * np.outer(w[t, b], k[s, b])
+                e_dk[s, b] += g[b, t, j] * u
+                e_dw[t, b] += g[b, t, j] * (q[t, b] @ k[s, b])
+    np.testing.assert_allclose(dq, e_dq, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dk, e_dk, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dw, e_dw, rtol=1e-12, atol=1e-12)
+
+
+def test_backward_all_nonpositive_dots_give_no_q_k_gradient():
+    # k = -q_0-like signs: with q >= 0 and k <= 0 every d <= 0, so the ReLU
+    # is flat: every gradient is zero.
+    q, k, w, ks, ke, idx, g = _bw_case(31, nonneg=True)
+    dq, dk, dw = oracle.indexer_backward(q, -k, w, idx, g, ks, ke)
+    assert not dq.any() and not dk.any() and not dw.any()
+
+
+def test_backward_ignores_invalid_entries_and_is_linear_in_the_gradient():
+    q, k, w, ks, ke, idx, g = _bw_case(40)
+    valid = _valid_mask(k, idx, ks, ke)
+    assert valid.any() and (~valid).any()
+    base = oracle.indexer_backward(q, k, w, idx, g, ks, ke)
+    noisy = np.where(valid, g, 1e6)
+    for a, b in zip(base, oracle.indexer_backward(q, k, w, idx, noisy, ks, ke)):
+        np.testing.assert_array_equal(a, b)
+    for a, b in zip(base, oracle.indexer_backward(q, k, w, idx, 2.0 * g, ks, ke)):
+        np.testing.assert_allclose(b, 2.0 * a, rtol=1e-13, atol=1e-13)
+    for a in oracle.indexer_backward(q, k, w, idx, np.zeros_like(g), ks, ke):
+        assert not a.any()
+
+
+def test_backward_duplicate_index_counts_twice():
+    q, k, w, ks, ke, _, _ = _bw_case(50, S=5, Skv=5, topk=3)
+    B = q.shape[1]
+    idx = np.full((B, 5, 3), -1)
+    g = np.zeros((B, 5, 3))
+    idx[1, 4, :2] = 3
+    g[1, 4, :2] = (0.75, -2.0)
+    one = np.full_like(idx, -1)
+    g1 = np.zeros_like(g)
+    one[1, 4, 2] = 3
+    g1[1, 4, 2] = -1.25
+    for a, b in zip(oracle.indexer_backward(q, k, w, idx, g, ks, ke),
+                    oracle.indexer_backward(q, k, w, one, g1, ks, ke)):
+        np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-13)
+
+
+def test_backward_bounds_contain_values():
+    q, k, w, ks, ke, idx, g = _bw_case(60)
+    grads, bounds = oracle.indexer_backward(q, k, w, idx, g, ks, ke, with_bounds=True)
+    for name, x in zip(("dq", "dk", "dw"), grads):
+        mag, amb = bounds[name]
+        assert np.all(np.abs(x) <= mag * (1 + 1e-12) + 1e-300)
+        assert np.all((amb >= 0) & (amb <= mag + 1e-300))
+    # Only near-zero dot products count as ambiguous: none here.
+    assert not any(bounds[n][1].any() for n in ("dq", "dk", "dw"))
+    for a, b in zip(grads, oracle.indexer_backward(q, k, w, idx, g, ks, ke)):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_backward_bounds_flag_zero_dot_products():
+    # A key orthogonal to one head's query: d = 0 exactly, which a float32
+    # dot product may place on either side of 0.
+    q, k, w, ks, ke, idx, g = _bw_case(61, S=3, B=1, Skv=3, H=2, D=4, topk=2, nonneg=True)
+    q[2, 0, 1] = (1.0, -1.0, 0.0, 0.0)
+    k[1, 0] = (2.0, 2.0, 5.0, 1.0)
+    idx[0, 2] = (1, -1)
+    _, bounds = oracle.indexer_backward(q, k, w, idx, g, ks, ke, with_bounds=True)
+    amb_dq = bounds["dq"][1]
+    assert amb_dq[2, 0, 1].any() and not amb_dq[2, 0, 0].any()
+
+
+def test_backward_checker_accepts_bf16_rounding_and_rejects_planted_errors():
+    q, k, w, ks, ke, idx, g = _bw_case(70, S=8, Skv=10, H=8, D=16, topk=6)
+    grads, bounds = oracle.indexer_backward(q, k, w, idx, g, ks, ke, with_bounds=True)
+    names = ("dq", "dk", "dw")
+    checkers.check_backward(dict(zip(names, grads)), grads, bounds)
+    # What a kernel with bf16-rounded gradient factors computes passes too.
+    g16 = oracle.rne_bf16(g)
+    w16 = oracle.rne_bf16(w)
+    dq16 = oracle.indexer_backward(q, k, w, idx, g16, ks, ke)[0]
+    dk16 = oracle.indexer_backward(q, k, w16, idx, g, ks, ke)[1]
+    checkers.check_backward({"dq": dq16, "dk": dk16, "dw": grads[2]}, grads, bounds)
+    # Planted mistakes in the oracle's arithmetic are caught.
+    planted = {
+        "dq without w": oracle.indexer_backward(q, k, np.ones_like(w), idx, g, ks, ke)[0],
+        "dq with the ReLU mask dropped": oracle.indexer_backward(np.abs(q), np.abs(k), w, idx, g, ks, ke)[0],
+        "dq with the sign of g flipped": -grads[0],
+    }
+    for what, bad in planted.items():
+        with pytest.raises(AssertionError):
+            checkers.check_backward({"dq": bad, "dk": grads[1], "dw": grads[2]}, grads, bounds)
+    with pytest.raises(AssertionError):
+        checkers.check_backward({"dq": grads[0], "dk": grads[1][::-1].copy(), "dw": grads[2]}, grads, bounds)
+    with pytest.raises(AssertionError):
+        checkers.check_backward({"dq": grads[0], "dk": grads[1], "dw": grads[2] * 1.01}, grads, bounds)
