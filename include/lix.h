@@ -162,6 +162,37 @@ int lix_indexer_scores_at(const void* q, const void* k, const float* w, const in
                           float* scores, hipStream_t stream);
 
 /*
+ * lix_indexer_backward - gradients of the scores at given indices.
+ *
+ * Page "...deepseek_v4.kernels.tilelang_indexer", class V4IndexerFunction:
+ * backward(grad_scores, grad_indices) of the forward above (the pages print
+ * no formula; this is the chain rule on the forward definition).  For each
+ * entry j of query (b, t) whose key i = indices[b,t,j] lies in [ks[t], ke[t])
+ * (ranges as for lix_indexer_logits), with g = grad_scores[b,t,j],
+ * d_h = q[t,b,h,:] . k[i,b,:] and m_h = 1 if d_h > 0 else 0:
+ *     dw[t,b,h]   += g * max(0, d_h)
+ *     dq[t,b,h,:] += g * w[t,b,h] * m_h * k[i,b,:]
+ *     dk[i,b,:]   += g * sum_h w[t,b,h] * m_h * q[t,b,h,:]
+ * Other entries contribute nothing (their score is the constant -inf,
+ * whatever their grad_scores value); a key listed twice contributes twice;
+ * the indices get no gradient.  The products take one bf16-rounded factor per
+ * term (g for dq, w for dk) and accumulate in fp32; dk is summed over queries
+ * with fp32 atomics, so its low bits vary from run to run.
+ *
+ *   q, k, w      as in lix_indexer_logits; heads H <= 64, 32 < D <= 128
+ *   indices      int32 [B, S, topk]  (any values)
+ *   grad_scores  fp32  [B, S, topk]
+ *   dq           fp32  [S, B, H, D]    out (every element written)
+ *   dk           fp32  [Skv, B, D]     out (cleared by the call, 16-byte aligned)
+ *   dw           fp32  [S, B, H]       out (every element written)
+ * Other H or D: LIX_ERR_UNSUPPORTED.
+ */
+int lix_indexer_backward(const void* q, const void* k, const float* w, const int32_t* indices,
+                         const float* grad_scores, int B, int S, int Skv, int H, int D,
+                         int compress_ratio, const int32_t* ks, const int32_t* ke, int topk,
+                         float* dq, float* dk, float* dw, hipStream_t stream);
+
+/*
  * lix_indexer_scores_v41 - V4.1 BF16-rounded scores with a visibility mask.
  *
  * Page "...deepseek_v41.indexer", module description (the GEMM output and

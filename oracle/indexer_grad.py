@@ -42,12 +42,14 @@ def _valid_entries(indices_row, lo, hi):
     return (idx >= lo) & (idx < hi)
 
 
-def indexer_backward(q, k, w, indices, grad_scores, ks, ke, with_bounds=False):
+def indexer_backward(q, k, w, indices, grad_scores, ks, ke, with_bounds=False, rows=None):
     """dq [S,B,H,D], dk [Skv,B,D], dw [S,B,H] in float64.
 
     q [S,B,H,D], k [Skv,B,D], w [S,B,H]; indices and grad_scores [B,S,topk];
     ks, ke [S] shared by every batch element (``causal_ranges`` gives the
-    causal ones).
+    causal ones).  With ``rows`` (query positions) only those queries are
+    processed: their dq and dw are complete, other queries' stay 0, and dk
+    holds only their contributions.
 
     With ``with_bounds`` also returns, for each output, a pair (mag, amb):
 
@@ -70,9 +72,10 @@ def indexer_backward(q, k, w, indices, grad_scores, ks, ke, with_bounds=False):
     if with_bounds:
         mag = {n: np.zeros_like(a) for n, a in (("dq", dq), ("dk", dk), ("dw", dw))}
         amb = {n: np.zeros_like(a) for n, a in (("dq", dq), ("dk", dk), ("dw", dw))}
+    query_rows = range(S) if rows is None else [int(t) for t in rows]
     for b in range(B):
         kb = _f64(k[:, b, :])                               # [Skv, D]
-        for t in range(S):
+        for t in query_rows:
             lo, hi = _clamped_range(ks, ke, t, n_kv)
             ok = _valid_entries(indices[b, t], lo, hi)
             if not ok.any():

@@ -1,4 +1,4 @@
-"""MI355X-native DeepSeek-V4 lightning indexer (forward).
+"""MI355X-native DeepSeek-V4 lightning indexer (forward and backward).
 
 The arithmetic lives in hand-written gfx950 HIP kernels behind the C ABI of
 liblix.so (include/lix.h); this package only binds it.
@@ -11,6 +11,8 @@ from .ops import (  # noqa: F401
     topk_from_logits,
     topk_scores,
     indexer_scores_at,
+    indexer_backward,
+    V4IndexerFunction,
     indexer_scores_v41,
     topk_bf16,
     v4_lighting_indexer,

@@ -26,6 +26,7 @@ SIGNATURES = {
     "lix_indexer_scores_v41": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
     "lix_indexer_scores_at": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P]),
     "lix_topk_bf16": (_I, [_P, _I, _I, _I, _I, _P, _P, _P]),
+    "lix_indexer_backward": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P, _P]),
 }
 
 _lib = None

@@ -17,7 +17,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblix.so")
-SOURCES = ["api.cpp", "score.hip", "topk.hip", "fused.hip", "sparse.hip"]
+SOURCES = ["api.cpp", "score.hip", "topk.hip", "fused.hip", "sparse.hip", "backward.hip"]
+# Units whose MFMA accumulators may live in AGPRs (more than 256 registers of
+# accumulators and operands at one wave per SIMD).
+AGPR_SOURCES = {"backward.hip"}
 ARCH = "gfx950"
 
 
@@ -28,19 +31,19 @@ def hipcc():
     raise RuntimeError("hipcc not found (ROCm is required to build liblix)")
 
 
-def common_flags():
-    return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
-            # keep packed fp32 VALU instructions out of the device code
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            # MFMA accumulators in VGPRs: the epilogue reads them directly
-            "-mllvm", "-amdgpu-mfma-vgpr-form",
-            "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-            "-Wall", "-Wno-unused-result"]
+def common_flags(src=""):
+    flags = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+             # keep packed fp32 VALU instructions out of the device code
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+    if src not in AGPR_SOURCES:
+        # MFMA accumulators in VGPRs: the epilogue reads them directly
+        flags += ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+    return flags + ["-I", os.path.join(ROOT, "include"), "-I", CSRC, "-Wall", "-Wno-unused-result"]
 
 
 def _compile(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + common_flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + common_flags(src) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

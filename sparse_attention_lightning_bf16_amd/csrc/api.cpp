@@ -150,6 +150,26 @@ int lix_indexer_scores_at(const void* q, const void* k, const float* w, const in
     return launch_status(lix::launch_sparse_scores(a));
 }
 
+int lix_indexer_backward(const void* q, const void* k, const float* w, const int32_t* indices,
+                         const float* grad_scores, int B, int S, int Skv, int H, int D, int compress_ratio,
+                         const int32_t* ks, const int32_t* ke, int topk, float* dq, float* dk, float* dw,
+                         hipStream_t stream) {
+    if (!q || !k || !w || !indices || !grad_scores || !dq || !dk || !dw) return LIX_ERR_NULL;
+    int st = check_dims_v4(B, S, Skv, H, D, compress_ratio, ks, ke);
+    if (st != LIX_OK) return st;
+    if (topk < 1) return LIX_ERR_SHAPE;
+    if (H > 64 || D <= 32 || D > 128) return LIX_ERR_UNSUPPORTED;
+    if (!fits(B, S, topk) || (long long)B * S * topk > (1LL << 38)) return LIX_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(w, 4) || !aligned(indices, 4) || !aligned(grad_scores, 4) ||
+        !aligned(dq, 4) || !aligned(dk, 16) || !aligned(dw, 4) || !aligned(ks, 4) || !aligned(ke, 4))
+        return LIX_ERR_UNSUPPORTED;
+    st = check_device({q, k, w, indices, grad_scores, dq, dk, dw, ks, ke});
+    if (st != LIX_OK) return st;
+    lix::BackwardArgs a{q, k, w, indices, grad_scores, B, S, Skv, H, D, compress_ratio, topk, ks, ke, dq, dk, dw,
+                        stream};
+    return launch_status(lix::launch_indexer_backward(a));
+}
+
 int lix_topk_bf16(const void* scores, int B, int L, int G, int topk, void* out_scores, int32_t* indices,
                   hipStream_t stream) {
     if (!scores || !out_scores || !indices) return LIX_ERR_NULL;

@@ -83,6 +83,23 @@ struct SparseArgs {
 
 hipError_t launch_v4_logits(const LogitsArgs& p);
 hipError_t launch_sparse_scores(const SparseArgs& p);
+
+// Gradients of the scores at given indices (dk is cleared, then accumulated).
+struct BackwardArgs {
+    const void* q;
+    const void* k;
+    const float* w;
+    const int32_t* indices;   // [B,S,topk]
+    const float* grad;        // [B,S,topk]
+    int B, S, Skv, H, D, ratio, topk;
+    const int32_t* ks;
+    const int32_t* ke;
+    float* dq;                // [S,B,H,D]
+    float* dk;                // [Skv,B,D]
+    float* dw;                // [S,B,H]
+    hipStream_t stream;
+};
+hipError_t launch_indexer_backward(const BackwardArgs& p);
 hipError_t launch_topk_rows(const TopkArgs& p);
 hipError_t launch_topk_bf16(const TopkBf16Args& p);
 hipError_t launch_fused_topk(const FusedArgs& p);

@@ -19,6 +19,7 @@
 // stage of the logits kernel (padded rows add exact zeros), so each score
 // equals the materialized logit bit for bit.
 #include "score_core.h"
+#include "gathered_block.h"
 #include "launch.h"
 
 namespace lix {
@@ -35,33 +36,6 @@ struct SparseTiling {
     static constexpr int NSTEP = DP / 16;               // MFMA k-steps over index_dim
     static constexpr int PER = 16 / NSTEP;              // epilogue elements per tile per k-step
     static constexpr int BLOCK_BYTES = NSTEP * 1024;    // one 32-key block in LDS
-};
-
-// LDS placement of one gathered 32-key block (NLOAD loads of 64 lanes x 16
-// bytes).  Load ld, lane L carries row segment p = RPI*ld + L/SEG, i.e. key
-// row p % 32, chunks SEG*(p/32) .. +SEG-1, and within the segment the chunk
-// (L % SEG) ^ swz(ld, L/SEG): consecutive lanes read one contiguous piece of
-// a key row.  The swizzle makes the 16 (and each 8) consecutive lanes of a
-// B-fragment read hit distinct 16-byte bank groups.
-template <int DP>
-struct BlockMap {
-    static constexpr int CPK = DP / 8;                  // 16-byte chunks per key row
-    static constexpr int SEG = CPK < 8 ? CPK : 8;       // chunks per row segment
-    static constexpr int RPI = 64 / SEG;                // row segments per load
-    static constexpr int NLOAD = 32 * CPK / 64;         // loads per block
-    static constexpr int NSTEP = DP / 16;
-    static constexpr int KR = SEG == 8 ? 4 : NSTEP;     // distinct per-lane read offsets
-    static_assert(SEG == 4 || SEG == 8, "row segments of 4 or 8 chunks");
-    __device__ static constexpr int swz(int ld, int m) {
-        return SEG == 8 ? (m ^ (ld & 1)) : (((m >> 1) ^ (m >> 3)) & (SEG - 1));
-    }
-    // Byte offset of this lane's B fragment for k-step st: key row lane % 32,
-    // chunk 2 st + lane / 32.  Equals frag_off(st % KR) + 4096 (st / KR).
-    __device__ static constexpr int frag_off(int st, int lane) {
-        const int r = lane & 31, c = 2 * st + (lane >> 5);
-        const int p = 32 * (c / SEG) + r, ld = p / RPI, m = p % RPI;
-        return 1024 * ld + 16 * (SEG * m + ((c % SEG) ^ swz(ld, m)));
-    }
 };
 
 template <int H, int DP>
@@ -118,22 +92,8 @@ __global__ __launch_bounds__(64, H >= 128 ? 1 : 2) void sparse_scores_kernel(InL
     auto load_idx = [&](int blk) { return ib[min(32 * blk + (lane & 31), topk - 1)]; };
     auto visible = [&](int idx, int blk) { return 32 * blk + (lane & 31) < topk && idx >= lo && idx < hi; };
     // Gather the 32 key rows of a block (invalid entries fetch key row 0).
-    // The row of each load's lane comes from the lane that holds that entry.
-    constexpr int NR = (32 / M::RPI) < M::NLOAD ? (32 / M::RPI) : M::NLOAD;
     auto gather = [&](uint8_t* buf, int idx, int blk) {
-        const int s = visible(idx, blk) ? idx : 0;
-        const int m = lane / M::SEG, cp = lane % M::SEG;
-        int rows[NR];
-#pragma unroll
-        for (int j = 0; j < NR; ++j) rows[j] = __shfl(s, (M::RPI * j + m) & 31);
-#pragma unroll
-        for (int ld = 0; ld < M::NLOAD; ++ld) {
-            const int p = M::RPI * ld + m;
-            const int d8 = min(M::SEG * (p >> 5) + (cp ^ M::swz(ld, m)), dlim);
-            const uint16_t* src = kb + (long)rows[ld % NR] * L.k_s + 8 * d8;
-            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
-                                             (lds_ptr_t)(buf + ld * kWave * 16), 16, 0, 0);
-        }
+        gather_block<DP>(buf, kb, L.k_s, dlim, visible(idx, blk) ? idx : 0, lane);
     };
     int fofs[M::KR];
 #pragma unroll

@@ -149,6 +149,64 @@ def indexer_scores_at(q, k, weights, compress_ratio, topk_indices, cu_seqlen_ks=
     return out
 
 
+def indexer_backward(q, k, weights, compress_ratio, topk_indices, grad_scores, cu_seqlen_ks=None,
+                     cu_seqlen_ke=None):
+    """lix_indexer_backward: gradients of indexer_scores_at's scores.  grad_scores fp32 [B,S,topk]
+    (the upstream gradient of the scores at topk_indices).  Returns fp32 (dq [S,B,H,D], dk [Skv,B,D],
+    dw [S,B,H]); entries outside the query's range contribute nothing."""
+    S, B, H, D, Skv = _v4_shapes(q, k, weights)
+    ks, ke = _ranges(cu_seqlen_ks, cu_seqlen_ke, S)
+    _need(topk_indices, "topk_indices", torch.int32, 3)
+    _need(grad_scores, "grad_scores", torch.float32, 3)
+    if topk_indices.shape[0] != B or topk_indices.shape[1] != S:
+        raise ValueError("topk_indices must be [B, S, topk]")
+    if grad_scores.shape != topk_indices.shape:
+        raise ValueError("grad_scores must have the shape of topk_indices")
+    if topk_indices.device != q.device or grad_scores.device != q.device:
+        raise ValueError("topk_indices and grad_scores must be on the device of q")
+    tk = topk_indices.shape[2]
+    dq = torch.empty(S, B, H, D, dtype=torch.float32, device=q.device)
+    dk = torch.empty(Skv, B, D, dtype=torch.float32, device=q.device)
+    dw = torch.empty(S, B, H, dtype=torch.float32, device=q.device)
+    st = _lib.load().lix_indexer_backward(q.data_ptr(), k.data_ptr(), weights.data_ptr(), topk_indices.data_ptr(),
+                                          grad_scores.data_ptr(), B, S, Skv, H, D, int(compress_ratio), _ptr(ks),
+                                          _ptr(ke), tk, dq.data_ptr(), dk.data_ptr(), dw.data_ptr(),
+                                          _stream(q.device))
+    _lib.check(st, "lix_indexer_backward")
+    return dq, dk, dw
+
+
+class V4IndexerFunction(torch.autograd.Function):
+    """Autograd Function of the indexer (page "...tilelang_indexer", class V4IndexerFunction).
+
+    forward(index_q, index_k, weights, compress_ratio, topk, topk_indices=None) returns
+    (scores, indices): the top-k of the fused kernel when topk_indices is None, else the scores at
+    topk_indices (returned unchanged as the indices).  backward(grad_scores, grad_indices) gives the
+    gradients of q, k and weights through the selected scores (lix_indexer_backward), in their dtypes;
+    the indices and the integer arguments get none.
+    """
+
+    @staticmethod
+    def forward(ctx, index_q, index_k, weights, compress_ratio, topk, topk_indices=None):
+        if topk_indices is None:
+            scores, indices = globals()["topk"](index_q, index_k, weights, compress_ratio, topk)
+        else:
+            indices = topk_indices
+            scores = indexer_scores_at(index_q, index_k, weights, compress_ratio, indices)
+        ctx.save_for_backward(index_q, index_k, weights, indices)
+        ctx.compress_ratio = int(compress_ratio)
+        ctx.mark_non_differentiable(indices)
+        return scores, indices
+
+    @staticmethod
+    def backward(ctx, grad_scores, grad_indices):
+        q, k, w, indices = ctx.saved_tensors
+        if grad_scores is None:
+            return None, None, None, None, None, None
+        dq, dk, dw = indexer_backward(q, k, w, ctx.compress_ratio, indices, grad_scores.contiguous().float())
+        return dq.to(q.dtype), dk.to(k.dtype), dw.to(w.dtype), None, None, None
+
+
 def indexer_scores_v41(queries, keys, weights, allowed):
     """lix_indexer_scores_v41: queries [B,L,H,D], keys [B,G,D], weights [B,L,H] (bf16),
     allowed [B,L,G] bool -> bf16 [B,L,G] (-inf where hidden)."""
@@ -188,8 +246,8 @@ def v4_lighting_indexer(index_q, index_k, weights, compress_ratio, topk, topk_in
     Without topk_indices: fused scoring + top-k, returns (scores, indices).
     With topk_indices [B,S,topk] int32: the scores at those indices, scored
     directly (lix_indexer_scores_at; equal bit for bit to gathering the
-    materialized logits), returns scores.
+    materialized logits), returns scores.  Both go through V4IndexerFunction,
+    so the scores carry gradients to index_q, index_k and weights.
     """
-    if topk_indices is None:
-        return globals()["topk"](index_q, index_k, weights, compress_ratio, topk)
-    return indexer_scores_at(index_q, index_k, weights, compress_ratio, topk_indices)
+    scores, indices = V4IndexerFunction.apply(index_q, index_k, weights, compress_ratio, topk, topk_indices)
+    return (scores, indices) if topk_indices is None else scores

@@ -12,5 +12,6 @@ from .workloads import (  # noqa: F401
     v41_inputs,
     v41_exact_inputs,
     document_starts,
+    upstream_gradient,
     bits,
 )

@@ -123,6 +123,12 @@ def v41_exact_inputs(batch, local_sequence, global_compressed, heads, index_dim,
                 weights=weights.contiguous(), allowed=allowed.contiguous())
 
 
+def upstream_gradient(batch, seqlen, topk, seed):
+    """grad_scores fp32 [B,S,topk] ~ N(0,1): the gradient a loss sends to the selected scores."""
+    g = _gen(seed)
+    return torch.randn(batch, seqlen, topk, generator=g, dtype=torch.float32)
+
+
 def bits(t):
     """CPU tensor -> NumPy array of its raw bits (bf16 -> uint16, fp32 -> float32)."""
     t = t.detach().cpu().contiguous()

@@ -122,17 +122,22 @@ def check_v41(gpu_bits, ora, lo, hi, where=""):
 BACKWARD_REL = 2.0 ** -8
 
 
+def check_backward_one(got, name, ora, bound, where=""):
+    """One gradient: got[name] float32 against the oracle's array and its (mag, amb)."""
+    g = np.asarray(got[name], dtype=np.float64)
+    assert g.shape == ora.shape, (name, g.shape, ora.shape)
+    mag, amb = bound
+    tol = BACKWARD_REL * mag + amb + 1e-6
+    err = np.abs(g - ora)
+    bad = ~(err <= tol)
+    if bad.any():
+        i = tuple(int(x) for x in np.argwhere(bad)[0])
+        raise AssertionError(f"{where} {name}: {int(bad.sum())} of {bad.size} outside tolerance; first at {i}: "
+                             f"got {g[i]!r} oracle {ora[i]!r} tol {tol[i]!r}")
+
+
 def check_backward(got, grads, bounds, where=""):
     """got: dict name -> float32 array for "dq", "dk", "dw"; grads: the
     oracle's (dq, dk, dw); bounds: its with_bounds dict."""
     for name, ora in zip(("dq", "dk", "dw"), grads):
-        g = np.asarray(got[name], dtype=np.float64)
-        assert g.shape == ora.shape, (name, g.shape, ora.shape)
-        mag, amb = bounds[name]
-        tol = BACKWARD_REL * mag + amb + 1e-6
-        err = np.abs(g - ora)
-        bad = ~(err <= tol)
-        if bad.any():
-            i = tuple(int(x) for x in np.argwhere(bad)[0])
-            raise AssertionError(f"{where} {name}: {int(bad.sum())} of {bad.size} outside tolerance; first at {i}: "
-                                 f"got {g[i]!r} oracle {ora[i]!r} tol {tol[i]!r}")
+        check_backward_one(got, name, ora, bounds[name], where)

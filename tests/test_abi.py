@@ -26,7 +26,8 @@ def test_library_exports_every_declared_function():
     lib = lx.load()
     names = declared_functions()
     assert set(names) == {"lix_status_string", "lix_version", "lix_indexer_logits", "lix_topk",
-                          "lix_topk_scores", "lix_indexer_scores_v41", "lix_indexer_scores_at", "lix_topk_bf16"}
+                          "lix_topk_scores", "lix_indexer_scores_v41", "lix_indexer_scores_at", "lix_topk_bf16",
+                          "lix_indexer_backward"}
     for name in names:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES
@@ -125,6 +126,24 @@ def scores_at_call(q=P, k=P, w=P, idx=P, B=1, S=8, Skv=4, H=64, D=128, c=4, ks=N
 def test_scores_at_validation(kw, code):
     # topk may exceed Skv here (given indices need not be distinct)
     assert scores_at_call(**kw) == code
+
+
+def backward_call(q=P, k=P, w=P, idx=P, g=P, B=1, S=8, Skv=4, H=64, D=128, c=4, ks=None, ke=None, topk=2, dq=P,
+                  dk=P, dw=P):
+    return lx.load().lix_indexer_backward(q, k, w, idx, g, B, S, Skv, H, D, c, ks, ke, topk, dq, dk, dw, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(w=None), NULL), (dict(idx=None), NULL), (dict(g=None), NULL),
+    (dict(dq=None), NULL), (dict(dk=None), NULL), (dict(dw=None), NULL),
+    (dict(B=0), SHAPE), (dict(S=0), SHAPE), (dict(Skv=-3), SHAPE), (dict(topk=0), SHAPE), (dict(c=0), SHAPE),
+    (dict(ke=P), SHAPE),
+    (dict(H=128), UNSUP), (dict(H=48), UNSUP), (dict(D=32), UNSUP), (dict(D=144), UNSUP), (dict(D=40), UNSUP),
+    (dict(q=P + 4), UNSUP), (dict(g=P + 2), UNSUP), (dict(dk=P + 4), UNSUP), (dict(dq=P + 2), UNSUP),
+    (dict(dw=P + 1), UNSUP), (dict(B=1 << 16, S=1 << 16, topk=1 << 16), UNSUP),
+])
+def test_backward_validation(kw, code):
+    assert backward_call(**kw) == code
 
 
 def topk_bf16_call(sc=P, B=1, L=8, G=16, topk=4, out=P, idx=P):

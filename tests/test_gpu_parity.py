@@ -313,6 +313,172 @@ def test_scores_at_32k_fused_selection_bitwise():
     assert torch.equal(sc, again)
 
 
+# ------------------------------------------------------------------ backward
+
+def backward_case(B, S, Skv, H, D, tk, seed, idx_mode="random"):
+    inp, nb = v4_case(B, S, Skv, H, D, seed=seed)
+    g = torch.Generator().manual_seed(seed + 1)
+    if idx_mode == "random":
+        # in-range keys, keys outside the causal range, negative and
+        # past-the-end indices, and duplicates
+        idx = torch.randint(-3, Skv + 3, (B, S, tk), generator=g, dtype=torch.int32)
+        idx[:, :, : min(tk, 4)] = idx[:, :, :1]
+    else:
+        idx = None
+    grad = synth.upstream_gradient(B, S, tk, seed + 2)
+    return inp, nb, idx, grad
+
+
+def check_backward_against_oracle(got, nb, idx, grad, ks, ke, where, rows=None):
+    grads, bounds = oracle.indexer_backward(nb["q"], nb["k"], nb["w"], idx, grad, ks, ke, with_bounds=True,
+                                            rows=rows)
+    if rows is not None:
+        got = {"dq": got["dq"][rows], "dw": got["dw"][rows]}
+        grads = (grads[0][rows], None, grads[2][rows])
+        bounds = {n: (bounds[n][0][rows], bounds[n][1][rows]) for n in ("dq", "dw")}
+        for name, i in (("dq", 0), ("dw", 2)):
+            sub = {name: got[name]}
+            checkers.check_backward_one(sub, name, grads[i], bounds[name], where)
+        return
+    checkers.check_backward(got, grads, bounds, where)
+
+
+@pytest.mark.parametrize("H,D,B,S,Skv,c,tk", [
+    (64, 128, 1, 256, 64, 4, 16),       # tiny workload shape
+    (64, 128, 2, 130, 100, 2, 70),      # ragged block of entries, B = 2
+    (64, 96, 1, 70, 90, 1, 45),         # index_dim padded inside the kernel
+    (64, 64, 1, 60, 50, 1, 33),
+    (32, 128, 2, 50, 80, 1, 64),
+    (16, 48, 1, 40, 30, 1, 20),
+    (8, 128, 1, 33, 70, 1, 96),
+    (1, 64, 2, 30, 40, 1, 9),
+    (64, 128, 1, 40, 35, 1, 1),          # one entry per query
+])
+def test_backward_matches_oracle(H, D, B, S, Skv, c, tk):
+    log(f"backward H={H} D={D} B={B} S={S} Skv={Skv} c={c} topk={tk}")
+    inp, nb, idx, grad = backward_case(B, S, Skv, H, D, tk, seed=300 + H + D + tk)
+    q, k, w = dev(inp["q"]), dev(inp["k"]), dev(inp["w"])
+    dq, dk, dw = lx.indexer_backward(q, k, w, c, dev(idx), dev(grad))
+    torch.cuda.synchronize()
+    ks, ke = ranges(S, Skv, c)
+    got = {"dq": dq.cpu().numpy(), "dk": dk.cpu().numpy(), "dw": dw.cpu().numpy()}
+    check_backward_against_oracle(got, nb, idx.numpy(), grad.numpy(), ks, ke, f"backward H={H} D={D}")
+
+
+def test_backward_given_ranges_and_repeat_runs():
+    B, S, Skv, H, D, tk = 2, 90, 70, 64, 128, 40
+    inp, nb, idx, grad = backward_case(B, S, Skv, H, D, tk, seed=330)
+    q, k, w = dev(inp["q"]), dev(inp["k"]), dev(inp["w"])
+    g = torch.Generator().manual_seed(331)
+    ks = torch.randint(0, 20, (S,), generator=g, dtype=torch.int32)
+    ke = ks + torch.randint(-5, 60, (S,), generator=g, dtype=torch.int32)
+    first = lx.indexer_backward(q, k, w, 1, dev(idx), dev(grad), dev(ks), dev(ke))
+    # A second call with other outputs in flight: dq and dw are the same bits;
+    # dk (float32 atomics) agrees within the tolerance.
+    second = lx.indexer_backward(q, k, w, 1, dev(idx), dev(grad), dev(ks), dev(ke))
+    assert torch.equal(first[0], second[0]) and torch.equal(first[2], second[2])
+    got = {"dq": first[0].cpu().numpy(), "dk": first[1].cpu().numpy(), "dw": first[2].cpu().numpy()}
+    check_backward_against_oracle(got, nb, idx.numpy(), grad.numpy(), ks.numpy().astype(np.int64),
+                                  ke.numpy().astype(np.int64), "backward given ranges")
+    got2 = {"dq": second[0].cpu().numpy(), "dk": second[1].cpu().numpy(), "dw": second[2].cpu().numpy()}
+    check_backward_against_oracle(got2, nb, idx.numpy(), grad.numpy(), ks.numpy().astype(np.int64),
+                                  ke.numpy().astype(np.int64), "backward given ranges, second call")
+
+
+def test_backward_invalid_entries_and_zero_gradient():
+    B, S, Skv, H, D, tk = 1, 40, 30, 64, 128, 32
+    inp, _, idx, grad = backward_case(B, S, Skv, H, D, tk, seed=340)
+    q, k, w = dev(inp["q"]), dev(inp["k"]), dev(inp["w"])
+    # every entry invalid: all gradients are exactly zero
+    bad = torch.full((B, S, tk), -1, dtype=torch.int32)
+    bad[:, :, ::2] = Skv + 5
+    for t in (bad, torch.full((B, S, tk), Skv - 1, dtype=torch.int32)):
+        dq, dk, dw = lx.indexer_backward(q, k, w, 4 if t is not bad else 1, dev(t), dev(grad))
+        if t is bad:
+            assert not dq.any() and not dk.any() and not dw.any()
+    # zero upstream gradient: all zero
+    dq, dk, dw = lx.indexer_backward(q, k, w, 1, dev(idx), torch.zeros(B, S, tk, device=DEV))
+    assert not dq.any() and not dk.any() and not dw.any()
+    # NaN gradients on invalid entries are ignored
+    g_nan = grad.clone()
+    valid = (idx >= 0) & (idx < torch.arange(S).view(1, S, 1) + 1) & (idx < Skv)
+    g_nan[~valid] = float("nan")
+    a = lx.indexer_backward(q, k, w, 1, dev(idx), dev(g_nan))
+    b = lx.indexer_backward(q, k, w, 1, dev(idx), dev(torch.where(valid, grad, torch.zeros_like(grad))))
+    assert torch.equal(a[0], b[0]) and torch.equal(a[2], b[2])
+    assert torch.isfinite(a[1]).all()
+
+
+def test_backward_4k_topk_selection():
+    # The 4K workload end to end: fused top-k, then the backward of its scores.
+    cfg = synth.WORKLOADS["4k"]
+    B, S, Skv, tk = cfg["batch"], cfg["seqlen"], cfg["seqlen_kv"], cfg["topk"]
+    inp, nb = v4_case(B, S, Skv, 64, 128, cfg["seed"])
+    q, k, w = dev(inp["q"]), dev(inp["k"]), dev(inp["w"])
+    log("4k: fused top-k, then the backward")
+    sc, ix = lx.topk(q, k, w, 4, tk)
+    grad = synth.upstream_gradient(B, S, tk, 345)
+    dq, dk, dw = lx.indexer_backward(q, k, w, 4, ix, dev(grad))
+    torch.cuda.synchronize()
+    ks, ke = ranges(S, Skv, 4)
+    got = {"dq": dq.cpu().numpy(), "dk": dk.cpu().numpy(), "dw": dw.cpu().numpy()}
+    log("4k: oracle backward")
+    check_backward_against_oracle(got, nb, ix.cpu().numpy(), grad.numpy(), ks, ke, "backward 4k")
+
+
+def test_backward_32k_sampled_rows_and_homogeneity():
+    # Full size, in the launch configuration the bench times.  dq and dw of a
+    # query depend on that query alone: sampled queries against the oracle.
+    # dk sums over every query: checked through Euler's identity for the
+    # positively homogeneous score (degree 1 in q, in k and in w):
+    # <dq, q> = <dk, k> = <dw, w> = sum over valid entries of g * score.
+    cfg = synth.WORKLOADS["32k"]
+    S, Skv, tk = cfg["seqlen"], cfg["seqlen_kv"], cfg["topk"]
+    inp, nb = v4_case(1, S, Skv, 64, 128, cfg["seed"])
+    q, k, w = dev(inp["q"]), dev(inp["k"]), dev(inp["w"])
+    log("32k: fused top-k, then the backward")
+    sc, ix = lx.topk(q, k, w, 4, tk)
+    grad = dev(synth.upstream_gradient(1, S, tk, 346))
+    dq, dk, dw = lx.indexer_backward(q, k, w, 4, ix, grad)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, S, 1024), [3, 4, 7, 8191, 8192, 8195, S - 1]]))
+    ks, ke = ranges(S, Skv, 4)
+    log(f"32k: oracle backward on {len(rows)} sampled queries")
+    check_backward_against_oracle({"dq": dq.cpu().numpy(), "dw": dw.cpu().numpy()}, nb, ix.cpu().numpy(),
+                                  grad.cpu().numpy(), ks, ke, "backward 32k", rows=rows)
+    valid = torch.isfinite(sc)
+    gs = torch.where(valid, grad, torch.zeros_like(grad))
+    total = (gs.double() * torch.where(valid, sc, torch.zeros_like(sc)).double()).sum().item()
+    # error scale: sum |g| * sum_h |w_h| relu(d_h), the scores taken with |w|
+    sc_abs = lx.indexer_scores_at(q, k, w.abs(), 4, ix)
+    scale = (gs.abs().double() * torch.where(valid, sc_abs, torch.zeros_like(sc_abs)).double()).sum().item()
+    for name, grad_t, x in (("dq", dq, q), ("dk", dk, k), ("dw", dw, w)):
+        inner = (grad_t.double() * x.double()).sum().item()
+        assert abs(inner - total) <= 2.0 ** -8 * scale + 1e-3, (name, inner, total, scale)
+
+
+def test_autograd_function_matches_the_backward_entry_point():
+    B, S, Skv, H, D, c, tk = 1, 64, 40, 64, 128, 2, 12
+    inp, _, idx, grad = backward_case(B, S, Skv, H, D, tk, seed=350)
+    q = dev(inp["q"]).requires_grad_()
+    k = dev(inp["k"]).requires_grad_()
+    w = dev(inp["w"]).requires_grad_()
+    scores = lx.v4_lighting_indexer(q, k, w, c, tk, dev(idx))
+    assert torch.equal(scores.detach(), lx.indexer_scores_at(q.detach(), k.detach(), w.detach(), c, dev(idx)))
+    scores.backward(dev(grad))
+    dq, dk, dw = lx.indexer_backward(q.detach(), k.detach(), w.detach(), c, dev(idx), dev(grad))
+    assert q.grad.dtype == torch.bfloat16 and k.grad.dtype == torch.bfloat16 and w.grad.dtype == torch.float32
+    assert torch.equal(q.grad, dq.to(torch.bfloat16)) and torch.equal(w.grad, dw)
+    assert torch.allclose(k.grad.float(), dk.to(torch.bfloat16).float(), rtol=2 ** -7, atol=1e-5)
+    # Without indices: the fused top-k's scores carry gradients the same way.
+    q.grad = k.grad = w.grad = None
+    sc2, ix2 = lx.v4_lighting_indexer(q, k, w, c, tk)
+    assert not ix2.requires_grad
+    sc2.backward(dev(grad))
+    dq2, _, dw2 = lx.indexer_backward(q.detach(), k.detach(), w.detach(), c, ix2, dev(grad))
+    assert torch.equal(q.grad, dq2.to(torch.bfloat16)) and torch.equal(w.grad, dw2)
+
+
 # ------------------------------------------------------------------ V4.1
 
 @pytest.mark.parametrize("H,D,B,L,G", [(64, 128, 1, 200, 60), (16, 32, 2, 70, 100), (128, 64, 1, 33, 20),

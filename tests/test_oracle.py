@@ -606,3 +606,18 @@ def test_backward_checker_accepts_bf16_rounding_and_rejects_planted_errors():
         checkers.check_backward({"dq": grads[0], "dk": grads[1][::-1].copy(), "dw": grads[2]}, grads, bounds)
     with pytest.raises(AssertionError):
         checkers.check_backward({"dq": grads[0], "dk": grads[1], "dw": grads[2] * 1.01}, grads, bounds)
+
+
+def test_backward_rows_subset_matches_full():
+    q, k, w, ks, ke, idx, g = _bw_case(80, S=7)
+    full = oracle.indexer_backward(q, k, w, idx, g, ks, ke)
+    rows = [1, 4, 6]
+    part = oracle.indexer_backward(q, k, w, idx, g, ks, ke, rows=rows)
+    np.testing.assert_array_equal(part[0][rows], full[0][rows])
+    np.testing.assert_array_equal(part[2][rows], full[2][rows])
+    others = [t for t in range(7) if t not in rows]
+    assert not part[0][others].any() and not part[2][others].any()
+    g_rows = np.zeros_like(g)
+    g_rows[:, rows] = g[:, rows]
+    np.testing.assert_allclose(part[1], oracle.indexer_backward(q, k, w, idx, g_rows, ks, ke)[1], rtol=1e-13,
+                               atol=1e-13)
