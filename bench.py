@@ -118,6 +118,16 @@ def extra_parts(dev, steps, warmup):
     out["copy_gbs"] = 2.0 * src.numel() * 4 / copy_ms / 1e6             # read + write
     flush = lambda: dst.fill_(0.0)                                        # 1 GiB write: evicts L2 and MALL
     del src
+    # achievable fp32 atomic-add rate: 2^21 rows of 128 floats added at random rows of a [8192, 128]
+    # table (the access pattern of the backward's dk adds), through torch's index_add_
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    rows = torch.randint(0, 8192, (1 << 21,), device=dev, generator=gen)
+    vals = torch.ones(1 << 21, 128, device=dev)
+    table = torch.zeros(8192, 128, device=dev)
+    atom_ms = time_each(lambda: table.index_add_(0, rows, vals), steps, warmup)
+    out["atomic_add_f32_per_s"] = float(vals.numel()) / (atom_ms * 1e-3)
+    del rows, vals, table
 
     cfg = synth.WORKLOADS["4k"]
     inp = synth.v4_inputs(**cfg)
@@ -316,6 +326,18 @@ def main():
             "logits_then_gather_ms": score_ms + gather_ms,
         })
         del logits
+
+        # backward of the selected scores (lix_indexer_backward) with a seeded upstream gradient
+        log("timing the backward")
+        g_up = synth.upstream_gradient(B, S, tk, 346).to(dev)
+        bw_ms, _ = time_loop(lambda: lx.indexer_backward(q, k, w, c, ix_f, g_up), max(3, args.steps // 4), 2)
+        parts.update({
+            "backward_ms": bw_ms,
+            # four GEMM passes over the selected entries: d twice (recompute), dq, dk
+            "backward_gemm_tflops": 4 * 2.0 * H * D * at_pairs / bw_ms / 1e9,
+            "backward_dk_atomic_adds_per_s": float(at_pairs) * D / (bw_ms * 1e-3),
+        })
+        del g_up
 
         log("timing the V4.1 workload")
         vcfg = synth.WORKLOADS["v41"]
