@@ -176,21 +176,37 @@ int lix_indexer_scores_at(const void* q, const void* k, const float* w, const in
  * Other entries contribute nothing (their score is the constant -inf,
  * whatever their grad_scores value); a key listed twice contributes twice;
  * the indices get no gradient.  The products take one bf16-rounded factor per
- * term (g for dq, w for dk) and accumulate in fp32; dk is summed over queries
- * with fp32 atomics, so its low bits vary from run to run.
+ * term (g for dq, g*w for dk) and accumulate in fp32.  dk is a sum over
+ * queries computed key-major (one partial per 256 keys and 512 queries, added
+ * with fp32 atomics), so its low bits may vary from run to run; dq and dw are
+ * deterministic.
  *
- *   q, k, w      as in lix_indexer_logits; heads H <= 64, 32 < D <= 128
+ *   q, k, w      as in lix_indexer_logits; heads H <= 64, 32 < D <= 128, Skv <= 32768
  *   indices      int32 [B, S, topk]  (any values)
  *   grad_scores  fp32  [B, S, topk]
  *   dq           fp32  [S, B, H, D]    out (every element written)
  *   dk           fp32  [Skv, B, D]     out (cleared by the call, 16-byte aligned)
  *   dw           fp32  [S, B, H]       out (every element written)
- * Other H or D: LIX_ERR_UNSUPPORTED.
+ *   workspace    device memory of at least lix_indexer_backward_workspace_bytes
+ *                bytes, 256-byte aligned, owned by the caller; its contents on
+ *                entry do not matter and on return are unspecified.  A smaller
+ *                workspace_bytes: LIX_ERR_SHAPE.
+ * Other H, D or Skv: LIX_ERR_UNSUPPORTED.
  */
 int lix_indexer_backward(const void* q, const void* k, const float* w, const int32_t* indices,
                          const float* grad_scores, int B, int S, int Skv, int H, int D,
                          int compress_ratio, const int32_t* ks, const int32_t* ke, int topk,
-                         float* dq, float* dk, float* dw, hipStream_t stream);
+                         float* dq, float* dk, float* dw, void* workspace, long long workspace_bytes,
+                         hipStream_t stream);
+
+/*
+ * lix_indexer_backward_workspace_bytes - device workspace lix_indexer_backward
+ * needs for these sizes: the dense upstream gradient [B, S, Skv] fp32 (written
+ * over each query's range only) plus q re-laid for the dk product
+ * (S*B*heads*index_dim*2 bytes, heads padded to 32 or 64, index_dim to 64 or
+ * 128).  -1 when the sizes are outside what lix_indexer_backward accepts.
+ */
+long long lix_indexer_backward_workspace_bytes(int B, int S, int Skv, int H, int D);
 
 /*
  * lix_indexer_scores_v41 - V4.1 BF16-rounded scores with a visibility mask.

@@ -17,6 +17,7 @@ LIX_FUSED_TOPK_MAX = 2048
 # Symbols exported by liblix.so, with their C signatures (include/lix.h).
 _P = ctypes.c_void_p
 _I = ctypes.c_int
+_LL = ctypes.c_longlong
 SIGNATURES = {
     "lix_status_string": (ctypes.c_char_p, [_I]),
     "lix_version": (_I, []),
@@ -26,7 +27,9 @@ SIGNATURES = {
     "lix_indexer_scores_v41": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
     "lix_indexer_scores_at": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P]),
     "lix_topk_bf16": (_I, [_P, _I, _I, _I, _I, _P, _P, _P]),
-    "lix_indexer_backward": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P, _P]),
+    "lix_indexer_backward": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P, _P, _LL,
+                                  _P]),
+    "lix_indexer_backward_workspace_bytes": (_LL, [_I, _I, _I, _I, _I]),
 }
 
 _lib = None

@@ -60,6 +60,18 @@ int check_device(std::initializer_list<const void*> ptrs) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? LIX_OK : LIX_ERR_LAUNCH; }
 
+// The backward's limits: heads <= 64, 32 < index_dim <= 128, a key row of G in LDS.
+int check_dims_backward(int B, int S, int Skv, int H, int D, int ratio, const int32_t* ks, const int32_t* ke,
+                        int topk) {
+    int st = check_dims_v4(B, S, Skv, H, D, ratio, ks, ke);
+    if (st != LIX_OK) return st;
+    if (topk < 1) return LIX_ERR_SHAPE;
+    if (H > 64 || D <= 32 || D > 128 || Skv > 32768) return LIX_ERR_UNSUPPORTED;
+    if (!fits(B, S, topk) || (long long)B * S * topk > (1LL << 38)) return LIX_ERR_UNSUPPORTED;
+    if ((long long)B * S > (1LL << 30) - 1) return LIX_ERR_UNSUPPORTED;
+    return LIX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -150,23 +162,27 @@ int lix_indexer_scores_at(const void* q, const void* k, const float* w, const in
     return launch_status(lix::launch_sparse_scores(a));
 }
 
+long long lix_indexer_backward_workspace_bytes(int B, int S, int Skv, int H, int D) {
+    if (check_dims_backward(B, S, Skv, H, D, 1, nullptr, nullptr, 1) != LIX_OK) return -1;
+    return lix::backward_workspace_bytes(B, S, Skv, H, D);
+}
+
 int lix_indexer_backward(const void* q, const void* k, const float* w, const int32_t* indices,
                          const float* grad_scores, int B, int S, int Skv, int H, int D, int compress_ratio,
                          const int32_t* ks, const int32_t* ke, int topk, float* dq, float* dk, float* dw,
-                         hipStream_t stream) {
-    if (!q || !k || !w || !indices || !grad_scores || !dq || !dk || !dw) return LIX_ERR_NULL;
-    int st = check_dims_v4(B, S, Skv, H, D, compress_ratio, ks, ke);
+                         void* workspace, long long workspace_bytes, hipStream_t stream) {
+    if (!q || !k || !w || !indices || !grad_scores || !dq || !dk || !dw || !workspace) return LIX_ERR_NULL;
+    int st = check_dims_backward(B, S, Skv, H, D, compress_ratio, ks, ke, topk);
     if (st != LIX_OK) return st;
-    if (topk < 1) return LIX_ERR_SHAPE;
-    if (H > 64 || D <= 32 || D > 128) return LIX_ERR_UNSUPPORTED;
-    if (!fits(B, S, topk) || (long long)B * S * topk > (1LL << 38)) return LIX_ERR_UNSUPPORTED;
+    if (workspace_bytes < lix::backward_workspace_bytes(B, S, Skv, H, D)) return LIX_ERR_SHAPE;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(w, 4) || !aligned(indices, 4) || !aligned(grad_scores, 4) ||
-        !aligned(dq, 4) || !aligned(dk, 16) || !aligned(dw, 4) || !aligned(ks, 4) || !aligned(ke, 4))
+        !aligned(dq, 4) || !aligned(dk, 16) || !aligned(dw, 4) || !aligned(ks, 4) || !aligned(ke, 4) ||
+        !aligned(workspace, 256))
         return LIX_ERR_UNSUPPORTED;
-    st = check_device({q, k, w, indices, grad_scores, dq, dk, dw, ks, ke});
+    st = check_device({q, k, w, indices, grad_scores, dq, dk, dw, ks, ke, workspace});
     if (st != LIX_OK) return st;
     lix::BackwardArgs a{q, k, w, indices, grad_scores, B, S, Skv, H, D, compress_ratio, topk, ks, ke, dq, dk, dw,
-                        stream};
+                        workspace, stream};
     return launch_status(lix::launch_indexer_backward(a));
 }
 

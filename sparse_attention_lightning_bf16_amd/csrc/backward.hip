@@ -12,22 +12,30 @@
 // Entries outside [ks, ke) (their score is the constant -inf) and the
 // indices themselves get no gradient.
 //
-// One wave per (b, t), walking the entries in blocks of 32 with the gathered
-// key blocks of the scores-at kernel.  Per block:
-//   * d is recomputed twice from the same register fragments: D = Q K^T
-//     (lanes are keys, accumulator rows heads) and D^T = K Q^T (lanes are
-//     heads, rows keys).
-//   * dw: g * relu(D^T) summed per lane (head) in registers.
-//   * dq += (m * g) K: the A operand is built from D^T's accumulators (the
-//     contraction index, the key, runs along each lane's rows), the B operand
-//     is the gathered block read key-major with 2-byte reads; dq stays in
-//     registers for the whole row and is scaled by w at the end.
-//   * the block's rows of dk = (m * w) Q, with the A operand built from D's
-//     accumulators and the B operand Q^T, staged in LDS once per query; each
-//     row is scaled by its g and added to dk with float32 atomics, issued
-//     before the dq product so that they complete while it runs.
-// The gradient products take bfloat16 operands (g rounded to bf16 for dq, w
-// for dk) and accumulate in float32; dw and the final scalings are float32.
+// dq and dw are sums over a query's own entries; dk is a sum over the queries
+// that selected a key.  Each is computed where its sum is local, so no output
+// element is accumulated with per-entry atomics:
+//
+//   1. grad_scatter_kernel: the dense upstream gradient G[b,t,s] (sum of g over
+//      the valid entries of (b,t) naming key s), written over each query's
+//      range [ks, ke) only (workspace).
+//   2. qt_fragments_kernel: q re-laid as the B fragments of the dk product
+//      (workspace), so a workgroup can move them into LDS with direct loads.
+//   3. backward_rows_kernel (query-major, one wave per query, the gathered
+//      32-key blocks of the scores-at kernel): d^T = K Q^T recomputed per block
+//      (lanes are heads, accumulator rows keys); dw += g relu(d^T) per lane;
+//      dq += (m g) K, whose A operand comes straight from d^T's accumulators and
+//      whose B operand is the gathered block read key-major; dq stays in
+//      registers for the whole row and is scaled by w at the end.
+//   4. dk_keys_kernel (key-major): a workgroup owns 256 keys (64 per wave, their
+//      K fragments in registers) and streams the queries that can see them:
+//      per query, q in A-fragment order and its dk fragments are moved into LDS
+//      (double-buffered, one barrier per query), D = Q K^T is recomputed (lanes
+//      are keys, rows heads), and dk += (m G w) Q accumulates in registers; the
+//      workgroup's partial is added to dk once at the end.
+//
+// The gradient products take bfloat16 operands (g rounded for dq, G w for dk)
+// and accumulate in float32; dw and the final scalings are float32.
 #include "score_core.h"
 #include "gathered_block.h"
 #include "launch.h"
@@ -37,6 +45,8 @@ namespace lix {
 namespace {
 
 constexpr int kBwWaitVmcnt0 = 0x0F70;     // s_waitcnt vmcnt(0), expcnt/lgkmcnt untouched
+constexpr int kKeysPerGroup = 256;        // keys per dk workgroup (64 per wave)
+constexpr int kQueryChunk = 512;          // queries per dk workgroup
 
 template <int H_, int DP_>
 struct BwTiling {
@@ -46,7 +56,8 @@ struct BwTiling {
     static constexpr int NSTEP = DP / 16;            // k-steps of the recompute over index_dim
     static constexpr int NDT = DP / 32;              // 32-column index_dim tiles of dq and dk
     static constexpr int NHS = 2 * NRT;              // 16-head k-steps of the dk product
-    static constexpr int QT_BYTES = NHS * NDT * 1024;
+    static constexpr int QS_BYTES = NRT * NSTEP * 1024;   // q of one query, A-fragment order
+    static constexpr int QT_BYTES = NHS * NDT * 1024;     // q of one query, dk B-fragment order
     static_assert(H <= 64 && (DP == 64 || DP == 128), "backward tiles cover H <= 64, index_dim 33..128");
 };
 
@@ -60,24 +71,94 @@ __device__ __forceinline__ uint32_t mask_pair(uint32_t v, float a_lo, float a_hi
     return v & m;
 }
 
+typedef __attribute__((address_space(1))) float gfloat;
+
 }  // namespace
 
+// ---------------------------------------------------------------- 1. G
+
+// One workgroup per (b, t): sum the valid entries' g per key in LDS (dynamic,
+// (hi - lo) floats), then write G[b,t,lo..hi).  Positions outside [lo, hi)
+// are not written; the dk kernel never reads them.
+__global__ __launch_bounds__(256) void grad_scatter_kernel(const int32_t* __restrict__ indices,
+                                                           const float* __restrict__ grad, int B, int S, int skv,
+                                                           int ratio, const int32_t* __restrict__ ks,
+                                                           const int32_t* __restrict__ ke, int topk,
+                                                           float* __restrict__ G) {
+    extern __shared__ float row[];
+    const int tid = threadIdx.x;
+    const int b = blockIdx.x % B, t = blockIdx.x / B;
+    int lo, hi;
+    key_range(ks, ke, t, S, skv, ratio, lo, hi);
+    const int n = hi - lo;
+    if (n <= 0) return;                                   // uniform: no barrier reached
+    for (int i = tid; i < n; i += 256) row[i] = 0.0f;
+    __syncthreads();
+    const int32_t* irow = indices + ((long)b * S + t) * topk;
+    const float* grow = grad + ((long)b * S + t) * topk;
+    for (int j = tid; j < topk; j += 256) {
+        const int s = irow[j];
+        if (s >= lo && s < hi) atomicAdd(&row[s - lo], grow[j]);
+    }
+    __syncthreads();
+    float* out = G + ((long)b * S + t) * skv + lo;
+    for (int i = tid; i < n; i += 256) out[i] = row[i];
+}
+
+// ---------------------------------------------------------------- 2. dk B fragments of q
+
+// Fragment (hs, dt) of query (t, b), lane l, holds q[head][32 dt + l%32] for the
+// 8 heads 32(hs/2) + 16(hs%2) + 8(jj/4) + 4(l/32) + jj%4, jj = 0..7: the order in
+// which the dk A operand walks a D accumulator's rows.  Padded heads and
+// index_dim entries >= D are zero.  One wave per (t, b); 1 KiB per fragment.
 template <int H, int DP>
-__global__ __launch_bounds__(64, 1) void indexer_backward_kernel(InLayout L, const float* __restrict__ w,
-                                                                const int32_t* __restrict__ indices,
-                                                                const float* __restrict__ grad, int B, int S,
-                                                                int skv, int ratio, const int32_t* __restrict__ ks,
-                                                                const int32_t* __restrict__ ke, int topk,
-                                                                float* __restrict__ dq, float* __restrict__ dk,
-                                                                float* __restrict__ dw) {
+__global__ __launch_bounds__(64) void qt_fragments_kernel(const uint16_t* __restrict__ q, int D,
+                                                          uint8_t* __restrict__ qt) {
+    using T = BwTiling<H, DP>;
+    const int lane = threadIdx.x, hf = lane >> 5, l32 = lane & 31;
+    const long tb = blockIdx.x;                           // t * B + b
+    const uint16_t* qrow = q + tb * H * D;
+    uint8_t* dst = qt + tb * T::QT_BYTES + 16 * lane;
+#pragma unroll
+    for (int hs = 0; hs < T::NHS; ++hs)
+#pragma unroll
+        for (int dt = 0; dt < T::NDT; ++dt) {
+            const int d = 32 * dt + l32;
+            uint32_t pk[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                uint32_t half[2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int jj = 2 * p + u;
+                    const int h = 32 * (hs >> 1) + 16 * (hs & 1) + 8 * (jj >> 2) + 4 * hf + (jj & 3);
+                    const uint16_t v = qrow[(long)min(h, H - 1) * D + min(d, D - 1)];
+                    half[u] = (h < H && d < D) ? v : 0u;
+                }
+                pk[p] = half[0] | (half[1] << 16);
+            }
+            *reinterpret_cast<u32x4*>(dst + (hs * T::NDT + dt) * 1024) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+        }
+}
+
+// ---------------------------------------------------------------- 3. dq, dw (query-major)
+
+// dq accumulators (H x DP fp32 per query) plus the q fragments need more than
+// 256 registers at 64 heads and index_dim 128: one wave per SIMD there.
+constexpr int rows_min_waves(int H, int DP) { return (H > 32 && DP > 64) ? 1 : 2; }
+
+template <int H, int DP>
+__global__ __launch_bounds__(64, rows_min_waves(H, DP)) void backward_rows_kernel(InLayout L, const float* __restrict__ w,
+                                                             const int32_t* __restrict__ indices,
+                                                             const float* __restrict__ grad, int B, int S, int skv,
+                                                             int ratio, const int32_t* __restrict__ ks,
+                                                             const int32_t* __restrict__ ke, int topk,
+                                                             float* __restrict__ dq, float* __restrict__ dw) {
     using T = BwTiling<H, DP>;
     using M = BlockMap<DP>;
     __shared__ __attribute__((aligned(16))) uint8_t buf0[M::BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t buf1[M::BYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t qt[T::QT_BYTES];
-    __shared__ float wsh[64];
     __shared__ __attribute__((aligned(16))) float stage_g[32];
-    __shared__ __attribute__((aligned(16))) int32_t stage_i[32];
 
     const int lane = threadIdx.x, hf = lane >> 5, l32 = lane & 31;
     const int b = blockIdx.x % B, t = blockIdx.x / B;
@@ -101,38 +182,6 @@ __global__ __launch_bounds__(64, 1) void indexer_backward_kernel(InLayout L, con
             a[r][st] = as_bf16x8(v);
         }
     }
-    // Q^T for the dk product: fragment (hs, dt), lane l holds q[head][32 dt + l%32]
-    // for the 8 heads 32(hs/2) + 16(hs%2) + 8(jj/4) + 4(l/32) + jj%4, jj = 0..7 (the
-    // order in which the dk A operand walks a D accumulator's rows).
-    {
-        const int sq = l32 >> 4, ho = l32 & 15;
-        const int jj = 4 * (ho >> 3) + (ho & 3), hw = (ho >> 2) & 1;
-#pragma unroll
-        for (int r = 0; r < T::NRT; ++r)
-#pragma unroll
-            for (int st = 0; st < T::NSTEP; ++st) {
-                const u32x4 v = __builtin_bit_cast(u32x4, a[r][st]);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int d = 16 * st + 8 * hf + e;
-                    const int off = ((2 * r + sq) * T::NDT + (d >> 5)) * 1024 + 16 * ((d & 31) + 32 * hw) + 2 * jj;
-                    *reinterpret_cast<uint16_t*>(qt + off) = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
-                }
-            }
-    }
-    // w of the query's heads in LDS (0 for padded heads); wpk[r][p] holds, as
-    // bf16, rows i = 2p, 2p+1 of tile r (heads 32r + c_row(i, hf)).
-    const float* wrow = w + ((long)t * B + b) * H;
-    {
-        const float v = wrow[min(lane, H - 1)];
-        wsh[lane] = lane < H ? v : 0.0f;
-    }
-    uint32_t wpk[T::NRT][8];
-#pragma unroll
-    for (int r = 0; r < T::NRT; ++r)
-#pragma unroll
-        for (int p = 0; p < 8; ++p)
-            wpk[r][p] = pack_bf16(wsh[32 * r + c_row(2 * p, hf)], wsh[32 * r + c_row(2 * p + 1, hf)]);
     // Key-major reads of a gathered block: element (key 16s + 8(jj/4) + 4hf + jj%4,
     // index_dim 32dt + lane%32) lies at kbase[dt%2][(jj%4) ^ (jj/4)]
     // + 1024(4(dt/2) + 2s + jj/4) + 128(jj%4) (the BlockMap placement, 8-chunk segments).
@@ -157,22 +206,6 @@ __global__ __launch_bounds__(64, 1) void indexer_backward_kernel(InLayout L, con
     auto load_idx = [&](int blk) { return irow[min(32 * blk + l32, topk - 1)]; };
     auto load_g = [&](int blk) { return grow[min(32 * blk + l32, topk - 1)]; };
     auto visible = [&](int idx, int blk) { return 32 * blk + l32 < topk && idx >= lo && idx < hi; };
-    // g and key row of the entries on this lane's accumulator rows (row i is
-    // entry 32 blk + c_row(i, hf)), through LDS: invalid entries get g = 0 and
-    // row -1.  One wave: its LDS operations run in order, no barrier needed.
-    auto rows_from_lanes = [&](float g_own, int idx_own, bool vis, float (&gv)[16], int (&iv)[16]) {
-        if (hf == 0) {
-            stage_g[l32] = vis ? g_own : 0.0f;
-            stage_i[l32] = vis ? idx_own : -1;
-        }
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const float4 gg = *reinterpret_cast<const float4*>(stage_g + 8 * q4 + 4 * hf);
-            const int4 ii = *reinterpret_cast<const int4*>(stage_i + 8 * q4 + 4 * hf);
-            gv[4 * q4 + 0] = gg.x; gv[4 * q4 + 1] = gg.y; gv[4 * q4 + 2] = gg.z; gv[4 * q4 + 3] = gg.w;
-            iv[4 * q4 + 0] = ii.x; iv[4 * q4 + 1] = ii.y; iv[4 * q4 + 2] = ii.z; iv[4 * q4 + 3] = ii.w;
-        }
-    };
 
     f32x16 dqacc[T::NRT][T::NDT];
 #pragma unroll
@@ -182,53 +215,28 @@ __global__ __launch_bounds__(64, 1) void indexer_backward_kernel(InLayout L, con
     float dwacc[T::NRT];
 #pragma unroll
     for (int r = 0; r < T::NRT; ++r) dwacc[r] = 0.0f;
-    typedef __attribute__((address_space(1))) float gfloat;
-    gfloat* const dkb = (gfloat*)dk + (long)b * D + l32;
 
-    auto compute = [&](const uint8_t* buf, float g_own, int idx_own, bool vis) {
-        f32x16 accd[T::NRT], acct[T::NRT];
+    auto compute = [&](const uint8_t* buf, float g_own, bool vis) {
+        f32x16 acct[T::NRT];
 #pragma unroll
-        for (int r = 0; r < T::NRT; ++r) { accd[r] = f32x16{}; acct[r] = f32x16{}; }
+        for (int r = 0; r < T::NRT; ++r) acct[r] = f32x16{};
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int st = 0; st < T::NSTEP; ++st) {
             const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(buf + fofs[st % M::KR] + 4096 * (st / M::KR)));
 #pragma unroll
-            for (int r = 0; r < T::NRT; ++r) {
-                accd[r] = mfma_32x32x16(a[r][st], kf, accd[r]);
-                acct[r] = mfma_32x32x16(kf, a[r][st], acct[r]);
-            }
+            for (int r = 0; r < T::NRT; ++r) acct[r] = mfma_32x32x16(kf, a[r][st], acct[r]);
         }
         __builtin_amdgcn_sched_barrier(0);
+        // g of the entries on this lane's accumulator rows (row i is entry
+        // 32 blk + c_row(i, hf)), through LDS; invalid entries get 0.  One
+        // wave: its LDS operations run in order, no barrier needed.
+        if (hf == 0) stage_g[l32] = vis ? g_own : 0.0f;
         float gv[16];
-        int iv[16];
-        rows_from_lanes(g_own, idx_own, vis, gv, iv);
-        // The block's rows of dk = (m * w) Q, scaled by each row's g, added to dk
-        // (first, so that the adds overlap the rest of the block).
 #pragma unroll
-        for (int dt = 0; dt < T::NDT; ++dt) {
-            f32x16 dkt = f32x16{};
-#pragma unroll
-            for (int r = 0; r < T::NRT; ++r)
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    u32x4 av;
-#pragma unroll
-                    for (int p = 0; p < 4; ++p)
-                        av[p] = mask_pair(wpk[r][4 * s + p], accd[r][8 * s + 2 * p], accd[r][8 * s + 2 * p + 1]);
-                    const bf16x8 qf = as_bf16x8(
-                        *reinterpret_cast<const u32x4*>(qt + ((2 * r + s) * T::NDT + dt) * 1024 + 16 * lane));
-                    dkt = mfma_32x32x16(as_bf16x8(av), qf, dkt);
-                }
-            // An invalid row adds +0.0 to key row 0: dk starts at +0.0 and never
-            // holds -0.0, so that add changes nothing (and needs no branch).
-            if (32 * dt + l32 < D) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    __hip_atomic_fetch_add(dkb + (long)max(iv[i], 0) * B * D + 32 * dt,
-                                           iv[i] >= 0 ? dkt[i] * gv[i] : 0.0f, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-            }
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 gg = *reinterpret_cast<const float4*>(stage_g + 8 * q4 + 4 * hf);
+            gv[4 * q4 + 0] = gg.x; gv[4 * q4 + 1] = gg.y; gv[4 * q4 + 2] = gg.z; gv[4 * q4 + 3] = gg.w;
         }
         // dw: lane = head 32r + lane%32, rows = keys c_row(i, hf).
 #pragma unroll
@@ -273,9 +281,9 @@ __global__ __launch_bounds__(64, 1) void indexer_backward_kernel(InLayout L, con
     };
 
     // Block order per step: wait for every outstanding vector-memory operation
-    // (this block's gather and g, issued one step earlier, and the previous
-    // step's dk adds), load the next block's g and the indices two blocks
-    // ahead, gather the next block into the other buffer, compute this block.  The explicit wait orders the LDS
+    // (this block's gather and g, issued one step earlier), load the next
+    // block's g and the indices two blocks ahead, gather the next block into
+    // the other buffer, compute this block.  The explicit wait orders the LDS
     // reads after the gather (one wave, no barrier).
     int idx_c = load_idx(0), idx_n = load_idx(1);
     float g_c = load_g(0);
@@ -290,12 +298,13 @@ __global__ __launch_bounds__(64, 1) void indexer_backward_kernel(InLayout L, con
         const int idx_nn = load_idx(blk + 2);
         const bool act_n = (blk + 1 < nb) && __ballot(visible(idx_n, blk + 1)) != 0ull;
         if (act_n) gather_block<DP>(other, kb, L.k_s, dlim, visible(idx_n, blk + 1) ? idx_n : 0, lane);
-        if (act_c) compute(cur, g_c, idx_c, visible(idx_c, blk));
+        if (act_c) compute(cur, g_c, visible(idx_c, blk));
         idx_c = idx_n; act_c = act_n; idx_n = idx_nn; g_c = g_n;
     }
 
     // dq = w * accumulated (m g) K: rows are heads 32r + c_row(i, hf), columns
     // index_dim 32 dt + lane%32.
+    const float* wrow = w + ((long)t * B + b) * H;
     float* dqrow = dq + ((long)t * B + b) * H * D;
 #pragma unroll
     for (int r = 0; r < T::NRT; ++r)
@@ -303,7 +312,7 @@ __global__ __launch_bounds__(64, 1) void indexer_backward_kernel(InLayout L, con
         for (int i = 0; i < 16; ++i) {
             const int h = 32 * r + c_row(i, hf);
             if (H < 32 && h >= H) continue;
-            const float wh = wsh[h];
+            const float wh = wrow[min(h, H - 1)];
 #pragma unroll
             for (int dt = 0; dt < T::NDT; ++dt) {
                 const int d = 32 * dt + l32;
@@ -319,17 +328,214 @@ __global__ __launch_bounds__(64, 1) void indexer_backward_kernel(InLayout L, con
     }
 }
 
+// ---------------------------------------------------------------- 4. dk (key-major)
+
+template <int H, int DP>
+__global__ __launch_bounds__(256, 1) void dk_keys_kernel(InLayout L, const float* __restrict__ w,
+                                                         const float* __restrict__ G,
+                                                         const uint8_t* __restrict__ qtf, int B, int S, int skv,
+                                                         int ratio, const int32_t* __restrict__ ks,
+                                                         const int32_t* __restrict__ ke, float* __restrict__ dk) {
+    using T = BwTiling<H, DP>;
+    __shared__ __attribute__((aligned(16))) uint8_t qs0[T::QS_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t qs1[T::QS_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t qt0[T::QT_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t qt1[T::QT_BYTES];
+    __shared__ __attribute__((aligned(16))) float ws0[64];
+    __shared__ __attribute__((aligned(16))) float ws1[64];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
+    const int b = blockIdx.y;
+    const int s_wave = blockIdx.x * kKeysPerGroup + 64 * wave;      // this wave's first key
+    const int D = L.D;
+    const int dlim = (D >> 3) - 1;
+
+    // Queries of this workgroup; with causal ranges no query before
+    // ratio * (first key) - 1 sees any of its keys.
+    int t0 = blockIdx.z * kQueryChunk;
+    const int t1 = min(S, t0 + kQueryChunk);
+    if (ks == nullptr) t0 = (int)max((long)t0, (long)ratio * blockIdx.x * kKeysPerGroup - 1);
+    if (t0 >= t1) return;                                  // uniform: before any barrier
+
+    // K fragments of the wave's 64 keys (B operand of D = Q K^T): kf[kc][st] =
+    // k[s_wave + 32kc + lane%32][16 st + 8 hf .. +7]; keys >= skv and index_dim
+    // entries >= D are zero.
+    bf16x8 kf[2][T::NSTEP];
+    const uint16_t* kb = L.k + (long)b * L.k_b;
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+        const int s = s_wave + 32 * kc + l32;
+        const uint16_t* base = kb + (long)min(s, skv - 1) * L.k_s;
+#pragma unroll
+        for (int st = 0; st < T::NSTEP; ++st) {
+            const int d0 = 16 * st + 8 * hf;
+            u32x4 v = *reinterpret_cast<const u32x4*>(base + min(d0, D - 8));
+            if (!(s < skv && d0 < D)) v = u32x4{0u, 0u, 0u, 0u};
+            kf[kc][st] = as_bf16x8(v);
+        }
+    }
+
+    // Stage query t into (qs, qt, ws): q in A-fragment order (block (r, st),
+    // lane l = head 32r + l%32, chunk 2st + l/32; padded heads repeat head H-1
+    // and padded chunks the last real one: they meet zero weights or zero K
+    // entries), the query's dk fragments, and its weights.
+    auto stage = [&](int t, uint8_t* qs, uint8_t* qt, float* ws) {
+        const uint16_t* qrow = L.q + (long)t * L.q_t + (long)b * L.q_b;
+#pragma unroll
+        for (int blk = wave; blk < T::NRT * T::NSTEP; blk += 4) {
+            const int r = blk / T::NSTEP, st = blk % T::NSTEP;
+            const int h = min(32 * r + l32, H - 1), d8 = min(2 * st + hf, dlim);
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(qrow + (long)h * D + 8 * d8),
+                                             (lds_ptr_t)(qs + blk * 1024), 16, 0, 0);
+        }
+        const uint8_t* src = qtf + ((long)t * B + b) * T::QT_BYTES + 16 * lane;
+#pragma unroll
+        for (int blk = wave; blk < T::NHS * T::NDT; blk += 4)
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + blk * 1024),
+                                             (lds_ptr_t)(qt + blk * 1024), 16, 0, 0);
+        if (wave == 0)
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(w + ((long)t * B + b) * H + min(lane, H - 1)),
+                                             (lds_ptr_t)ws, 4, 0, 0);
+    };
+    // G of this lane's keys for query t, 0 outside the query's range.
+    auto load_g = [&](int t, float (&g)[2]) {
+        int lo, hi;
+        key_range(ks, ke, t, S, skv, ratio, lo, hi);
+        const float* grow = G + ((long)b * S + t) * skv;
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+            const int s = s_wave + 32 * kc + l32;
+            const float v = grow[hi > lo ? min(max(s, lo), hi - 1) : 0];      // a written position
+            g[kc] = (s >= lo && s < hi) ? v : 0.0f;
+        }
+    };
+
+    f32x16 dkacc[2][T::NDT];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int dt = 0; dt < T::NDT; ++dt) dkacc[kc][dt] = f32x16{};
+
+    auto compute = [&](const uint8_t* qs, const uint8_t* qt, const float* ws, const float (&g)[2]) {
+        if (__ballot(g[0] != 0.0f || g[1] != 0.0f) == 0ull) return;     // no selected key in this wave
+        // D = Q K^T: lanes are keys (32kc + lane%32), rows heads 32r + c_row(i, hf).
+        f32x16 accd[T::NRT][2];
+#pragma unroll
+        for (int r = 0; r < T::NRT; ++r) { accd[r][0] = f32x16{}; accd[r][1] = f32x16{}; }
+#pragma unroll
+        for (int st = 0; st < T::NSTEP; ++st)
+#pragma unroll
+            for (int r = 0; r < T::NRT; ++r) {
+                const bf16x8 qa = as_bf16x8(*reinterpret_cast<const u32x4*>(qs + (r * T::NSTEP + st) * 1024 + 16 * lane));
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc) accd[r][kc] = mfma_32x32x16(qa, kf[kc][st], accd[r][kc]);
+            }
+        // w of the heads on the accumulator rows (4 consecutive heads per group).
+        float wv[T::NRT][16];
+#pragma unroll
+        for (int r = 0; r < T::NRT; ++r)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const float4 ww = *reinterpret_cast<const float4*>(ws + 32 * r + c_row(4 * q4, hf));
+                const float wx[4] = {ww.x, ww.y, ww.z, ww.w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) wv[r][4 * q4 + u] = (32 * r + c_row(4 * q4 + u, hf) < H) ? wx[u] : 0.0f;
+            }
+        // dk += (m G w) Q: A from D's accumulators (contraction over heads), B the
+        // query's dk fragments.
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+            for (int r = 0; r < T::NRT; ++r)
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    u32x4 av;
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        const int i0 = 8 * s + 2 * p;
+                        av[p] = mask_pair(pack_bf16(g[kc] * wv[r][i0], g[kc] * wv[r][i0 + 1]), accd[r][kc][i0],
+                                          accd[r][kc][i0 + 1]);
+                    }
+                    const bf16x8 af = as_bf16x8(av);
+#pragma unroll
+                    for (int dt = 0; dt < T::NDT; ++dt) {
+                        const bf16x8 qf = as_bf16x8(
+                            *reinterpret_cast<const u32x4*>(qt + ((2 * r + s) * T::NDT + dt) * 1024 + 16 * lane));
+                        dkacc[kc][dt] = mfma_32x32x16(af, qf, dkacc[kc][dt]);
+                    }
+                }
+    };
+
+    // One barrier per query: it waits for the staging of the query computed
+    // next (issued a query earlier) and for every wave to be done with the
+    // buffers the following staging overwrites.
+    float g_c[2], g_n[2] = {0.0f, 0.0f};
+    stage(t0, qs0, qt0, ws0);
+    load_g(t0, g_c);
+    __syncthreads();
+    for (int t = t0; t < t1; ++t) {
+        const bool odd = ((t - t0) & 1) != 0;
+        if (t + 1 < t1) {
+            stage(t + 1, odd ? qs0 : qs1, odd ? qt0 : qt1, odd ? ws0 : ws1);
+            load_g(t + 1, g_n);
+        }
+        compute(odd ? qs1 : qs0, odd ? qt1 : qt0, odd ? ws1 : ws0, g_c);
+        g_c[0] = g_n[0]; g_c[1] = g_n[1];
+        __syncthreads();
+    }
+
+    // dk rows of the wave's keys: key s_wave + 32kc + c_row(i, hf), index_dim
+    // 32 dt + lane%32; added to dk (other query chunks add theirs).
+    gfloat* dkb = (gfloat*)dk + (long)b * D + l32;
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int s = s_wave + 32 * kc + c_row(i, hf);
+            if (s >= skv) continue;
+#pragma unroll
+            for (int dt = 0; dt < T::NDT; ++dt)
+                if (32 * dt + l32 < D)
+                    __hip_atomic_fetch_add(dkb + (long)s * B * D + 32 * dt, dkacc[kc][dt][i], __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+        }
+}
+
+// ---------------------------------------------------------------- launch
+
 __global__ void zero_f32_kernel(float* __restrict__ p, long n4) {
     for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (long)gridDim.x * blockDim.x)
         reinterpret_cast<float4*>(p)[i] = float4{0.0f, 0.0f, 0.0f, 0.0f};
+}
+
+static long g_bytes(int B, int S, int Skv) { return ((long)B * S * Skv * 4 + 255) & ~255L; }
+
+long backward_workspace_bytes(int B, int S, int Skv, int H, int D) {
+    const int nrt = H > 32 ? 2 : 1, ndt = padded_dim(D) / 32;
+    return g_bytes(B, S, Skv) + (long)S * B * (2 * nrt) * ndt * 1024;
 }
 
 template <int H, int DP>
 static hipError_t launch_backward_t(const BackwardArgs& p) {
     InLayout L{static_cast<const uint16_t*>(p.q), (long)p.B * H * p.D, (long)H * p.D,
                static_cast<const uint16_t*>(p.k), (long)p.B * p.D, (long)p.D, p.D};
-    hipLaunchKernelGGL((indexer_backward_kernel<H, DP>), dim3((unsigned)((long)p.B * p.S)), dim3(kWave), 0, p.stream,
-                       L, p.w, p.indices, p.grad, p.B, p.S, p.Skv, p.ratio, p.ks, p.ke, p.topk, p.dq, p.dk, p.dw);
+    float* G = reinterpret_cast<float*>(p.workspace);
+    uint8_t* qtf = reinterpret_cast<uint8_t*>(p.workspace) + g_bytes(p.B, p.S, p.Skv);
+    const unsigned rows = (unsigned)((long)p.B * p.S);
+    const size_t row_bytes = (size_t)p.Skv * 4;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(grad_scatter_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)row_bytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(grad_scatter_kernel, dim3(rows), dim3(256), row_bytes, p.stream, p.indices, p.grad,
+                       p.B, p.S, p.Skv, p.ratio, p.ks, p.ke, p.topk, G);
+    hipLaunchKernelGGL((qt_fragments_kernel<H, DP>), dim3(rows), dim3(kWave), 0, p.stream,
+                       static_cast<const uint16_t*>(p.q), p.D, qtf);
+    hipLaunchKernelGGL((backward_rows_kernel<H, DP>), dim3(rows), dim3(kWave), 0, p.stream, L, p.w, p.indices,
+                       p.grad, p.B, p.S, p.Skv, p.ratio, p.ks, p.ke, p.topk, p.dq, p.dw);
+    const dim3 grid((unsigned)((p.Skv + kKeysPerGroup - 1) / kKeysPerGroup), (unsigned)p.B,
+                    (unsigned)((p.S + kQueryChunk - 1) / kQueryChunk));
+    hipLaunchKernelGGL((dk_keys_kernel<H, DP>), grid, dim3(256), 0, p.stream, L, p.w, G, qtf, p.B, p.S, p.Skv,
+                       p.ratio, p.ks, p.ke, p.dk);
     return hipGetLastError();
 }
 
@@ -343,7 +549,8 @@ static hipError_t dispatch_dp_backward(const BackwardArgs& p) {
 }
 
 hipError_t launch_indexer_backward(const BackwardArgs& p) {
-    // dk accumulates: clear it first (a fill kernel, so the sequence can be captured).
+    // dk is a sum of workgroup partials: clear it first (a fill kernel, so the
+    // sequence can be captured).
     const long n4 = (long)p.Skv * p.B * p.D / 4;
     const long blocks = (n4 + 255) / 256;
     hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, p.stream,

@@ -97,8 +97,10 @@ struct BackwardArgs {
     float* dq;                // [S,B,H,D]
     float* dk;                // [Skv,B,D]
     float* dw;                // [S,B,H]
+    void* workspace;          // backward_workspace_bytes(B, S, Skv, H, D) bytes
     hipStream_t stream;
 };
+long backward_workspace_bytes(int B, int S, int Skv, int H, int D);
 hipError_t launch_indexer_backward(const BackwardArgs& p);
 hipError_t launch_topk_rows(const TopkArgs& p);
 hipError_t launch_topk_bf16(const TopkBf16Args& p);

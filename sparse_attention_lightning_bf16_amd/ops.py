@@ -153,7 +153,8 @@ def indexer_backward(q, k, weights, compress_ratio, topk_indices, grad_scores, c
                      cu_seqlen_ke=None):
     """lix_indexer_backward: gradients of indexer_scores_at's scores.  grad_scores fp32 [B,S,topk]
     (the upstream gradient of the scores at topk_indices).  Returns fp32 (dq [S,B,H,D], dk [Skv,B,D],
-    dw [S,B,H]); entries outside the query's range contribute nothing."""
+    dw [S,B,H]); entries outside the query's range contribute nothing.  The workspace the call needs
+    (lix_indexer_backward_workspace_bytes) is allocated here with torch."""
     S, B, H, D, Skv = _v4_shapes(q, k, weights)
     ks, ke = _ranges(cu_seqlen_ks, cu_seqlen_ke, S)
     _need(topk_indices, "topk_indices", torch.int32, 3)
@@ -165,13 +166,18 @@ def indexer_backward(q, k, weights, compress_ratio, topk_indices, grad_scores, c
     if topk_indices.device != q.device or grad_scores.device != q.device:
         raise ValueError("topk_indices and grad_scores must be on the device of q")
     tk = topk_indices.shape[2]
+    lib = _lib.load()
+    ws_bytes = lib.lix_indexer_backward_workspace_bytes(B, S, Skv, H, D)
+    if ws_bytes < 0:
+        raise _lib.LixError(-3, "lix_indexer_backward_workspace_bytes")
     dq = torch.empty(S, B, H, D, dtype=torch.float32, device=q.device)
     dk = torch.empty(Skv, B, D, dtype=torch.float32, device=q.device)
     dw = torch.empty(S, B, H, dtype=torch.float32, device=q.device)
-    st = _lib.load().lix_indexer_backward(q.data_ptr(), k.data_ptr(), weights.data_ptr(), topk_indices.data_ptr(),
-                                          grad_scores.data_ptr(), B, S, Skv, H, D, int(compress_ratio), _ptr(ks),
-                                          _ptr(ke), tk, dq.data_ptr(), dk.data_ptr(), dw.data_ptr(),
-                                          _stream(q.device))
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    st = lib.lix_indexer_backward(q.data_ptr(), k.data_ptr(), weights.data_ptr(), topk_indices.data_ptr(),
+                                  grad_scores.data_ptr(), B, S, Skv, H, D, int(compress_ratio), _ptr(ks), _ptr(ke), tk,
+                                  dq.data_ptr(), dk.data_ptr(), dw.data_ptr(), ws.data_ptr(), ws_bytes,
+                                  _stream(q.device))
     _lib.check(st, "lix_indexer_backward")
     return dq, dk, dw
 

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_function():
     names = declared_functions()
     assert set(names) == {"lix_status_string", "lix_version", "lix_indexer_logits", "lix_topk",
                           "lix_topk_scores", "lix_indexer_scores_v41", "lix_indexer_scores_at", "lix_topk_bf16",
-                          "lix_indexer_backward"}
+                          "lix_indexer_backward", "lix_indexer_backward_workspace_bytes"}
     for name in names:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES
@@ -129,8 +129,9 @@ def test_scores_at_validation(kw, code):
 
 
 def backward_call(q=P, k=P, w=P, idx=P, g=P, B=1, S=8, Skv=4, H=64, D=128, c=4, ks=None, ke=None, topk=2, dq=P,
-                  dk=P, dw=P):
-    return lx.load().lix_indexer_backward(q, k, w, idx, g, B, S, Skv, H, D, c, ks, ke, topk, dq, dk, dw, None)
+                  dk=P, dw=P, ws=P, ws_bytes=1 << 40):
+    return lx.load().lix_indexer_backward(q, k, w, idx, g, B, S, Skv, H, D, c, ks, ke, topk, dq, dk, dw, ws, ws_bytes,
+                                          None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -141,9 +142,21 @@ def backward_call(q=P, k=P, w=P, idx=P, g=P, B=1, S=8, Skv=4, H=64, D=128, c=4, 
     (dict(H=128), UNSUP), (dict(H=48), UNSUP), (dict(D=32), UNSUP), (dict(D=144), UNSUP), (dict(D=40), UNSUP),
     (dict(q=P + 4), UNSUP), (dict(g=P + 2), UNSUP), (dict(dk=P + 4), UNSUP), (dict(dq=P + 2), UNSUP),
     (dict(dw=P + 1), UNSUP), (dict(B=1 << 16, S=1 << 16, topk=1 << 16), UNSUP),
+    (dict(ws=None), NULL), (dict(ws_bytes=1000), SHAPE), (dict(ws=P + 16), UNSUP), (dict(Skv=32769), UNSUP),
 ])
 def test_backward_validation(kw, code):
     assert backward_call(**kw) == code
+
+
+def test_backward_workspace_bytes():
+    lib = lx.load()
+    # dense upstream gradient (rounded up to 256 bytes) + q re-laid for the dk product
+    assert lib.lix_indexer_backward_workspace_bytes(1, 8, 4, 64, 128) == 256 + 8 * 64 * 128 * 2
+    g_bytes = (2 * 100 * 30 * 4 + 255) // 256 * 256
+    assert lib.lix_indexer_backward_workspace_bytes(2, 100, 30, 16, 48) == g_bytes + 100 * 2 * 32 * 64 * 2
+    assert lib.lix_indexer_backward_workspace_bytes(1, 32768, 8192, 64, 128) == (1 << 30) + (1 << 29)
+    assert lib.lix_indexer_backward_workspace_bytes(1, 8, 4, 128, 128) == -1
+    assert lib.lix_indexer_backward_workspace_bytes(1, 8, 40000, 64, 128) == -1
 
 
 def topk_bf16_call(sc=P, B=1, L=8, G=16, topk=4, out=P, idx=P):
