@@ -175,8 +175,9 @@ int lix_indexer_scores_at(const void* q, const void* k, const float* w, const in
  *     dk[i,b,:]   += g * sum_h w[t,b,h] * m_h * q[t,b,h,:]
  * Other entries contribute nothing (their score is the constant -inf,
  * whatever their grad_scores value); a key listed twice contributes twice;
- * the indices get no gradient.  The products take one bf16-rounded factor per
- * term (g for dq, g*w for dk) and accumulate in fp32.  dk is a sum over
+ * the indices get no gradient.  The products take bf16 operands (g rounded
+ * for dq; the summed g of a (query, key) pair and w*q rounded for dk) and
+ * accumulate in fp32.  dk is a sum over
  * queries computed key-major (one partial per 256 keys and 512 queries, added
  * with fp32 atomics), so its low bits may vary from run to run; dq and dw are
  * deterministic.

@@ -19,8 +19,9 @@
 //   1. grad_scatter_kernel: the dense upstream gradient G[b,t,s] (sum of g over
 //      the valid entries of (b,t) naming key s), written over each query's
 //      range [ks, ke) only (workspace).
-//   2. qt_fragments_kernel: q re-laid as the B fragments of the dk product
-//      (workspace), so a workgroup can move them into LDS with direct loads.
+//   2. qt_fragments_kernel: w_h q_h (bf16) laid out as the B fragments of the
+//      dk product (workspace), so a workgroup can move them into LDS with
+//      direct loads.
 //   3. backward_rows_kernel (query-major, one wave per query, the gathered
 //      32-key blocks of the scores-at kernel): d^T = K Q^T recomputed per block
 //      (lanes are heads, accumulator rows keys); dw += g relu(d^T) per lane;
@@ -31,11 +32,12 @@
 //      K fragments in registers) and streams the queries that can see them:
 //      per query, q in A-fragment order and its dk fragments are moved into LDS
 //      (double-buffered, one barrier per query), D = Q K^T is recomputed (lanes
-//      are keys, rows heads), and dk += (m G w) Q accumulates in registers; the
-//      workgroup's partial is added to dk once at the end.
+//      are keys, rows heads), and dk += (m G) (w Q) accumulates in registers;
+//      the workgroup's partial is added to dk once at the end.
 //
-// The gradient products take bfloat16 operands (g rounded for dq, G w for dk)
-// and accumulate in float32; dw and the final scalings are float32.
+// The gradient products take one bfloat16-rounded factor per term (g for dq,
+// G and w q for dk) and accumulate in float32; dw and the final scalings are
+// float32.
 #include "score_core.h"
 #include "gathered_block.h"
 #include "launch.h"
@@ -107,17 +109,18 @@ __global__ __launch_bounds__(256) void grad_scatter_kernel(const int32_t* __rest
 
 // ---------------------------------------------------------------- 2. dk B fragments of q
 
-// Fragment (hs, dt) of query (t, b), lane l, holds q[head][32 dt + l%32] for the
-// 8 heads 32(hs/2) + 16(hs%2) + 8(jj/4) + 4(l/32) + jj%4, jj = 0..7: the order in
-// which the dk A operand walks a D accumulator's rows.  Padded heads and
-// index_dim entries >= D are zero.  One wave per (t, b); 1 KiB per fragment.
+// Fragment (hs, dt) of query (t, b), lane l, holds bf16(w[head] q[head][32 dt + l%32])
+// for the 8 heads 32(hs/2) + 16(hs%2) + 8(jj/4) + 4(l/32) + jj%4, jj = 0..7: the
+// order in which the dk A operand walks a D accumulator's rows.  Padded heads
+// and index_dim entries >= D are zero.  One wave per (t, b); 1 KiB per fragment.
 template <int H, int DP>
-__global__ __launch_bounds__(64) void qt_fragments_kernel(const uint16_t* __restrict__ q, int D,
-                                                          uint8_t* __restrict__ qt) {
+__global__ __launch_bounds__(64) void qt_fragments_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
+                                                          int D, uint8_t* __restrict__ qt) {
     using T = BwTiling<H, DP>;
     const int lane = threadIdx.x, hf = lane >> 5, l32 = lane & 31;
     const long tb = blockIdx.x;                           // t * B + b
     const uint16_t* qrow = q + tb * H * D;
+    const float* wrow = w + tb * H;
     uint8_t* dst = qt + tb * T::QT_BYTES + 16 * lane;
 #pragma unroll
     for (int hs = 0; hs < T::NHS; ++hs)
@@ -133,7 +136,8 @@ __global__ __launch_bounds__(64) void qt_fragments_kernel(const uint16_t* __rest
                     const int jj = 2 * p + u;
                     const int h = 32 * (hs >> 1) + 16 * (hs & 1) + 8 * (jj >> 2) + 4 * hf + (jj & 3);
                     const uint16_t v = qrow[(long)min(h, H - 1) * D + min(d, D - 1)];
-                    half[u] = (h < H && d < D) ? v : 0u;
+                    const float wq = wrow[min(h, H - 1)] * bf16_to_f32(v);
+                    half[u] = (h < H && d < D) ? (uint32_t)bf16_bits(wq) : 0u;
                 }
                 pk[p] = half[0] | (half[1] << 16);
             }
@@ -330,6 +334,10 @@ __global__ __launch_bounds__(64, rows_min_waves(H, DP)) void backward_rows_kerne
 
 // ---------------------------------------------------------------- 4. dk (key-major)
 
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left at their maxima).
+constexpr int wait_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 template <int H, int DP>
 __global__ __launch_bounds__(256, 1) void dk_keys_kernel(InLayout L, const float* __restrict__ w,
                                                          const float* __restrict__ G,
@@ -337,16 +345,24 @@ __global__ __launch_bounds__(256, 1) void dk_keys_kernel(InLayout L, const float
                                                          int ratio, const int32_t* __restrict__ ks,
                                                          const int32_t* __restrict__ ke, float* __restrict__ dk) {
     using T = BwTiling<H, DP>;
-    __shared__ __attribute__((aligned(16))) uint8_t qs0[T::QS_BYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t qs1[T::QS_BYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t qt0[T::QT_BYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t qt1[T::QT_BYTES];
-    __shared__ __attribute__((aligned(16))) float ws0[64];
-    __shared__ __attribute__((aligned(16))) float ws1[64];
+    // Three stages, each: q in A-fragment order, the query's dk fragments
+    // (w q) and G at the workgroup's 256 keys.
+    constexpr int QS = 0, QT = T::QS_BYTES, GS = QT + T::QT_BYTES;
+    constexpr int STAGE = GS + 4 * kKeysPerGroup;
+    // Three separate arrays, used in a fixed rotation, so the compiler can tell
+    // that loads into one never alias reads of another.
+    __shared__ __attribute__((aligned(16))) uint8_t lds0[STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t lds1[STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t lds2[STAGE];
+    // Vector-memory operations one wave issues per stage: its share of the q
+    // and fragment blocks and one G load.
+    constexpr int PER_WAVE = (T::NRT * T::NSTEP + T::NHS * T::NDT) / 4 + 1;
+    static_assert((T::NRT * T::NSTEP) % 4 == 0 && (T::NHS * T::NDT) % 4 == 0, "blocks split over 4 waves");
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
     const int b = blockIdx.y;
-    const int s_wave = blockIdx.x * kKeysPerGroup + 64 * wave;      // this wave's first key
+    const int s_group = blockIdx.x * kKeysPerGroup;
+    const int s_wave = s_group + 64 * wave;                          // this wave's first key
     const int D = L.D;
     const int dlim = (D >> 3) - 1;
 
@@ -354,7 +370,7 @@ __global__ __launch_bounds__(256, 1) void dk_keys_kernel(InLayout L, const float
     // ratio * (first key) - 1 sees any of its keys.
     int t0 = blockIdx.z * kQueryChunk;
     const int t1 = min(S, t0 + kQueryChunk);
-    if (ks == nullptr) t0 = (int)max((long)t0, (long)ratio * blockIdx.x * kKeysPerGroup - 1);
+    if (ks == nullptr) t0 = (int)max((long)t0, (long)ratio * s_group - 1);
     if (t0 >= t1) return;                                  // uniform: before any barrier
 
     // K fragments of the wave's 64 keys (B operand of D = Q K^T): kf[kc][st] =
@@ -375,39 +391,34 @@ __global__ __launch_bounds__(256, 1) void dk_keys_kernel(InLayout L, const float
         }
     }
 
-    // Stage query t into (qs, qt, ws): q in A-fragment order (block (r, st),
-    // lane l = head 32r + l%32, chunk 2st + l/32; padded heads repeat head H-1
-    // and padded chunks the last real one: they meet zero weights or zero K
-    // entries), the query's dk fragments, and its weights.
-    auto stage = [&](int t, uint8_t* qs, uint8_t* qt, float* ws) {
+    // Stage query t (all by direct global->LDS loads): q in A-fragment order
+    // (block (r, st), lane l = head 32r + l%32, chunk 2st + l/32; padded heads
+    // repeat head H-1 and padded chunks the last real one: they meet zero
+    // fragments or zero K entries), the query's dk fragments, and G at this
+    // wave's keys (clamped into the query's written range; masked where it is
+    // read).
+    auto stage = [&](int t, uint8_t* st_base) {
         const uint16_t* qrow = L.q + (long)t * L.q_t + (long)b * L.q_b;
 #pragma unroll
         for (int blk = wave; blk < T::NRT * T::NSTEP; blk += 4) {
             const int r = blk / T::NSTEP, st = blk % T::NSTEP;
             const int h = min(32 * r + l32, H - 1), d8 = min(2 * st + hf, dlim);
             __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(qrow + (long)h * D + 8 * d8),
-                                             (lds_ptr_t)(qs + blk * 1024), 16, 0, 0);
+                                             (lds_ptr_t)(st_base + QS + blk * 1024), 16, 0, 0);
         }
         const uint8_t* src = qtf + ((long)t * B + b) * T::QT_BYTES + 16 * lane;
 #pragma unroll
         for (int blk = wave; blk < T::NHS * T::NDT; blk += 4)
             __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + blk * 1024),
-                                             (lds_ptr_t)(qt + blk * 1024), 16, 0, 0);
-        if (wave == 0)
-            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(w + ((long)t * B + b) * H + min(lane, H - 1)),
-                                             (lds_ptr_t)ws, 4, 0, 0);
-    };
-    // G of this lane's keys for query t, 0 outside the query's range.
-    auto load_g = [&](int t, float (&g)[2]) {
+                                             (lds_ptr_t)(st_base + QT + blk * 1024), 16, 0, 0);
+        // One 64-lane dword load per wave: lane l carries key s_wave + l.
         int lo, hi;
         key_range(ks, ke, t, S, skv, ratio, lo, hi);
         const float* grow = G + ((long)b * S + t) * skv;
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-            const int s = s_wave + 32 * kc + l32;
-            const float v = grow[hi > lo ? min(max(s, lo), hi - 1) : 0];      // a written position
-            g[kc] = (s >= lo && s < hi) ? v : 0.0f;
-        }
+        const int sg = s_wave + lane;
+        const int sc = hi > lo ? min(max(sg, lo), hi - 1) : 0;           // a written position
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(grow + sc),
+                                         (lds_ptr_t)(st_base + GS + 4 * 64 * wave), 4, 0, 0);
     };
 
     f32x16 dkacc[2][T::NDT];
@@ -416,7 +427,16 @@ __global__ __launch_bounds__(256, 1) void dk_keys_kernel(InLayout L, const float
 #pragma unroll
         for (int dt = 0; dt < T::NDT; ++dt) dkacc[kc][dt] = f32x16{};
 
-    auto compute = [&](const uint8_t* qs, const uint8_t* qt, const float* ws, const float (&g)[2]) {
+    auto compute = [&](int t, const uint8_t* st_base) {
+        int lo, hi;
+        key_range(ks, ke, t, S, skv, ratio, lo, hi);
+        float g[2];
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+            const int s = s_wave + 32 * kc + l32;
+            const float v = reinterpret_cast<const float*>(st_base + GS)[64 * wave + 32 * kc + l32];
+            g[kc] = (s >= lo && s < hi) ? v : 0.0f;
+        }
         if (__ballot(g[0] != 0.0f || g[1] != 0.0f) == 0ull) return;     // no selected key in this wave
         // D = Q K^T: lanes are keys (32kc + lane%32), rows heads 32r + c_row(i, hf).
         f32x16 accd[T::NRT][2];
@@ -426,62 +446,61 @@ __global__ __launch_bounds__(256, 1) void dk_keys_kernel(InLayout L, const float
         for (int st = 0; st < T::NSTEP; ++st)
 #pragma unroll
             for (int r = 0; r < T::NRT; ++r) {
-                const bf16x8 qa = as_bf16x8(*reinterpret_cast<const u32x4*>(qs + (r * T::NSTEP + st) * 1024 + 16 * lane));
+                const bf16x8 qa =
+                    as_bf16x8(*reinterpret_cast<const u32x4*>(st_base + QS + (r * T::NSTEP + st) * 1024 + 16 * lane));
 #pragma unroll
                 for (int kc = 0; kc < 2; ++kc) accd[r][kc] = mfma_32x32x16(qa, kf[kc][st], accd[r][kc]);
             }
-        // w of the heads on the accumulator rows (4 consecutive heads per group).
-        float wv[T::NRT][16];
+        // dk += (m G) (w Q): A = the key's G (bf16) where d > 0, in the order of
+        // D's accumulator rows (contraction over heads); B the query's dk
+        // fragments, each read once for both key halves.
+        const uint32_t gg[2] = {(uint32_t)bf16_bits(g[0]) * 0x10001u, (uint32_t)bf16_bits(g[1]) * 0x10001u};
 #pragma unroll
         for (int r = 0; r < T::NRT; ++r)
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const float4 ww = *reinterpret_cast<const float4*>(ws + 32 * r + c_row(4 * q4, hf));
-                const float wx[4] = {ww.x, ww.y, ww.z, ww.w};
+            for (int s = 0; s < 2; ++s) {
+                bf16x8 af[2];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) wv[r][4 * q4 + u] = (32 * r + c_row(4 * q4 + u, hf) < H) ? wx[u] : 0.0f;
-            }
-        // dk += (m G w) Q: A from D's accumulators (contraction over heads), B the
-        // query's dk fragments.
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-            for (int r = 0; r < T::NRT; ++r)
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
+                for (int kc = 0; kc < 2; ++kc) {
                     u32x4 av;
 #pragma unroll
                     for (int p = 0; p < 4; ++p) {
                         const int i0 = 8 * s + 2 * p;
-                        av[p] = mask_pair(pack_bf16(g[kc] * wv[r][i0], g[kc] * wv[r][i0 + 1]), accd[r][kc][i0],
-                                          accd[r][kc][i0 + 1]);
+                        av[p] = mask_pair(gg[kc], accd[r][kc][i0], accd[r][kc][i0 + 1]);
                     }
-                    const bf16x8 af = as_bf16x8(av);
-#pragma unroll
-                    for (int dt = 0; dt < T::NDT; ++dt) {
-                        const bf16x8 qf = as_bf16x8(
-                            *reinterpret_cast<const u32x4*>(qt + ((2 * r + s) * T::NDT + dt) * 1024 + 16 * lane));
-                        dkacc[kc][dt] = mfma_32x32x16(af, qf, dkacc[kc][dt]);
-                    }
+                    af[kc] = as_bf16x8(av);
                 }
+#pragma unroll
+                for (int dt = 0; dt < T::NDT; ++dt) {
+                    const bf16x8 qf = as_bf16x8(
+                        *reinterpret_cast<const u32x4*>(st_base + QT + ((2 * r + s) * T::NDT + dt) * 1024 + 16 * lane));
+#pragma unroll
+                    for (int kc = 0; kc < 2; ++kc) dkacc[kc][dt] = mfma_32x32x16(af[kc], qf, dkacc[kc][dt]);
+                }
+            }
     };
 
-    // One barrier per query: it waits for the staging of the query computed
-    // next (issued a query earlier) and for every wave to be done with the
-    // buffers the following staging overwrites.
-    float g_c[2], g_n[2] = {0.0f, 0.0f};
-    stage(t0, qs0, qt0, ws0);
-    load_g(t0, g_c);
-    __syncthreads();
-    for (int t = t0; t < t1; ++t) {
-        const bool odd = ((t - t0) & 1) != 0;
-        if (t + 1 < t1) {
-            stage(t + 1, odd ? qs0 : qs1, odd ? qt0 : qt1, odd ? ws0 : ws1);
-            load_g(t + 1, g_n);
-        }
-        compute(odd ? qs1 : qs0, odd ? qt1 : qt0, odd ? ws1 : ws0, g_c);
-        g_c[0] = g_n[0]; g_c[1] = g_n[1];
-        __syncthreads();
+    auto wait_and_barrier = [&](bool more) {
+        if (!more) __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+        else __builtin_amdgcn_s_waitcnt(wait_vmcnt(PER_WAVE));
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    };
+    auto iter = [&](int t, const uint8_t* cur, uint8_t* ahead2) {
+        if (t + 2 < t1) stage(t + 2, ahead2);
+        compute(t, cur);
+        wait_and_barrier(t + 2 < t1);
+    };
+    stage(t0, lds0);
+    if (t0 + 1 < t1) stage(t0 + 1, lds1);
+    wait_and_barrier(t0 + 1 < t1);
+    for (int t = t0; t < t1; t += 3) {
+        iter(t, lds0, lds2);
+        if (t + 1 >= t1) break;
+        iter(t + 1, lds1, lds0);
+        if (t + 2 >= t1) break;
+        iter(t + 2, lds2, lds1);
     }
 
     // dk rows of the wave's keys: key s_wave + 32kc + c_row(i, hf), index_dim
@@ -529,7 +548,7 @@ static hipError_t launch_backward_t(const BackwardArgs& p) {
     hipLaunchKernelGGL(grad_scatter_kernel, dim3(rows), dim3(256), row_bytes, p.stream, p.indices, p.grad,
                        p.B, p.S, p.Skv, p.ratio, p.ks, p.ke, p.topk, G);
     hipLaunchKernelGGL((qt_fragments_kernel<H, DP>), dim3(rows), dim3(kWave), 0, p.stream,
-                       static_cast<const uint16_t*>(p.q), p.D, qtf);
+                       static_cast<const uint16_t*>(p.q), p.w, p.D, qtf);
     hipLaunchKernelGGL((backward_rows_kernel<H, DP>), dim3(rows), dim3(kWave), 0, p.stream, L, p.w, p.indices,
                        p.grad, p.B, p.S, p.Skv, p.ratio, p.ks, p.ke, p.topk, p.dq, p.dw);
     const dim3 grid((unsigned)((p.Skv + kKeysPerGroup - 1) / kKeysPerGroup), (unsigned)p.B,

@@ -14,12 +14,14 @@ Test infrastructure.  Tolerances:
 * V4.1 scores: within 2 bf16 ulp of the oracle, or inside the interval the
   oracle derives for float32 accumulation in any order; -inf exactly where
   hidden.
-* Backward (dq, dk, dw): |g - o| <= 2**-8 * mag + amb + 1e-6, with mag and
-  amb from the oracle: the kernel's gradient GEMMs take one bfloat16-rounded
-  factor per term (g_j for dq, w_h for dk: relative error <= 2**-9) and add
-  in float32 (<= 2**-24 per addition, far below 2**-9 for the term counts
-  here); amb covers (head, key) pairs whose dot product a float32 sum may put
-  on the other side of 0.
+* Backward (dq, dk, dw): |g - o| <= (2**-7 + 2**-12) * mag + amb + 1e-6,
+  with mag and amb from the oracle: the kernel's gradient GEMMs take up to two
+  bfloat16-rounded factors per term (g for dq; G and w q for dk), each with
+  relative error <= 2**-8 (bf16 keeps 8 significant bits), so a term is off by
+  at most 2 * 2**-8 + 2**-16 of its size, and they add in float32 (<= 2**-24
+  per addition: below 2**-13 of mag for the term counts here); amb covers
+  (head, key) pairs whose dot product a float32 sum may put on the other side
+  of 0.
 """
 
 import numpy as np
@@ -119,7 +121,7 @@ def check_v41(gpu_bits, ora, lo, hi, where=""):
     return int((~near & inside).sum())
 
 
-BACKWARD_REL = 2.0 ** -8
+BACKWARD_REL = 2.0 ** -7 + 2.0 ** -12
 
 
 def check_backward_one(got, name, ora, bound, where=""):

@@ -587,12 +587,23 @@ def test_backward_checker_accepts_bf16_rounding_and_rejects_planted_errors():
     grads, bounds = oracle.indexer_backward(q, k, w, idx, g, ks, ke, with_bounds=True)
     names = ("dq", "dk", "dw")
     checkers.check_backward(dict(zip(names, grads)), grads, bounds)
-    # What a kernel with bf16-rounded gradient factors computes passes too.
+    # What a kernel with bf16-rounded gradient factors computes passes too:
+    # g rounded for dq; G rounded and w q rounded for dk.
     g16 = oracle.rne_bf16(g)
-    w16 = oracle.rne_bf16(w)
     dq16 = oracle.indexer_backward(q, k, w, idx, g16, ks, ke)[0]
-    dk16 = oracle.indexer_backward(q, k, w16, idx, g, ks, ke)[1]
-    checkers.check_backward({"dq": dq16, "dk": dk16, "dw": grads[2]}, grads, bounds)
+    checkers.check_backward({"dq": dq16, "dk": grads[1], "dw": grads[2]}, grads, bounds)
+    S, B, H, D = q.shape
+    dk16 = np.zeros_like(k)
+    for b in range(B):
+        for t in range(S):
+            for j in range(idx.shape[2]):
+                s_ = idx[b, t, j]
+                if not (ks[t] <= s_ < min(ke[t], k.shape[0])):
+                    continue
+                m = (q[t, b] @ k[s_, b] > 0).astype(np.float64)
+                wq = oracle.rne_bf16(w[t, b][:, None] * q[t, b])             # [H, D]
+                dk16[s_, b] += oracle.rne_bf16(g[b, t, j]) * (m @ wq)
+    checkers.check_backward({"dq": grads[0], "dk": dk16, "dw": grads[2]}, grads, bounds)
     # Planted mistakes in the oracle's arithmetic are caught.
     planted = {
         "dq without w": oracle.indexer_backward(q, k, np.ones_like(w), idx, g, ks, ke)[0],
