@@ -10,7 +10,8 @@ are timed on the same inputs: lix_topk's fused path (no logits in HBM) and
 the materialized path (lix_indexer_logits, then lix_topk over the logits);
 the step is the faster one, named in config.path.  The same run also times
 the gather lix_topk_scores at the selected indices, the direct scoring at
-those indices (lix_indexer_scores_at), lix_indexer_scores_v41 and a top-512 of its
+those indices (lix_indexer_scores_at), the backward of those scores
+(lix_indexer_backward, seeded upstream gradient), lix_indexer_scores_v41 and a top-512 of its
 bf16 scores (lix_topk_bf16) on the V4.1 workload (batch 1, 16384 queries, 4096
 keys, packed documents), a 1 GiB device copy (achievable HBM bandwidth), the
 4K workload cold (L2 and MALL flushed by a 1 GiB write before each call) and
@@ -118,16 +119,6 @@ def extra_parts(dev, steps, warmup):
     out["copy_gbs"] = 2.0 * src.numel() * 4 / copy_ms / 1e6             # read + write
     flush = lambda: dst.fill_(0.0)                                        # 1 GiB write: evicts L2 and MALL
     del src
-    # achievable fp32 atomic-add rate: 2^21 rows of 128 floats added at random rows of a [8192, 128]
-    # table (the access pattern of the backward's dk adds), through torch's index_add_
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(5)
-    rows = torch.randint(0, 8192, (1 << 21,), device=dev, generator=gen)
-    vals = torch.ones(1 << 21, 128, device=dev)
-    table = torch.zeros(8192, 128, device=dev)
-    atom_ms = time_each(lambda: table.index_add_(0, rows, vals), steps, warmup)
-    out["atomic_add_f32_per_s"] = float(vals.numel()) / (atom_ms * 1e-3)
-    del rows, vals, table
 
     cfg = synth.WORKLOADS["4k"]
     inp = synth.v4_inputs(**cfg)
@@ -333,9 +324,8 @@ def main():
         bw_ms, _ = time_loop(lambda: lx.indexer_backward(q, k, w, c, ix_f, g_up), max(3, args.steps // 4), 2)
         parts.update({
             "backward_ms": bw_ms,
-            # four GEMM passes over the selected entries: d twice (recompute), dq, dk
+            # algorithmic work: four GEMM passes over the selected entries (d twice, dq, dk)
             "backward_gemm_tflops": 4 * 2.0 * H * D * at_pairs / bw_ms / 1e9,
-            "backward_dk_atomic_adds_per_s": float(at_pairs) * D / (bw_ms * 1e-3),
         })
         del g_up
 
