@@ -548,40 +548,46 @@ __global__ __launch_bounds__(kRowThreads, MINB) void topk_rows_reg_kernel(
 
 // ---------------------------------------------------------------- binned workgroup row top-k
 //
-// Rows of at most 1024*VEC visible keys, one workgroup (four waves) per row.
-// The row sits in registers: wave w holds elements w*256*VEC + 256*j +
-// 4*lane + m in x[j][m]; slots past the row hold NaN.  The bin of a score is
-// a monotone function of it: u = 1 + 2^-12 + (v - vmin) * (1 - 2^-11) / span
-// lies in [1, 2), so the 11 leading mantissa bits of u are a linear bin in
-// 0..2047 (a subtract, an fma and a bit-field extract per element; the
-// margins keep u inside [1, 2) under rounding).  A 2048-bin LDS histogram
-// locates the bin holding the topk-th best element; that bin's elements
-// (a handful for smooth score distributions) are gathered and ranked exactly
-// by (score descending, key index ascending), which gives the cut element
-// (vT, iT).  A boundary bin of more than kBinCand elements, or a row whose
-// score range is zero or not finite, falls back to a radix select on
-// order-preserving keys.  The ordered write is that of the register-resident
-// kernel.
+// Rows of at most 1024*NCH visible keys, one workgroup (four waves) per row.
+// The row is cut into chunks of 256 keys dealt round-robin to the waves:
+// chunk c = 4j + w sits in wave w's registers as x[j][m] = key 256c + 64m +
+// lane (one coalesced 4- or 2-byte load per slot), so every wave holds about
+// a quarter of any row; the row's last, partial chunk holds NaN past the row.
+// Walking chunk c's slots in m order visits its keys in ascending order, 64
+// at a time, so the output position of a selected slot is the selection count
+// of the chunks before c, plus a wave-uniform running count, plus the
+// selected lanes below it (mbcnt over the compare mask): no per-lane scans.
+//
+// The bin of a score is a monotone function of it: u = v*sc + c0 lies in
+// [1, 2) for every v in [vmin, vmax] (sc = (1 - 2^-11)/span, c0 = 1 + 2^-12 -
+// vmin*sc; one fma, and the margins of 2^-12 absorb the rounding of c0 while
+// |vmin*sc| <= 256; otherwise u = (v - vmin)*sc + 1 + 2^-12), so the 11
+// leading mantissa bits of u are a linear bin in 0..2047.  A 2048-bin LDS
+// histogram locates the bin holding the topk-th best element; that bin's
+// elements (a handful for smooth score distributions) are gathered and ranked
+// exactly by (score descending, key index ascending), which gives the cut
+// element (vT, iT).  Equal scores share a bin, so the ranking also tells
+// whether any other key ties with vT; when none does, the selection is the
+// single compare v >= vT.  A boundary bin of more than kBinCand elements, or a
+// row whose score range is zero or not finite, falls back to a radix select
+// on order-preserving keys.
 constexpr int kBinCand = 256;
 constexpr int kBinThreads = 256;
+constexpr int kBinChunks = 32;                    // 256-key chunks per row (8192 keys)
 
 struct BinShared {
     uint32_t hist[kBins];
     float cand_v[kBinCand];
     int cand_i[kBinCand];
+    int ccnt[kBinChunks];                         // per-chunk counts, row order
     float wmin[4], wmax[4];
     int wtot[4];
     int ncand;
     int bstar, rstar;
     float cut_v;
     int cut_i;
+    int cut_ties;                                 // another key has score vT
 };
-
-// Bin of score v for a row with minimum vmin; sc = (1 - 2^-11) / span.
-__device__ __forceinline__ int score_bin(float v, float vmin, float sc) {
-    const float u = fmaf(v - vmin, sc, 1.000244140625f);          // 1 + 2^-12
-    return (int)((__float_as_uint(u) >> 12) & (uint32_t)(kBins - 1));
-}
 
 // Block-wide: the bin holding the need-th largest element of hist[0..NB) and
 // the element's 1-based rank inside it, counted from the top, into sh.bstar /
@@ -620,23 +626,55 @@ __device__ void block_find_bin(BinShared& sh, int need, int tid) {
     __syncthreads();
 }
 
+// Number of set bits of mask in lanes below this one, plus acc.
+__device__ __forceinline__ int mbcnt(unsigned long long mask, int acc) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mask, (uint32_t)acc));
+}
+
+// f(j, partial) for the wave's chunks j < jmax that hold keys; partial is a
+// compile-time flag, true for chunk jpart (the row's last chunk, which may
+// hold NaN slots) or for every chunk when ALL_PARTIAL.  The bounds pass
+// through an empty asm statement so each pass recomputes its scalar chunk
+// conditions instead of keeping them live across the kernel.
+template <int NCH, bool ALL_PARTIAL, class F>
+__device__ __forceinline__ void visit_chunks(int jmax, int jpart, F&& f) {
+    asm volatile("" : "+s"(jmax), "+s"(jpart));
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        if (j >= jmax) break;
+        if (ALL_PARTIAL || j == jpart) f(j, std::true_type{});
+        else f(j, std::false_type{});
+    }
+}
+
+// Exclusive prefix of sh.ccnt over the row's chunks, as a lane value: lane c
+// (< nch) holds the count of chunks 0..c-1; *total = count of all chunks.
+__device__ __forceinline__ int chunk_offsets(const BinShared& sh, int nch, int lane, int* total) {
+    const int c = lane < nch ? sh.ccnt[lane] : 0;
+    const int incl = wave_incl_scan(c, lane);
+    *total = __builtin_amdgcn_readlane(incl, 63);
+    return incl - c;
+}
+
 // BF16 = false: fp32 logits of the causal or given ranges (lix_topk).
 // BF16 = true: V4.1 bf16 scores over whole rows, where bf16 -inf (0xFF80)
 // marks a hidden key: hidden keys are loaded as NaN slots, so they are
 // never binned, ranked or selected; a row with at most topk visible keys
 // selects all of them and pads the rest with (-1, bf16 -inf).  Selected
 // values are written back in the input's type, bit for bit.
-template <int VEC, bool BF16>
+template <int NCH, bool BF16>
 __global__ __launch_bounds__(kBinThreads) void topk_rows_bin_kernel(const void* __restrict__ logits_v, int B, int S,
                                                                     int skv, int ratio,
                                                                     const int32_t* __restrict__ ks,
                                                                     const int32_t* __restrict__ ke, int topk,
                                                                     void* __restrict__ scores_v,
                                                                     int32_t* __restrict__ indices) {
+    static_assert(4 * NCH <= kBinChunks, "chunk table too small");
     using In = typename std::conditional<BF16, uint16_t, float>::type;
-    constexpr int SPAN = 256 * VEC;                           // elements per wave
     __shared__ BinShared sh;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int b = blockIdx.x % B;
     const int t = S - 1 - (int)(blockIdx.x / B);              // longest causal rows first
     int lo = 0, hi = skv;
@@ -669,58 +707,45 @@ __global__ __launch_bounds__(kBinThreads) void topk_rows_bin_kernel(const void* 
         }
     }
 
-    // ---- this wave's part of the row (every load issues before the first wait)
+    // ---- chunks: nch of the row, jmax of this wave, jpart the wave's partial one
+    const int nch = (n + 255) >> 8;
+    const int jmax = (nch - wv + 3) >> 2;
+    const int jpart = (((nch - 1) & 3) == wv && (n & 255) != 0) ? (nch - 1) >> 2 : -1;
+    auto key_of = [&](int j, int m) { return (4 * j + wv) * 256 + 64 * m + lane; };   // key - lo
+    constexpr bool AP = BF16;                                 // bf16: hidden keys anywhere
+
+    // ---- this wave's chunks (every load issues before the first use)
     const float qnan = __uint_as_float(0x7fc00000u);
-    const int ebase = wv * SPAN;
-    const int nloc = max(0, min(n - ebase, SPAN));
-    const bool vec_ok = (reinterpret_cast<uintptr_t>(logits) & 15) == 0 && ((skv | lo) & 3) == 0;
     auto cvt = [&](In raw) -> float {
         if constexpr (BF16) return raw == (uint16_t)0xff80u ? qnan : bf16_to_f32(raw);
         else return raw;
     };
-    float x[VEC][4];
+    float x[NCH][4];
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) x[j][0] = x[j][1] = x[j][2] = x[j][3] = qnan;
-    if (nloc > 0) {
-        const In* wrow = row + ebase;
-        if (vec_ok) {
-            const int last = (nloc - 1) & ~3;
+    for (int j = 0; j < NCH; ++j)
 #pragma unroll
-            for (int j = 0; j < VEC; ++j) {
-                const int e0 = j * 256 + 4 * lane;
-                In y[4];
-                if constexpr (BF16) {
-                    const uint2 r = *reinterpret_cast<const uint2*>(wrow + min(e0, last));
-                    y[0] = (uint16_t)(r.x & 0xffffu); y[1] = (uint16_t)(r.x >> 16);
-                    y[2] = (uint16_t)(r.y & 0xffffu); y[3] = (uint16_t)(r.y >> 16);
-                } else {
-                    const float4 r = *reinterpret_cast<const float4*>(wrow + min(e0, last));
-                    y[0] = r.x; y[1] = r.y; y[2] = r.z; y[3] = r.w;
-                }
+        for (int m = 0; m < 4; ++m) x[j][m] = qnan;           // chunks past the row
+    visit_chunks<NCH, false>(jmax, jpart, [&](int j, auto partial) {
 #pragma unroll
-                for (int m = 0; m < 4; ++m) x[j][m] = (e0 + m < nloc) ? cvt(y[m]) : qnan;
+        for (int m = 0; m < 4; ++m) {
+            const int e = key_of(j, m);
+            if constexpr (decltype(partial)::value) {
+                const float v = cvt(row[min(e, n - 1)]);
+                x[j][m] = (e < n) ? v : qnan;
+            } else {
+                x[j][m] = cvt(row[e]);
             }
-        } else {
-#pragma unroll
-            for (int j = 0; j < VEC; ++j)
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const int e = j * 256 + 4 * lane + m;
-                    const In v = wrow[min(e, nloc - 1)];
-                    x[j][m] = (e < nloc) ? cvt(v) : qnan;
-                }
         }
-    }
+    });
 
     // ---- bf16 rows: count the visible keys; at most topk of them means all
     int visible = n;
     if constexpr (BF16) {
         int c = 0;
+        visit_chunks<NCH, AP>(jmax, jpart, [&](int j, auto) {
 #pragma unroll
-        for (int j = 0; j < VEC; ++j)
-#pragma unroll
-            for (int m = 0; m < 4; ++m) c += (x[j][m] == x[j][m]) ? 1 : 0;
-        c = __builtin_amdgcn_readlane(wave_incl_scan(c, lane), 63);
+            for (int m = 0; m < 4; ++m) c += __popcll(__ballot(x[j][m] == x[j][m]));
+        });
         if (lane == 0) sh.wtot[wv] = c;
         __syncthreads();
         visible = sh.wtot[0] + sh.wtot[1] + sh.wtot[2] + sh.wtot[3];
@@ -728,10 +753,10 @@ __global__ __launch_bounds__(kBinThreads) void topk_rows_bin_kernel(const void* 
     }
     const bool take_all = visible <= topk;                    // same in every thread
 
-    // ---- row min / max (NaN slots are ignored)
+    // ---- row min / max over every slot (NaN slots are ignored)
     float vmin = __uint_as_float(0x7f800000u), vmax = neg_inf();
 #pragma unroll
-    for (int j = 0; j < VEC; ++j)
+    for (int j = 0; j < NCH; ++j)
 #pragma unroll
         for (int m = 0; m < 4; ++m) { vmin = fminf(vmin, x[j][m]); vmax = fmaxf(vmax, x[j][m]); }
 #pragma unroll
@@ -749,22 +774,31 @@ __global__ __launch_bounds__(kBinThreads) void topk_rows_bin_kernel(const void* 
     // (A span below 1e-30 would overflow the scale; such rows take the radix path.)
     const bool binned = span > 1.0e-30f && span < 3.0e38f;   // same in every thread
     const float sc = binned ? 0.99951171875f / span : 0.0f;  // (1 - 2^-11) / span
+    const bool one_fma = binned && fabsf(vmin) * sc <= 256.0f;
+    const float c0 = one_fma ? 1.000244140625f - vmin * sc : 1.000244140625f;   // 1 + 2^-12
+    // bin_of(one, v): `one` selects the one-fma form at compile time; each
+    // pass branches once (uniformly) between the two forms.
+    auto bin_of = [&](auto one, float v) -> int {
+        const float u = decltype(one)::value ? fmaf(v, sc, c0) : fmaf(v - vmin, sc, c0);
+        return (int)((__float_as_uint(u) >> 12) & (uint32_t)(kBins - 1));
+    };
+    auto with_form = [&](auto&& f) {
+        if (one_fma) f(std::true_type{});
+        else f(std::false_type{});
+    };
 
     int bstar = 0, rstar = topk, cb = 1 << 30;
+    bool counted = false;                                     // sh.ccnt holds the chunk counts
     if (binned && !take_all) {
-#pragma unroll
-        for (int j = 0; j < VEC; ++j) {
-            if (!BF16 && (j + 1) * 256 <= nloc) {             // whole chunk inside the row (no NaN slots)
-#pragma unroll
-                for (int m = 0; m < 4; ++m) atomicAdd(&sh.hist[score_bin(x[j][m], vmin, sc)], 1u);
-            } else if (j * 256 < nloc) {
+        with_form([&](auto one) {
+            visit_chunks<NCH, AP>(jmax, jpart, [&](int j, auto partial) {
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const float v = x[j][m];
-                    if (v == v) atomicAdd(&sh.hist[score_bin(v, vmin, sc)], 1u);
+                    if (!decltype(partial)::value || v == v) atomicAdd(&sh.hist[bin_of(one, v)], 1u);
                 }
-            }
-        }
+            });
+        });
         __syncthreads();
         block_find_bin<kBins>(sh, topk, tid);
         bstar = sh.bstar;
@@ -774,41 +808,56 @@ __global__ __launch_bounds__(kBinThreads) void topk_rows_bin_kernel(const void* 
 
     if (take_all) {
         // ---- at most topk visible keys: every visible key is selected
-        if (tid == 0) { sh.cut_v = neg_inf(); sh.cut_i = 0x7fffffff; }
+        if (tid == 0) { sh.cut_v = neg_inf(); sh.cut_i = 0x7fffffff; sh.cut_ties = 1; }
         __syncthreads();
     } else if (cb <= kBinCand) {
-        // ---- gather the boundary bin and rank it exactly
+        // ---- gather the boundary bin (exactly the cb keys the histogram
+        // counted there) and rank it exactly.  The same pass counts, per
+        // chunk, the keys in bins above it (all selected); each selected
+        // candidate then adds itself to its chunk's count.
+        int ccv = 0;                                          // lane j: count of chunk j
+        with_form([&](auto one) {
+            visit_chunks<NCH, AP>(jmax, jpart, [&](int j, auto partial) {
+                int above = 0;
 #pragma unroll
-        for (int j = 0; j < VEC; ++j)
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const float v = x[j][m];
-                const bool c = (v == v) && score_bin(v, vmin, sc) == bstar;
-                const unsigned long long mask = __ballot(c);
-                if (mask != 0ull) {
-                    int base = 0;
-                    if (lane == 0) base = atomicAdd(&sh.ncand, __popcll(mask));
-                    base = __shfl(base, 0, 64);
-                    if (c) {
-                        const int p = base + lanes_below(mask, lane);
-                        sh.cand_v[p] = v;
-                        sh.cand_i[p] = ebase + j * 256 + 4 * lane + m;
+                for (int m = 0; m < 4; ++m) {
+                    const float v = x[j][m];
+                    const int bn = bin_of(one, v);
+                    const bool ok = !decltype(partial)::value || v == v;
+                    above += __popcll(__ballot(bn > bstar && ok));
+                    const bool c = bn == bstar && ok;
+                    const unsigned long long mask = __ballot(c);
+                    if (mask != 0ull) {
+                        int base = 0;
+                        if (lane == 0) base = atomicAdd(&sh.ncand, __popcll(mask));
+                        base = __shfl(base, 0, 64);
+                        if (c) {
+                            const int p = mbcnt(mask, base);
+                            sh.cand_v[p] = v;
+                            sh.cand_i[p] = key_of(j, m);
+                        }
                     }
                 }
-            }
+                ccv = (lane == j) ? above : ccv;
+            });
+        });
+        if (lane < jmax) sh.ccnt[4 * lane + wv] = ccv;
         __syncthreads();
         if (tid < cb) {
             const float vi = sh.cand_v[tid];
             const int ii = sh.cand_i[tid];
-            int rank = 0;
+            int rank = 0, eq = 0;
             for (int jj = 0; jj < cb; ++jj) {
                 const float vj = sh.cand_v[jj];
                 const int ij = sh.cand_i[jj];
                 rank += (vj > vi) || (vj == vi && ij < ii);
+                eq += (vj == vi);
             }
-            if (rank == rstar - 1) { sh.cut_v = vi; sh.cut_i = ii; }
+            if (rank == rstar - 1) { sh.cut_v = vi; sh.cut_i = ii; sh.cut_ties = eq > 1; }
+            if (rank < rstar) atomicAdd(&sh.ccnt[ii >> 8], 1);
         }
         __syncthreads();
+        counted = true;
     } else {
         // ---- radix select on the keys of the boundary bin (or of the whole
         // row when it is not binned), 8-bit digits ...
@@ -817,15 +866,17 @@ __global__ __launch_bounds__(kBinThreads) void topk_rows_bin_kernel(const void* 
         for (int shift = 24; shift >= 0; shift -= 8) {
             for (int i = tid; i < 256; i += kBinThreads) sh.hist[i] = 0u;
             __syncthreads();
+            with_form([&](auto one) {
+                visit_chunks<NCH, true>(jmax, jpart, [&](int j, auto) {
 #pragma unroll
-            for (int j = 0; j < VEC; ++j)
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const float v = x[j][m];
-                    const bool in = (v == v) && (!binned || score_bin(v, vmin, sc) == bstar);
-                    const uint32_t k = f32_to_key(v);
-                    if (in && (k & pmask) == prefix) atomicAdd(&sh.hist[(k >> shift) & 255u], 1u);
-                }
+                    for (int m = 0; m < 4; ++m) {
+                        const float v = x[j][m];
+                        const bool in = (v == v) && (!binned || bin_of(one, v) == bstar);
+                        const uint32_t k = f32_to_key(v);
+                        if (in && (k & pmask) == prefix) atomicAdd(&sh.hist[(k >> shift) & 255u], 1u);
+                    }
+                });
+            });
             __syncthreads();
             block_find_bin<256>(sh, need, tid);
             prefix |= (uint32_t)sh.bstar << shift;
@@ -833,77 +884,94 @@ __global__ __launch_bounds__(kBinThreads) void topk_rows_bin_kernel(const void* 
             need = sh.rstar;
             __syncthreads();                                  // bstar / rstar read before reuse
         }
-        // ... then the need-th smallest key index among the scores equal to it
+        // ... then the need-th smallest key index among the scores equal to
+        // it: count them per chunk, then walk the chunks in row order
         const float vt = key_to_f32(prefix);
-        int cnt = 0;
-#pragma unroll
-        for (int j = 0; j < VEC; ++j)
-#pragma unroll
-            for (int m = 0; m < 4; ++m) cnt += (x[j][m] == vt) ? 1 : 0;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
-        if (lane == 0) sh.wtot[wv] = cnt;
-        __syncthreads();
-        int run = 0;
-        for (int w2 = 0; w2 < wv; ++w2) run += sh.wtot[w2];
-#pragma unroll
-        for (int j = 0; j < VEC; ++j) {
+        visit_chunks<NCH, true>(jmax, jpart, [&](int j, auto) {
             int c = 0;
 #pragma unroll
-            for (int m = 0; m < 4; ++m) c += (x[j][m] == vt) ? 1 : 0;
-            const int incl = wave_incl_scan(c, lane);
-            int r = run + incl - c;
-            if (r < need && need <= r + c) {
+            for (int m = 0; m < 4; ++m) c += __popcll(__ballot(x[j][m] == vt));
+            if (lane == 0) sh.ccnt[4 * j + wv] = c;
+        });
+        __syncthreads();
+        int total_eq;
+        const int off = chunk_offsets(sh, nch, lane, &total_eq);
+        visit_chunks<NCH, true>(jmax, jpart, [&](int j, auto) {
+            int run = __builtin_amdgcn_readlane(off, 4 * j + wv);
 #pragma unroll
-                for (int m = 0; m < 4; ++m)
-                    if (x[j][m] == vt) {
-                        ++r;
-                        if (r == need) { sh.cut_v = vt; sh.cut_i = ebase + j * 256 + 4 * lane + m; }
-                    }
+            for (int m = 0; m < 4; ++m) {
+                const unsigned long long mask = __ballot(x[j][m] == vt);
+                const int c = __popcll(mask);
+                if (run < need && need <= run + c && ((mask >> lane) & 1ull) && mbcnt(mask, run) == need - 1) {
+                    sh.cut_v = vt;
+                    sh.cut_i = key_of(j, m);
+                    sh.cut_ties = total_eq > 1;
+                }
+                run += c;
             }
-            run += __shfl(incl, 63, 64);
-        }
+        });
         __syncthreads();
     }
-    const float vT = sh.cut_v;
-    const int iT = sh.cut_i;
 
-    // ---- ordered write of the selection.  The selection is evaluated once,
-    // as a bit mask (bit 4j+m), for both the per-wave count and the write.
-    uint32_t selm = 0;
+    // ---- ordered write of the selection: an element is selected iff its
+    // score is above vT, or equal to it with key index <= iT (with no tie,
+    // iff its score is >= vT).  Bins are monotone in the score, so that is
+    // every key in a bin above the boundary bin plus the selected candidates:
+    // the counts the boundary pass made.  The other routes count each chunk's
+    // selection in a pass of their own.  The write pass puts each selected
+    // slot at its position (32-bit byte offsets from the row's output base).
+    // Each pass reads the cut from LDS, so no compare mask stays live across
+    // a barrier.
+    auto selected = [&](auto tie, int j, int m, float vT, int iT) -> bool {
+        const float v = x[j][m];
+        if constexpr (!decltype(tie)::value) return v >= vT;
+        else return (v > vT) | ((v == vT) & (key_of(j, m) <= iT));
+    };
+    auto with_ties = [&](bool ties, auto&& f) {
+        if (ties) f(std::true_type{});
+        else f(std::false_type{});
+    };
+    if (!counted) {
+        const float vT = sh.cut_v;
+        const int iT = sh.cut_i;
+        int ccv = 0;                                          // lane j: count of chunk j
+        with_ties(sh.cut_ties != 0, [&](auto tie) {
+            visit_chunks<NCH, AP>(jmax, jpart, [&](int j, auto) {
+                int c = 0;
 #pragma unroll
-    for (int j = 0; j < VEC; ++j)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const float v = x[j][m];
-            const bool f = v > vT || (v == vT && ebase + j * 256 + 4 * lane + m <= iT);
-            selm |= f ? (1u << (4 * j + m)) : 0u;
-        }
-    const int wcnt = __builtin_amdgcn_readlane(wave_incl_scan(__popc(selm), lane), 63);
-    __syncthreads();                                          // wtot reads above are done
-    if (lane == 0) sh.wtot[wv] = wcnt;
-    __syncthreads();
-    int run = 0;
-    for (int w2 = 0; w2 < wv; ++w2) run += sh.wtot[w2];
-#pragma unroll
-    for (int j = 0; j < VEC; ++j) {
-        const uint32_t bits = (selm >> (4 * j)) & 15u;
-        const int c = __popc(bits);
-        const int incl = wave_incl_scan(c, lane);
-        int pos = run + incl - c;
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-            if (((bits >> m) & 1u) && pos < topk) {
-                so[pos] = out_val(x[j][m]);
-                io[pos] = lo + ebase + j * 256 + 4 * lane + m;
-                ++pos;
-            }
-        run += __builtin_amdgcn_readlane(incl, 63);
+                for (int m = 0; m < 4; ++m) c += __popcll(__ballot(selected(tie, j, m, vT, iT)));
+                ccv = (lane == j) ? c : ccv;
+            });
+        });
+        if (lane < jmax) sh.ccnt[4 * lane + wv] = ccv;
+        __syncthreads();
     }
-    if constexpr (BF16) {
-        const int total = sh.wtot[0] + sh.wtot[1] + sh.wtot[2] + sh.wtot[3];
-        for (int i = total + tid; i < topk; i += kBinThreads) { so[i] = pad_val; io[i] = -1; }
+    int total;
+    const int off = chunk_offsets(sh, nch, lane, &total);
+    const int key0 = lo + lane + 256 * wv;
+    char* so_b = reinterpret_cast<char*>(so);
+    char* io_b = reinterpret_cast<char*>(io);
+    {
+        const float vT = sh.cut_v;
+        const int iT = sh.cut_i;
+        with_ties(sh.cut_ties != 0, [&](auto tie) {
+            visit_chunks<NCH, AP>(jmax, jpart, [&](int j, auto) {
+                int run = __builtin_amdgcn_readlane(off, 4 * j + wv);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const bool f = selected(tie, j, m, vT, iT);
+                    const unsigned long long mask = __ballot(f);
+                    const uint32_t pos = (uint32_t)mbcnt(mask, run);
+                    if (f && pos < (uint32_t)topk) {
+                        *reinterpret_cast<In*>(so_b + pos * (uint32_t)sizeof(In)) = out_val(x[j][m]);
+                        *reinterpret_cast<int32_t*>(io_b + pos * 4u) = key0 + 1024 * j + 64 * m;
+                    }
+                    run += __popcll(mask);
+                }
+            });
+        });
     }
+    for (int i = total + tid; i < topk; i += kBinThreads) { so[i] = pad_val; io[i] = -1; }
 }
 
 __global__ __launch_bounds__(256) void gather_kernel(const float* __restrict__ logits,
