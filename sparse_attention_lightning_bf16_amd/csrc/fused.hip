@@ -121,7 +121,8 @@ __global__ __launch_bounds__(256) void v4_fused_topk_kernel(InLayout L, const fl
     __shared__ uint32_t hist_all[T::NWAVE][256];
     extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int nqb = (S + T::QB - 1) / T::QB;
     const int b = blockIdx.x % B;
     const int qb = nqb - 1 - (int)(blockIdx.x / B);

@@ -41,7 +41,8 @@ __global__ __launch_bounds__(256, stage_min_waves(H, DP)) void v4_logits_kernel(
     __shared__ __attribute__((aligned(16))) uint8_t lds0[T::STAGE_BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t lds1[T::STAGE_BYTES];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int nqb = (S + T::QB - 1) / T::QB;
     const int nblk = nqb * B;
     const int G = gridDim.x;
@@ -92,7 +93,24 @@ __global__ __launch_bounds__(256, stage_min_waves(H, DP)) void v4_logits_kernel(
             if constexpr (H >= 8) {
                 // Both halves hold full sums; per pair of column blocks the lower
                 // half writes the first and the upper half the second: 64
-                // consecutive keys per query and store.
+                // consecutive keys per query and store.  (For H >= 8 a slot's
+                // query and range are wave-uniform: a stage inside every range
+                // of the wave stores without per-key checks.)
+                bool inside = pend_s0 + T::KT <= skv;
+#pragma unroll
+                for (int q = 0; q < T::QW; ++q)
+                    inside = inside && tq0 + q < S && lo_s[q] <= pend_s0 && pend_s0 + T::KT <= hi_s[q];
+                if (inside) {
+#pragma unroll
+                    for (int cp = 0; cp < T::NCB / 2; ++cp) {
+                        const int s = pend_s0 + 64 * cp + lane;
+#pragma unroll
+                        for (int q = 0; q < T::QW; ++q)
+                            __builtin_nontemporal_store(pick(hf != 0, pend[2 * cp + 1][q], pend[2 * cp][q]),
+                                                        out_b + (long)(tq0 + q) * skv + s);
+                    }
+                    return;
+                }
 #pragma unroll
                 for (int cp = 0; cp < T::NCB / 2; ++cp) {
                     const int s = pend_s0 + 64 * cp + lane;
@@ -229,7 +247,8 @@ __global__ __launch_bounds__(256, stage_min_waves(H, DP)) void v41_scores_kernel
     __shared__ __attribute__((aligned(16))) uint8_t lds1[T::STAGE_BYTES];
     __shared__ int span_lo, span_hi;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int nqb = (Lq + T::QB - 1) / T::QB;
     const int b = blockIdx.x % B;
     const int qb = nqb - 1 - (int)(blockIdx.x / B);

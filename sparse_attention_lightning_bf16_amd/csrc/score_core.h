@@ -104,7 +104,8 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // Direct global->LDS loads of the key stage starting at s0: each of the stage's
 // NCB*NSTEP fragment blocks is one 64-lane load of 16 bytes per lane, written
-// by the hardware to block base + 16*lane; wave w issues blocks w, w+NWAVE, ...
+// by the hardware to block base + 16*lane; wave w (wave-uniform) issues blocks
+// w, w+NWAVE, ...
 // Lane lp of block (cb, st) fetches key row s0 + 32cb + lp%32, index_dim chunk
 // 2st + lp/32.  Rows past skv are clamped to the last key and chunks past D to
 // the last real chunk, so every access stays inside k; clamped rows only feed
@@ -113,11 +114,30 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 template <class T>
 __device__ __forceinline__ void dma_k_stage(uint8_t* stage, const InLayout& L, const uint16_t* kb, int s0, int skv,
                                             int wave, int lane) {
-    const int rowlim = skv - 1 - s0;                      // uniform
+    static_assert((T::NCB * T::NSTEP) % T::NWAVE == 0, "fragment blocks split evenly over the waves");
+    constexpr int PER_WAVE = T::NCB * T::NSTEP / T::NWAVE;
+    const int rowlim = skv - 1 - s0;                      // uniform (wave is wave-uniform too)
     const int dlim = (L.D >> 3) - 1;
     const uint16_t* base = kb + (long)s0 * L.k_s;         // uniform
+    if (rowlim >= T::KT - 1 && dlim >= 2 * T::NSTEP - 1) {
+        // Whole stage inside k: nothing to clamp, and the lane's part of the
+        // address is the same for every block (a per-block scalar base plus
+        // one lane offset).
+        const uint32_t lane_bytes =
+            2u * (__umul24((uint32_t)(lane & 31), (uint32_t)L.k_s) + 8u * (uint32_t)(lane >> 5));
 #pragma unroll
-    for (int blk = wave; blk < T::NCB * T::NSTEP; blk += T::NWAVE) {
+        for (int i = 0; i < PER_WAVE; ++i) {
+            const int blk = wave + T::NWAVE * i;
+            const int cb = blk / T::NSTEP, st = blk % T::NSTEP;
+            const char* p = reinterpret_cast<const char*>(base + (long)(32 * cb) * L.k_s + 16 * st);
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(p + lane_bytes),
+                                             (lds_ptr_t)(stage + blk * kWave * 16), 16, 0, 0);
+        }
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+        const int blk = wave + T::NWAVE * i;
         const int cb = blk / T::NSTEP, st = blk % T::NSTEP;
         const int row = min(32 * cb + (lane & 31), rowlim);
         const int d8 = min(2 * st + (lane >> 5), dlim);
@@ -140,7 +160,7 @@ __device__ __forceinline__ void stream_key_stages(const InLayout& L, int b, int 
                                                   uint8_t* lds0, uint8_t* lds1, int tid, Body&& body) {
     const uint16_t* kb = L.k + (long)b * L.k_b;
     const int s_first = tile_lo * T::KT;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     dma_k_stage<T>(lds0, L, kb, s_first, skv, wave, lane);
     __syncthreads();
     for (int it = 0; it < ntile; it += 2) {
