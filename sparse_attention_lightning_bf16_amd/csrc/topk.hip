@@ -576,9 +576,9 @@ constexpr int kBinThreads = 256;
 constexpr int kBinChunks = 32;                    // 256-key chunks per row (8192 keys)
 
 struct BinShared {
-    uint32_t hist[kBins];
-    float cand_v[kBinCand];
-    int cand_i[kBinCand];
+    alignas(16) uint32_t hist[kBins];
+    alignas(16) float cand_v[kBinCand];
+    alignas(16) int cand_i[kBinCand];
     int ccnt[kBinChunks];                         // per-chunk counts, row order
     float wmin[4], wmax[4];
     int wtot[4];
@@ -592,8 +592,9 @@ struct BinShared {
 // Block-wide: the bin holding the need-th largest element of hist[0..NB) and
 // the element's 1-based rank inside it, counted from the top, into sh.bstar /
 // sh.rstar.  Thread tid owns bins [BPT*tid, BPT*tid + BPT), read rotated by
-// tid so a wave's reads spread over the LDS banks.  Every thread calls it;
-// it ends with a barrier.  Requires 1 <= need <= sum of hist.
+// tid so a wave's reads spread over the LDS banks; the suffix sums over lanes
+// come from a DPP prefix scan.  Every thread calls it; it ends with a
+// barrier.  Requires 1 <= need <= sum of hist.
 template <int NB>
 __device__ void block_find_bin(BinShared& sh, int need, int tid) {
     constexpr int BPT = NB / kBinThreads;
@@ -602,13 +603,10 @@ __device__ void block_find_bin(BinShared& sh, int need, int tid) {
     int local = 0;
 #pragma unroll
     for (int i = 0; i < BPT; ++i) local += (int)sh.hist[base + ((i + tid) & (BPT - 1))];
-    int v = local;                                   // inclusive suffix sum over lanes >= this one
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int u = __shfl_down(v, off, 64);
-        if (lane + off < 64) v += u;
-    }
-    if (lane == 0) sh.wtot[wv] = v;
+    const int incl = wave_incl_scan(local, lane);
+    const int wsum = __builtin_amdgcn_readlane(incl, 63);
+    const int v = wsum - incl + local;               // inclusive suffix sum over lanes >= this one
+    if (lane == 0) sh.wtot[wv] = wsum;
     __syncthreads();
     int above = v - local;
     for (int w2 = wv + 1; w2 < 4; ++w2) above += sh.wtot[w2];
@@ -624,6 +622,38 @@ __device__ void block_find_bin(BinShared& sh, int need, int tid) {
         }
     }
     __syncthreads();
+}
+
+// One wave: the bin holding the need-th largest element of hist[0..NB) and
+// the element's 1-based rank inside it, counted from the top, into sh.bstar /
+// sh.rstar, in two levels: lane l sums bins [32l, 32l + 32) (16-byte reads,
+// rotated by lane across the LDS banks) and a DPP scan finds the lane whose
+// bins hold it; then lane i < 32 takes that lane's bin i and a second scan
+// finds the bin.  Requires 1 <= need <= sum of hist.
+template <int NB>
+__device__ __forceinline__ void wave_find_bin_lds(BinShared& sh, int need, int lane) {
+    constexpr int BPL = NB / 64;
+    static_assert(BPL == 32, "two levels of 32 bins");
+    int local = 0;
+#pragma unroll
+    for (int i = 0; i < BPL / 4; ++i) {
+        const int k = (i + lane) & (BPL / 4 - 1);
+        const uint4 q = *reinterpret_cast<const uint4*>(&sh.hist[BPL * lane + 4 * k]);
+        local += (int)(q.x + q.y + q.z + q.w);
+    }
+    const int incl = wave_incl_scan(local, lane);
+    const int above = __builtin_amdgcn_readlane(incl, 63) - incl;   // bins of the lanes above this one
+    const unsigned long long m = __ballot(above < need && need <= above + local);
+    const int L = m ? __ffsll((long long)m) - 1 : 0;                  // wave-uniform
+    const int above_l = __builtin_amdgcn_readlane(above, L);
+    const int hb = lane < BPL ? (int)sh.hist[BPL * L + lane] : 0;
+    const int incl2 = wave_incl_scan(hb, lane);
+    const int above_i = above_l + __builtin_amdgcn_readlane(incl2, 63) - incl2;   // bins above bin i of lane L
+    const unsigned long long m2 = __ballot(lane < BPL && above_i < need && need <= above_i + hb);
+    if (m2 && lane == __ffsll((long long)m2) - 1) {
+        sh.bstar = BPL * L + lane;
+        sh.rstar = need - above_i;
+    }
 }
 
 // Number of set bits of mask in lanes below this one, plus acc.
@@ -765,7 +795,8 @@ __global__ __launch_bounds__(kBinThreads) void topk_rows_bin_kernel(const void* 
         vmax = fmaxf(vmax, __shfl_xor(vmax, off, 64));
     }
     if (lane == 0) { sh.wmin[wv] = vmin; sh.wmax[wv] = vmax; }
-    for (int i = tid; i < kBins; i += kBinThreads) sh.hist[i] = 0u;
+#pragma unroll
+    for (int i = 4 * tid; i < kBins; i += 4 * kBinThreads) *reinterpret_cast<uint4*>(&sh.hist[i]) = uint4{0u, 0u, 0u, 0u};
     if (tid == 0) sh.ncand = 0;
     __syncthreads();
     vmin = fminf(fminf(sh.wmin[0], sh.wmin[1]), fminf(sh.wmin[2], sh.wmin[3]));
@@ -778,10 +809,10 @@ __global__ __launch_bounds__(kBinThreads) void topk_rows_bin_kernel(const void* 
     const float c0 = one_fma ? 1.000244140625f - vmin * sc : 1.000244140625f;   // 1 + 2^-12
     // bin_of(one, v): `one` selects the one-fma form at compile time; each
     // pass branches once (uniformly) between the two forms.
-    auto bin_of = [&](auto one, float v) -> int {
-        const float u = decltype(one)::value ? fmaf(v, sc, c0) : fmaf(v - vmin, sc, c0);
-        return (int)((__float_as_uint(u) >> 12) & (uint32_t)(kBins - 1));
+    auto u_bits = [&](auto one, float v) -> uint32_t {
+        return __float_as_uint(decltype(one)::value ? fmaf(v, sc, c0) : fmaf(v - vmin, sc, c0));
     };
+    auto bin_of = [&](auto one, float v) -> int { return (int)((u_bits(one, v) >> 12) & (uint32_t)(kBins - 1)); };
     auto with_form = [&](auto&& f) {
         if (one_fma) f(std::true_type{});
         else f(std::false_type{});
@@ -800,7 +831,8 @@ __global__ __launch_bounds__(kBinThreads) void topk_rows_bin_kernel(const void* 
             });
         });
         __syncthreads();
-        block_find_bin<kBins>(sh, topk, tid);
+        if (wv == 0) wave_find_bin_lds<kBins>(sh, topk, lane);
+        __syncthreads();
         bstar = sh.bstar;
         rstar = sh.rstar;
         cb = (int)sh.hist[bstar];
@@ -816,16 +848,20 @@ __global__ __launch_bounds__(kBinThreads) void topk_rows_bin_kernel(const void* 
         // chunk, the keys in bins above it (all selected); each selected
         // candidate then adds itself to its chunk's count.
         int ccv = 0;                                          // lane j: count of chunk j
+        const uint32_t ub_lo = 0x3f800000u + ((uint32_t)bstar << 12), ub_hi = ub_lo + 4096u;
         with_form([&](auto one) {
             visit_chunks<NCH, AP>(jmax, jpart, [&](int j, auto partial) {
                 int above = 0;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const float v = x[j][m];
-                    const int bn = bin_of(one, v);
+                    // bins compared on the bits of u (in [1, 2)): bin > bstar
+                    // iff bits >= ub_hi, bin == bstar iff ub_lo <= bits < ub_hi
+                    const uint32_t ub = u_bits(one, v);
                     const bool ok = !decltype(partial)::value || v == v;
-                    above += __popcll(__ballot(bn > bstar && ok));
-                    const bool c = bn == bstar && ok;
+                    const bool hi = ub >= ub_hi;
+                    above += __popcll(__ballot(hi && ok));
+                    const bool c = ub >= ub_lo && !hi && ok;
                     const unsigned long long mask = __ballot(c);
                     if (mask != 0ull) {
                         int base = 0;
@@ -844,15 +880,25 @@ __global__ __launch_bounds__(kBinThreads) void topk_rows_bin_kernel(const void* 
         if (lane < jmax) sh.ccnt[4 * lane + wv] = ccv;
         __syncthreads();
         if (tid < cb) {
+            // rank = candidates before this one in (score desc, key asc);
+            // the other candidates are read 8 at a time (broadcast reads)
             const float vi = sh.cand_v[tid];
             const int ii = sh.cand_i[tid];
             int rank = 0, eq = 0;
-            for (int jj = 0; jj < cb; ++jj) {
-                const float vj = sh.cand_v[jj];
-                const int ij = sh.cand_i[jj];
+            auto visit = [&](float vj, int ij) {
                 rank += (vj > vi) || (vj == vi && ij < ii);
                 eq += (vj == vi);
+            };
+            int jj = 0;
+            for (; jj + 8 <= cb; jj += 8) {
+                const float4 va = *reinterpret_cast<const float4*>(&sh.cand_v[jj]);
+                const float4 vb = *reinterpret_cast<const float4*>(&sh.cand_v[jj + 4]);
+                const int4 ia = *reinterpret_cast<const int4*>(&sh.cand_i[jj]);
+                const int4 ib = *reinterpret_cast<const int4*>(&sh.cand_i[jj + 4]);
+                visit(va.x, ia.x); visit(va.y, ia.y); visit(va.z, ia.z); visit(va.w, ia.w);
+                visit(vb.x, ib.x); visit(vb.y, ib.y); visit(vb.z, ib.z); visit(vb.w, ib.w);
             }
+            for (; jj < cb; ++jj) visit(sh.cand_v[jj], sh.cand_i[jj]);
             if (rank == rstar - 1) { sh.cut_v = vi; sh.cut_i = ii; sh.cut_ties = eq > 1; }
             if (rank < rstar) atomicAdd(&sh.ccnt[ii >> 8], 1);
         }
