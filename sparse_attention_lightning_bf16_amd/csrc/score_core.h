@@ -183,7 +183,7 @@ __device__ __forceinline__ bf16x8 b_frag(const uint8_t* stage, int cb, int st, i
 // One stage as a rolling pipeline over its NCB column blocks: each k-step of
 // block c issues its MFMAs and then a slice of the epilogue of block c-1, so
 // the VALU works on finished accumulators while the matrix pipe runs; only
-// the last block's epilogue runs alone.  B fragments are read one k-step
+// the last block's epilogue runs alone.  B fragments are read AHEAD k-steps
 // ahead, across block boundaries.  Scheduling fences keep this order (the
 // compiler would otherwise hoist the epilogue above the MFMAs and stall on
 // results still in flight, or wait for each read right after issuing it).
@@ -195,15 +195,22 @@ __device__ __forceinline__ void rolling_stage(const bf16x8 (&a)[T::NRT][T::NSTEP
                                               Epi&& epi) {
     static_assert(16 % T::NSTEP == 0, "the epilogue splits evenly over k-steps");
     constexpr int PER = 16 / T::NSTEP;                    // elements per row tile per step
+    constexpr int NF = T::NCB * T::NSTEP;                 // fragments per stage, read in order
+    // fragments in flight (one where the wave's A fragments alone fill the
+    // register file: 128 heads x index_dim 256)
+    constexpr int AHEAD = T::NRT * T::NSTEP >= 64 ? 1 : 3;
     f32x16 accp[T::NRT], accc[T::NRT];
-    bf16x8 bn = b_frag<T>(stage, 0, 0, lane);
+    bf16x8 bq[AHEAD];
+#pragma unroll
+    for (int n = 0; n < AHEAD && n < NF; ++n) bq[n] = b_frag<T>(stage, n / T::NSTEP, n % T::NSTEP, lane);
 #pragma unroll
     for (int cb = 0; cb < T::NCB; ++cb) {
 #pragma unroll
         for (int st = 0; st < T::NSTEP; ++st) {
-            const bf16x8 bc = bn;
-            if (st + 1 < T::NSTEP) bn = b_frag<T>(stage, cb, st + 1, lane);
-            else if (cb + 1 < T::NCB) bn = b_frag<T>(stage, cb + 1, 0, lane);
+            const int n = cb * T::NSTEP + st;
+            const bf16x8 bc = bq[n % AHEAD];
+            if (n + AHEAD < NF)
+                bq[n % AHEAD] = b_frag<T>(stage, (n + AHEAD) / T::NSTEP, (n + AHEAD) % T::NSTEP, lane);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int r = 0; r < T::NRT; ++r) accc[r] = mfma_32x32x16(a[r][st], bc, st == 0 ? f32x16{} : accc[r]);
