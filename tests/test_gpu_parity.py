@@ -648,7 +648,8 @@ def test_topk_from_logits_edge_rows_bitwise(Skv):
     # Every size class of the row kernel, with rows that stress each branch:
     # all-equal scores (degenerate range), a few distinct values (large
     # boundary bins), -inf inside the range (non-finite range), signed zeros,
-    # misaligned row starts (ks odd), a crowded boundary bin and ragged ends.
+    # misaligned row starts (ks odd), a crowded boundary bin, scores far from
+    # zero relative to their spread, and ragged ends.
     g = torch.Generator().manual_seed(Skv)
     B, S = 2, 24
     lg = torch.randn(B, S, Skv, generator=g)
@@ -661,6 +662,8 @@ def test_topk_from_logits_edge_rows_bitwise(Skv):
     lg[:, 5] = torch.randn(B, Skv, generator=g) * 1e30      # huge range
     lg[:, 6] = torch.randn(B, Skv, generator=g) * 100.0      # a tight cluster inside a wide range:
     lg[:, 6, : Skv // 2] = 1.0 + torch.randn(B, Skv // 2, generator=g) * 1e-5   # one crowded bin
+    lg[:, 7] = 1000.0 + torch.randn(B, Skv, generator=g) * 0.01   # range far from zero relative to its width
+    lg[:, 8] = -1000.0 + torch.randn(B, Skv, generator=g) * 0.01  # (the row kernel's subtract-first binning)
     ks = torch.randint(0, max(1, Skv // 5), (S,), generator=g, dtype=torch.int32)
     ks[::3] |= 1
     ke = torch.clamp(ks + torch.randint(Skv // 3, Skv + 10, (S,), generator=g, dtype=torch.int32), max=Skv)
