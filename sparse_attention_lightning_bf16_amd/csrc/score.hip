@@ -238,6 +238,26 @@ __device__ __forceinline__ void fill_bf16_neg_inf(uint16_t* __restrict__ p, long
     for (long i = head + 8 * nb + tid; i < n; i += nthreads) p[i] = 0xff80u;
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+
+// acc + bf16(w0 * max(0, bf16(d0))) + bf16(w1 * max(0, bf16(d1))) for two
+// heads of one query: both dots rounded to bf16 by one packed convert (round
+// to nearest even), the ReLU as a packed int16 max with 0 (a bf16 with the
+// sign bit set is a negative int16; -0 becomes +0), the products with the
+// bf16 weights exact in fp32 and rounded by one packed convert, and the two
+// terms added to the fp32 sum by one bf16 dot product with (1, 1).
+__device__ __forceinline__ float v41_pair_terms(float d0, float d1, float w0, float w1, float acc) {
+    const bf16x2 r = __builtin_convertvector(f32x2{d0, d1}, bf16x2);
+    const i16x2 rm = __builtin_elementwise_max(__builtin_bit_cast(i16x2, r), i16x2{0, 0});
+    const uint32_t u = __builtin_bit_cast(uint32_t, rm);
+    const float r0 = __uint_as_float(u << 16), r1 = __uint_as_float(u & 0xffff0000u);
+    const bf16x2 e = __builtin_convertvector(f32x2{w0 * r0, w1 * r1}, bf16x2);
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(e, ones, acc, false);
+}
+
 template <int H, int DP>
 __global__ __launch_bounds__(256, stage_min_waves(H, DP)) void v41_scores_kernel(InLayout L, const uint16_t* __restrict__ wts,
                                                          const uint8_t* __restrict__ allowed, int B, int Lq,
@@ -326,9 +346,19 @@ __global__ __launch_bounds__(256, stage_min_waves(H, DP)) void v41_scores_kernel
                     const float rr = round_bf16(relu(acc_v));    // bf16(d); ReLU commutes with rounding
                     return round_bf16(w_v * rr);                  // exact product, then bf16
                 };
-                rolling_stage<T>(a, stage, lane, [&](int cb, const f32x16 (&acc)[T::NRT], int r, int i) {
-                    part[cb][T::slot(r, i)] += term(acc[r][i], wr[r][i]);
-                });
+                if constexpr (H >= 8) {
+                    // heads in pairs (elements i - 1, i share a query): packed
+                    // roundings and one dot2 add per pair
+                    rolling_stage<T>(a, stage, lane, [&](int cb, const f32x16 (&acc)[T::NRT], int r, int i) {
+                        if (i & 1)
+                            part[cb][T::slot(r, i)] = v41_pair_terms(acc[r][i - 1], acc[r][i], wr[r][i - 1],
+                                                                     wr[r][i], part[cb][T::slot(r, i)]);
+                    });
+                } else {
+                    rolling_stage<T>(a, stage, lane, [&](int cb, const f32x16 (&acc)[T::NRT], int r, int i) {
+                        part[cb][T::slot(r, i)] += term(acc[r][i], wr[r][i]);
+                    });
+                }
                 if constexpr (H >= 8) {
 #pragma unroll
                     for (int cb = 0; cb < T::NCB; ++cb)
