@@ -511,13 +511,16 @@ def test_v41_exact_inputs_bitwise():
     assert np.array_equal(got, want)
 
 
-def test_v41_golden_rounding_cases_on_gpu():
+@pytest.mark.parametrize("min_heads", [1, 8])
+def test_v41_golden_rounding_cases_on_gpu(min_heads):
+    # min_heads = 8 pads each case with zero heads (q = 0, w = 0: each adds an
+    # exact 0), so the cases also run through the paired-head epilogue
     import json
     import os
     g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "v41_rounding.json")))
     D = g["index_dim"]
     for case in g["cases"]:
-        H = len(case["heads"])
+        H = max(len(case["heads"]), min_heads)
         q = torch.zeros(1, 1, H, D)
         w = torch.zeros(1, 1, H)
         for h, hd in enumerate(case["heads"]):
