@@ -181,9 +181,10 @@ __device__ __forceinline__ bf16x8 b_frag(const uint8_t* stage, int cb, int st, i
 }
 
 // One stage as a rolling pipeline over its NCB column blocks: each k-step of
-// block c issues its MFMAs and then a slice of the epilogue of block c-1, so
-// the VALU works on finished accumulators while the matrix pipe runs; only
-// the last block's epilogue runs alone.  B fragments are read AHEAD k-steps
+// block c issues its MFMAs, each followed by a slice of the epilogue of block
+// c-1 (that row tile's elements), so the VALU works on finished accumulators
+// while the matrix pipe runs and the wave has VALU work between its MFMAs;
+// only the last block's epilogue runs alone.  B fragments are read AHEAD k-steps
 // ahead, across block boundaries.  Scheduling fences keep this order (the
 // compiler would otherwise hoist the epilogue above the MFMAs and stall on
 // results still in flight, or wait for each read right after issuing it).
@@ -211,15 +212,17 @@ __device__ __forceinline__ void rolling_stage(const bf16x8 (&a)[T::NRT][T::NSTEP
             const bf16x8 bc = bq[n % AHEAD];
             if (n + AHEAD < NF)
                 bq[n % AHEAD] = b_frag<T>(stage, (n + AHEAD) / T::NSTEP, (n + AHEAD) % T::NSTEP, lane);
-            __builtin_amdgcn_sched_barrier(0);
+            // each row tile's MFMA is followed by that tile's epilogue slice,
+            // so the wave has VALU work to issue while the matrix pipe runs
 #pragma unroll
-            for (int r = 0; r < T::NRT; ++r) accc[r] = mfma_32x32x16(a[r][st], bc, st == 0 ? f32x16{} : accc[r]);
-            __builtin_amdgcn_sched_barrier(0);
-            if (cb > 0) {
-#pragma unroll
-                for (int r = 0; r < T::NRT; ++r)
+            for (int r = 0; r < T::NRT; ++r) {
+                __builtin_amdgcn_sched_barrier(0);
+                accc[r] = mfma_32x32x16(a[r][st], bc, st == 0 ? f32x16{} : accc[r]);
+                __builtin_amdgcn_sched_barrier(0);
+                if (cb > 0) {
 #pragma unroll
                     for (int i = st * PER; i < (st + 1) * PER; ++i) epi(cb - 1, accp, r, i);
+                }
             }
         }
 #pragma unroll
