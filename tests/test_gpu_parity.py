@@ -670,7 +670,7 @@ def test_topk_from_logits_edge_rows_bitwise(Skv):
     ks = torch.randint(0, max(1, Skv // 5), (S,), generator=g, dtype=torch.int32)
     ks[::3] |= 1
     ke = torch.clamp(ks + torch.randint(Skv // 3, Skv + 10, (S,), generator=g, dtype=torch.int32), max=Skv)
-    for tk in (1, 17, min(1000, Skv // 3), min(2048, Skv // 2)):
+    for tk in (1, 17, min(1000, Skv // 3), min(2048, Skv // 2), 3 * Skv // 4):
         log(f"Skv={Skv} topk={tk}")
         sc, ix = lx.topk_from_logits(dev(lg), 1, tk, dev(ks), dev(ke))
         sc, ix = sc.cpu().numpy(), ix.cpu().numpy()
