@@ -108,6 +108,89 @@ __device__ uint32_t wave_select(uint32_t* keys, uint16_t* idx, int cnt, int want
     return T;
 }
 
+// Make room in a full candidate buffer: keys[0..cnt) binned linearly in the
+// score between the smallest and largest (256 bins, monotone); every key in the
+// bins from the one holding the want-th best upward is kept, in index order,
+// and the rest is dropped.  At least want kept keys are strictly above every
+// dropped key, so a later key that is not above the largest dropped one
+// cannot enter the final top-want (ties go to the earlier, lower index): that
+// key becomes the new threshold, returned in *thr.  Returns the kept count,
+// or -1 (buffer untouched) when the boundary bin is so crowded that fewer than
+// `room` slots would be freed; the caller then selects exactly.  Wave-local:
+// `hist` (256 words) belongs to this wave; all 64 lanes call it together.
+__device__ int wave_prune(uint32_t* keys, uint16_t* idx, int cnt, int want, int room, uint32_t* hist, int lane,
+                          uint32_t* thr) {
+    const int nch = (cnt + 63) >> 6;
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
+    for (int c = 0; c < nch; ++c) {
+        const int e = 64 * c + lane;
+        if (e < cnt) { const uint32_t k = keys[e]; kmin = min(kmin, k); kmax = max(kmax, k); }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, 64));
+        kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, 64));
+    }
+    // bins linear in the score (the keys' order is the scores' order)
+    const float vmin = key_to_f32(kmin), span = key_to_f32(kmax) - vmin;
+    if (!(span > 1.0e-30f && span < 3.0e38f)) return -1;      // one value, or a range the scale cannot hold
+    const float sc = 255.0f / span;
+    auto bin_of = [&](uint32_t k) { return min(255, (int)((key_to_f32(k) - vmin) * sc)); };
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hist[4 * lane + i] = 0u;
+    for (int c = 0; c < nch; ++c) {
+        const int e = 64 * c + lane;
+        if (e < cnt) atomicAdd(&hist[bin_of(keys[e])], 1u);
+    }
+    // bin holding the want-th best: lane l owns bins 4l..4l+3
+    int h[4], local = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { h[i] = (int)hist[4 * lane + i]; local += h[i]; }
+    int v = local;                                            // suffix sum over lanes >= this one
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int u = __shfl_down(v, off, 64);
+        if (lane + off < 64) v += u;
+    }
+    int above = v - local, bin = -1, kept = 0;
+    if (above < want && want <= above + local) {
+#pragma unroll
+        for (int i = 3; i >= 0; --i) {
+            if (bin < 0) {
+                if (want <= above + h[i]) { bin = 4 * lane + i; kept = above + h[i]; }
+                else above += h[i];
+            }
+        }
+    }
+    const unsigned long long found = __ballot(bin >= 0);
+    const int src = found ? __ffsll((long long)found) - 1 : 0;
+    bin = __shfl(bin, src, 64);
+    kept = __shfl(kept, src, 64);
+    if (bin < 0 || cnt - kept < room) return -1;
+    // keep bins >= bin in order; the largest dropped key is the new threshold
+    int run = 0;
+    uint32_t dmax = 0u;
+    for (int c = 0; c < nch; ++c) {
+        const int e = 64 * c + lane;
+        const bool valid = e < cnt;
+        const uint32_t k = valid ? keys[e] : 0u;
+        const int id = valid ? (int)idx[e] : 0;
+        const bool keep = valid && bin_of(k) >= bin;
+        if (valid && !keep) dmax = max(dmax, k);
+        const unsigned long long km = __ballot(keep);
+        if (keep) {
+            const int pos = run + lanes_below_f(km, lane);   // <= e: nothing unread is overwritten
+            keys[pos] = k;
+            idx[pos] = (uint16_t)id;
+        }
+        run += __popcll(km);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) dmax = max(dmax, (uint32_t)__shfl_xor((int)dmax, off, 64));
+    *thr = max(*thr, dmax);
+    return run;
+}
+
 template <int H, int DP>
 __global__ __launch_bounds__(256) void v4_fused_topk_kernel(InLayout L, const float* __restrict__ w, int B, int S,
                                                             int skv, int ratio, const int32_t* __restrict__ ks,
@@ -202,8 +285,13 @@ __global__ __launch_bounds__(256) void v4_fused_topk_kernel(InLayout L, const fl
                 bool acc_ok = in_range && key > thr[j];
                 unsigned long long m = __ballot(acc_ok);
                 if (m != 0ull && cnt[j] + __popcll(m) > cap) {
-                    thr[j] = wave_select<false>(bkey[j], bidx[j], cnt[j], topk, hist, lane, nullptr, nullptr);
-                    cnt[j] = topk;
+                    const int kept = wave_prune(bkey[j], bidx[j], cnt[j], topk, kWave, hist, lane, &thr[j]);
+                    if (kept >= 0) {
+                        cnt[j] = kept;
+                    } else {
+                        thr[j] = wave_select<false>(bkey[j], bidx[j], cnt[j], topk, hist, lane, nullptr, nullptr);
+                        cnt[j] = topk;
+                    }
                     acc_ok = in_range && key > thr[j];
                     m = __ballot(acc_ok);
                 }
