@@ -191,13 +191,19 @@ __device__ int wave_prune(uint32_t* keys, uint16_t* idx, int cnt, int want, int 
     return run;
 }
 
+// Key stages of 128 keys for 64 heads (index_dim <= 128; four queries per
+// workgroup), else 64, so that the candidate buffers of the workgroup's
+// queries keep room for topk up to 2048 next to the two stage buffers.
+template <int H, int DP>
+using FusedTiling = Tiling<H, DP, (H == 64 && DP <= 128) ? 128 : 64>;
+
 template <int H, int DP>
 __global__ __launch_bounds__(256) void v4_fused_topk_kernel(InLayout L, const float* __restrict__ w, int B, int S,
                                                             int skv, int ratio, const int32_t* __restrict__ ks,
                                                             const int32_t* __restrict__ ke, int topk, int cap,
                                                             float* __restrict__ scores,
                                                             int32_t* __restrict__ indices) {
-    using T = Tiling<H, DP, 64>;
+    using T = FusedTiling<H, DP>;
     static_assert(H >= 8, "the fused path keeps each query inside one lane pair");
     __shared__ __attribute__((aligned(16))) uint8_t lds0[T::STAGE_BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t lds1[T::STAGE_BYTES];
@@ -275,11 +281,15 @@ __global__ __launch_bounds__(256) void v4_fused_topk_kernel(InLayout L, const fl
 #pragma unroll
                 for (int j = 0; j < T::QW; ++j) part[cb][j] = xor32_add(part[cb][j]);
 
-            // Lane l holds key s0 + l of each of its queries.
-            const int s = s0 + lane;
+            // Per pair of column blocks, lane l holds key s0 + 64 cp + l of each of
+            // its queries (the lower half's sums are block 2cp's, the upper half's
+            // block 2cp+1's); keys are appended in ascending order.
+#pragma unroll
+            for (int cp = 0; cp < T::NCB / 2; ++cp)
 #pragma unroll
             for (int j = 0; j < T::QW; ++j) {
-                const float v = pick(hf != 0, part[1][j], part[0][j]);
+                const int s = s0 + 64 * cp + lane;
+                const float v = pick(hf != 0, part[2 * cp + 1][j], part[2 * cp][j]);
                 const uint32_t key = f32_to_key(v);
                 const bool in_range = (s >= lo_s[j]) && (s < hi_s[j]);
                 bool acc_ok = in_range && key > thr[j];
@@ -332,7 +342,7 @@ __global__ __launch_bounds__(256) void v4_fused_topk_kernel(InLayout L, const fl
 // Largest candidate capacity (multiple of 64) that fits next to the staging tiles.
 template <int H, int DP>
 static int fused_cap(int topk) {
-    using T = Tiling<H, DP, 64>;
+    using T = FusedTiling<H, DP>;
     const long fixed = 2L * T::STAGE_BYTES + T::NWAVE * 256 * 4;
     const long per_entry = (long)T::QB * 6;
     long max_cap = ((kFusedLdsBudget - fixed) / per_entry) & ~63L;
@@ -344,7 +354,7 @@ static int fused_cap(int topk) {
 
 template <int H, int DP>
 static hipError_t launch_fused_t(const FusedArgs& p) {
-    using T = Tiling<H, DP, 64>;
+    using T = FusedTiling<H, DP>;
     const int cap = fused_cap<H, DP>(p.topk);
     if (cap < 0) return hipErrorInvalidValue;
     const size_t dyn = (size_t)T::QB * cap * 6;
