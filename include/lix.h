@@ -39,8 +39,10 @@
  *                                 index_dim not a multiple of 16 or above
  *                                 256, a misaligned pointer, a size whose
  *                                 element count overflows int64 indexing
- *                                 limits, or topk above the fused kernel's
- *                                 on-chip capacity (2048);
+ *                                 limits, batch * index_dim >= 2^24 (the
+ *                                 key row stride of the V4 kernels), or a
+ *                                 shape the fused top-k cannot hold on chip
+ *                                 (see lix_topk);
  *             LIX_ERR_DEVICE      a pointer that is not device memory of
  *                                 the current device (page
  *                                 "...deepseek_v41.indexer", indexer_scores:
@@ -105,7 +107,19 @@ int lix_indexer_logits(const void* q, const void* k, const float* w,
  *
  * logits == NULL: fused path.  Scores are computed from q, k, w (layouts as
  *   in lix_indexer_logits) and selected on chip; no [B,S,Skv] tensor is
- *   written.  topk <= LIX_FUSED_TOPK_MAX.
+ *   written.  The candidates of every query of a workgroup live in LDS, which
+ *   bounds the shapes (LIX_ERR_UNSUPPORTED otherwise; lix_topk_fused_supported
+ *   answers for given sizes):
+ *     heads >= 8 (a query's heads must fill a lane pair of the MFMA tile),
+ *     Skv <= 65536 (key indices are held in 16 bits),
+ *     topk <= LIX_FUSED_TOPK_MAX and topk <= the capacity for (heads,
+ *     index_dim padded to 32/64/128/256):
+ *         heads 8:   704 / 640 / 576 / 384
+ *         heads 16: 1472 / 1408 / 1216 / 896
+ *         heads 32: 2048 / 2048 / 2048 / 1856
+ *         heads 64, 128: 2048.
+ *   Selecting from materialized logits (lix_indexer_logits, then this call
+ *   with logits != NULL) has none of these limits.
  * logits != NULL: selection from a caller-provided fp32 [B,S,Skv] tensor
  *   (for instance the output of lix_indexer_logits); q, k, w, H and D are
  *   ignored and may be NULL / 0.
@@ -122,6 +136,14 @@ int lix_topk(const void* q, const void* k, const float* w, const float* logits,
              int B, int S, int Skv, int H, int D, int compress_ratio,
              const int32_t* ks, const int32_t* ke, int topk,
              float* scores, int32_t* indices, hipStream_t stream);
+
+/*
+ * lix_topk_fused_supported - whether lix_topk's fused path (logits == NULL)
+ * accepts these sizes: 1 if so, 0 if it would return LIX_ERR_UNSUPPORTED or
+ * LIX_ERR_SHAPE for them (limits listed at lix_topk).  Pure host function: no
+ * HIP call, no pointer.
+ */
+int lix_topk_fused_supported(int Skv, int H, int D, int topk);
 
 /*
  * lix_topk_scores - scores at given key indices.
@@ -175,9 +197,11 @@ int lix_indexer_scores_at(const void* q, const void* k, const float* w, const in
  *     dk[i,b,:]   += g * sum_h w[t,b,h] * m_h * q[t,b,h,:]
  * Other entries contribute nothing (their score is the constant -inf,
  * whatever their grad_scores value); a key listed twice contributes twice;
- * the indices get no gradient.  The products take bf16 operands (g rounded
- * for dq; the summed g of a (query, key) pair and w*q rounded for dk) and
- * accumulate in fp32.  dk is a sum over
+ * the indices get no gradient.  Each term of a gradient product carries one
+ * bf16 rounding, as a bf16 autograd graph of the forward would: the upstream
+ * factor is rounded (g for dq, w applied in fp32 afterwards; the summed g of a
+ * (query, key) pair times w_h for dk) and multiplies the exact bf16 k or q;
+ * the products accumulate in fp32.  dk is a sum over
  * queries computed key-major (one partial per 256 keys and 512 queries, added
  * with fp32 atomics), so its low bits may vary from run to run; dq and dw are
  * deterministic.

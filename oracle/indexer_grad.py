@@ -57,10 +57,13 @@ def indexer_backward(q, k, w, indices, grad_scores, ks, ke, with_bounds=False, r
       (the scale of the rounding error of a kernel that forms them in low
       precision and adds them in float32);
     * amb: the part of the output that comes from (head, key) pairs whose d
-      lies within ``2 * D * 2**-24 * sum_i |q_i k_i|`` of 0, where a float32
-      dot product may take the ReLU's other branch; for such a pair the term
-      of dq and dk may be present or absent, and the term of dw is at most
-      that size.
+      lies within ``eps = 2 * D * 2**-24 * sum_i |q_i k_i|`` of 0, where a
+      float32 dot product may take the ReLU's other branch; for such a pair
+      the term of dq and dk may be present or absent, and the term of dw is at
+      most that size.  For dw it also holds sum |g| * eps over every pair: eps
+      bounds the error of a float32 dot product of D exact products summed in
+      any order (at most D - 1 additions, each off by at most 2**-24 of the
+      partial sum), and dw takes d itself, not only its sign.
     """
     S, B, H, D = q.shape
     n_kv = k.shape[0]
@@ -93,9 +96,10 @@ def indexer_backward(q, k, w, indices, grad_scores, ks, ke, with_bounds=False, r
             np.add.at(dk[:, b, :], sel, contrib)
             if with_bounds:
                 ag, aw = np.abs(g), np.abs(wt)
-                amb_pair = (np.abs(d) <= 2.0 * D * 2.0 ** -24 * (np.abs(qt) @ np.abs(ksel).T)).astype(np.float64)
+                eps = 2.0 * D * 2.0 ** -24 * (np.abs(qt) @ np.abs(ksel).T)      # [H, m]
+                amb_pair = (np.abs(d) <= eps).astype(np.float64)
                 mag["dw"][t, b] = np.abs(d) @ ag
-                amb["dw"][t, b] = (amb_pair * np.abs(d)) @ ag
+                amb["dw"][t, b] = (amb_pair * np.abs(d)) @ ag + eps @ ag
                 mag["dq"][t, b] = aw[:, None] * ((m * ag[None, :]) @ np.abs(ksel))
                 amb["dq"][t, b] = aw[:, None] * ((amb_pair * ag[None, :]) @ np.abs(ksel))
                 np.add.at(mag["dk"][:, b, :], sel, ag[:, None] * ((m * aw[:, None]).T @ np.abs(qt)))

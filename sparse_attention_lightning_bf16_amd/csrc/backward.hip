@@ -19,8 +19,8 @@
 //   1. grad_scatter_kernel: the dense upstream gradient G[b,t,s] (sum of g over
 //      the valid entries of (b,t) naming key s), written over each query's
 //      range [ks, ke) only (workspace).
-//   2. qt_fragments_kernel: w_h q_h (bf16) laid out as the B fragments of the
-//      dk product (workspace), so a workgroup can move them into LDS with
+//   2. qt_fragments_kernel: q (bf16, exact) laid out as the B fragments of
+//      the dk product (workspace), so a workgroup can move them into LDS with
 //      direct loads.
 //   3. backward_rows_kernel (query-major, one wave per query, the gathered
 //      32-key blocks of the scores-at kernel): d^T = K Q^T recomputed per block
@@ -31,13 +31,15 @@
 //   4. dk_keys_kernel (key-major): a workgroup owns 256 keys (64 per wave, their
 //      K fragments in registers) and streams the queries that can see them:
 //      per query, q in A-fragment order and its dk fragments are moved into LDS
-//      (double-buffered, one barrier per query), D = Q K^T is recomputed (lanes
-//      are keys, rows heads), and dk += (m G) (w Q) accumulates in registers;
-//      the workgroup's partial is added to dk once at the end.
+//      (three-stage rotation, one barrier per query), D = Q K^T is recomputed
+//      (lanes are keys, rows heads), and dk += bf16(m G w) Q accumulates in
+//      registers; the workgroup's partial is added to dk once at the end.
 //
-// The gradient products take one bfloat16-rounded factor per term (g for dq,
-// G and w q for dk) and accumulate in float32; dw and the final scalings are
-// float32.
+// Every term of a gradient product carries one bfloat16 rounding, the one a
+// bfloat16 autograd graph of the forward makes: the upstream factor is
+// rounded (g for dq, with w applied in float32 at the end; the key's summed g
+// times w_h for dk), the other operand (k for dq, q for dk) is the exact bf16
+// input, and the products accumulate in float32; dw is float32 throughout.
 #include "score_core.h"
 #include "gathered_block.h"
 #include "launch.h"
@@ -49,19 +51,6 @@ namespace {
 constexpr int kBwWaitVmcnt0 = 0x0F70;     // s_waitcnt vmcnt(0), expcnt/lgkmcnt untouched
 constexpr int kKeysPerGroup = 256;        // keys per dk workgroup (64 per wave)
 constexpr int kQueryChunk = 512;          // queries per dk workgroup
-
-template <int H_, int DP_>
-struct BwTiling {
-    static constexpr int H = H_;
-    static constexpr int DP = DP_;
-    static constexpr int NRT = H > 32 ? 2 : 1;       // 32-row head tiles (padded rows are zero)
-    static constexpr int NSTEP = DP / 16;            // k-steps of the recompute over index_dim
-    static constexpr int NDT = DP / 32;              // 32-column index_dim tiles of dq and dk
-    static constexpr int NHS = 2 * NRT;              // 16-head k-steps of the dk product
-    static constexpr int QS_BYTES = NRT * NSTEP * 1024;   // q of one query, A-fragment order
-    static constexpr int QT_BYTES = NHS * NDT * 1024;     // q of one query, dk B-fragment order
-    static_assert(H <= 64 && (DP == 64 || DP == 128), "backward tiles cover H <= 64, index_dim 33..128");
-};
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
     return (uint32_t)bf16_bits(lo) | ((uint32_t)bf16_bits(hi) << 16);
@@ -109,18 +98,18 @@ __global__ __launch_bounds__(256) void grad_scatter_kernel(const int32_t* __rest
 
 // ---------------------------------------------------------------- 2. dk B fragments of q
 
-// Fragment (hs, dt) of query (t, b), lane l, holds bf16(w[head] q[head][32 dt + l%32])
-// for the 8 heads 32(hs/2) + 16(hs%2) + 8(jj/4) + 4(l/32) + jj%4, jj = 0..7: the
-// order in which the dk A operand walks a D accumulator's rows.  Padded heads
-// and index_dim entries >= D are zero.  One wave per (t, b); 1 KiB per fragment.
+// Fragment (hs, dt) of query (t, b), lane l, holds q[head][32 dt + l%32] (the
+// bf16 input bits) for the 8 heads 32(hs/2) + 16(hs%2) + 8(jj/4) + 4(l/32) + jj%4,
+// jj = 0..7: the order in which the dk A operand walks a D accumulator's rows.
+// Padded heads and index_dim entries >= D are zero.  One wave per (t, b);
+// 1 KiB per fragment.
 template <int H, int DP>
-__global__ __launch_bounds__(64) void qt_fragments_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
-                                                          int D, uint8_t* __restrict__ qt) {
+__global__ __launch_bounds__(64) void qt_fragments_kernel(const uint16_t* __restrict__ q, int D,
+                                                          uint8_t* __restrict__ qt) {
     using T = BwTiling<H, DP>;
     const int lane = threadIdx.x, hf = lane >> 5, l32 = lane & 31;
     const long tb = blockIdx.x;                           // t * B + b
     const uint16_t* qrow = q + tb * H * D;
-    const float* wrow = w + tb * H;
     uint8_t* dst = qt + tb * T::QT_BYTES + 16 * lane;
 #pragma unroll
     for (int hs = 0; hs < T::NHS; ++hs)
@@ -136,8 +125,7 @@ __global__ __launch_bounds__(64) void qt_fragments_kernel(const uint16_t* __rest
                     const int jj = 2 * p + u;
                     const int h = 32 * (hs >> 1) + 16 * (hs & 1) + 8 * (jj >> 2) + 4 * hf + (jj & 3);
                     const uint16_t v = qrow[(long)min(h, H - 1) * D + min(d, D - 1)];
-                    const float wq = wrow[min(h, H - 1)] * bf16_to_f32(v);
-                    half[u] = (h < H && d < D) ? (uint32_t)bf16_bits(wq) : 0u;
+                    half[u] = (h < H && d < D) ? (uint32_t)v : 0u;
                 }
                 pk[p] = half[0] | (half[1] << 16);
             }
@@ -345,18 +333,19 @@ __global__ __launch_bounds__(256, 1) void dk_keys_kernel(InLayout L, const float
                                                          int ratio, const int32_t* __restrict__ ks,
                                                          const int32_t* __restrict__ ke, float* __restrict__ dk) {
     using T = BwTiling<H, DP>;
-    // Three stages, each: q in A-fragment order, the query's dk fragments
-    // (w q) and G at the workgroup's 256 keys.
-    constexpr int QS = 0, QT = T::QS_BYTES, GS = QT + T::QT_BYTES;
-    constexpr int STAGE = GS + 4 * kKeysPerGroup;
+    // Three stages, each: q in A-fragment order, q in the dk B-fragment order,
+    // G at the workgroup's 256 keys and one copy of the query's head weights
+    // per wave (64 floats; heads past H repeat w[H-1] and meet zero B rows).
+    constexpr int QS = 0, QT = T::QS_BYTES, GS = QT + T::QT_BYTES, WS = GS + 4 * kKeysPerGroup;
+    constexpr int STAGE = WS + 4 * 4 * 64;
     // Three separate arrays, used in a fixed rotation, so the compiler can tell
     // that loads into one never alias reads of another.
     __shared__ __attribute__((aligned(16))) uint8_t lds0[STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t lds1[STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t lds2[STAGE];
     // Vector-memory operations one wave issues per stage: its share of the q
-    // and fragment blocks and one G load.
-    constexpr int PER_WAVE = (T::NRT * T::NSTEP + T::NHS * T::NDT) / 4 + 1;
+    // and fragment blocks, one G load and one weight load.
+    constexpr int PER_WAVE = (T::NRT * T::NSTEP + T::NHS * T::NDT) / 4 + 2;
     static_assert((T::NRT * T::NSTEP) % 4 == 0 && (T::NHS * T::NDT) % 4 == 0, "blocks split over 4 waves");
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
@@ -394,9 +383,10 @@ __global__ __launch_bounds__(256, 1) void dk_keys_kernel(InLayout L, const float
     // Stage query t (all by direct global->LDS loads): q in A-fragment order
     // (block (r, st), lane l = head 32r + l%32, chunk 2st + l/32; padded heads
     // repeat head H-1 and padded chunks the last real one: they meet zero
-    // fragments or zero K entries), the query's dk fragments, and G at this
+    // fragments or zero K entries), the query's dk fragments, G at this
     // wave's keys (clamped into the query's written range; masked where it is
-    // read).
+    // read) and the query's head weights (lane l: head min(l, H-1)) into the
+    // wave's own copy.
     auto stage = [&](int t, uint8_t* st_base) {
         const uint16_t* qrow = L.q + (long)t * L.q_t + (long)b * L.q_b;
 #pragma unroll
@@ -419,6 +409,9 @@ __global__ __launch_bounds__(256, 1) void dk_keys_kernel(InLayout L, const float
         const int sc = hi > lo ? min(max(sg, lo), hi - 1) : 0;           // a written position
         __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(grow + sc),
                                          (lds_ptr_t)(st_base + GS + 4 * 64 * wave), 4, 0, 0);
+        const float* wrow = w + ((long)t * B + b) * H;
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(wrow + min(lane, H - 1)),
+                                         (lds_ptr_t)(st_base + WS + 4 * 64 * wave), 4, 0, 0);
     };
 
     f32x16 dkacc[2][T::NDT];
@@ -451,14 +444,22 @@ __global__ __launch_bounds__(256, 1) void dk_keys_kernel(InLayout L, const float
 #pragma unroll
                 for (int kc = 0; kc < 2; ++kc) accd[r][kc] = mfma_32x32x16(qa, kf[kc][st], accd[r][kc]);
             }
-        // dk += (m G) (w Q): A = the key's G (bf16) where d > 0, in the order of
-        // D's accumulator rows (contraction over heads); B the query's dk
-        // fragments, each read once for both key halves.
-        const uint32_t gg[2] = {(uint32_t)bf16_bits(g[0]) * 0x10001u, (uint32_t)bf16_bits(g[1]) * 0x10001u};
+        // dk += bf16(m G w) Q: A = the key's G times the head's weight, rounded
+        // to bf16, where d > 0, in the order of D's accumulator rows
+        // (contraction over heads: row i of tile r is head 32r + c_row(i, hf));
+        // B the query's exact q fragments, each read once for both key halves.
+        const float* wl = reinterpret_cast<const float*>(st_base + WS + 4 * 64 * wave);
 #pragma unroll
         for (int r = 0; r < T::NRT; ++r)
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
+                // heads of accumulator rows 8s .. 8s+7: two runs of four
+                float wv[8];
+#pragma unroll
+                for (int g4 = 0; g4 < 2; ++g4) {
+                    const float4 v4 = *reinterpret_cast<const float4*>(wl + 32 * r + 8 * (2 * s + g4) + 4 * hf);
+                    wv[4 * g4 + 0] = v4.x; wv[4 * g4 + 1] = v4.y; wv[4 * g4 + 2] = v4.z; wv[4 * g4 + 3] = v4.w;
+                }
                 bf16x8 af[2];
 #pragma unroll
                 for (int kc = 0; kc < 2; ++kc) {
@@ -466,7 +467,9 @@ __global__ __launch_bounds__(256, 1) void dk_keys_kernel(InLayout L, const float
 #pragma unroll
                     for (int p = 0; p < 4; ++p) {
                         const int i0 = 8 * s + 2 * p;
-                        av[p] = mask_pair(gg[kc], accd[r][kc][i0], accd[r][kc][i0 + 1]);
+                        const float e0 = accd[r][kc][i0] > 0.0f ? g[kc] * wv[2 * p] : 0.0f;
+                        const float e1 = accd[r][kc][i0 + 1] > 0.0f ? g[kc] * wv[2 * p + 1] : 0.0f;
+                        av[p] = pack_bf16(e0, e1);
                     }
                     af[kc] = as_bf16x8(av);
                 }
@@ -527,19 +530,12 @@ __global__ void zero_f32_kernel(float* __restrict__ p, long n4) {
         reinterpret_cast<float4*>(p)[i] = float4{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
-static long g_bytes(int B, int S, int Skv) { return ((long)B * S * Skv * 4 + 255) & ~255L; }
-
-long backward_workspace_bytes(int B, int S, int Skv, int H, int D) {
-    const int nrt = H > 32 ? 2 : 1, ndt = padded_dim(D) / 32;
-    return g_bytes(B, S, Skv) + (long)S * B * (2 * nrt) * ndt * 1024;
-}
-
 template <int H, int DP>
 static hipError_t launch_backward_t(const BackwardArgs& p) {
     InLayout L{static_cast<const uint16_t*>(p.q), (long)p.B * H * p.D, (long)H * p.D,
                static_cast<const uint16_t*>(p.k), (long)p.B * p.D, (long)p.D, p.D};
     float* G = reinterpret_cast<float*>(p.workspace);
-    uint8_t* qtf = reinterpret_cast<uint8_t*>(p.workspace) + g_bytes(p.B, p.S, p.Skv);
+    uint8_t* qtf = reinterpret_cast<uint8_t*>(p.workspace) + backward_g_bytes(p.B, p.S, p.Skv);
     const unsigned rows = (unsigned)((long)p.B * p.S);
     const size_t row_bytes = (size_t)p.Skv * 4;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(grad_scatter_kernel),
@@ -548,7 +544,7 @@ static hipError_t launch_backward_t(const BackwardArgs& p) {
     hipLaunchKernelGGL(grad_scatter_kernel, dim3(rows), dim3(256), row_bytes, p.stream, p.indices, p.grad,
                        p.B, p.S, p.Skv, p.ratio, p.ks, p.ke, p.topk, G);
     hipLaunchKernelGGL((qt_fragments_kernel<H, DP>), dim3(rows), dim3(kWave), 0, p.stream,
-                       static_cast<const uint16_t*>(p.q), p.w, p.D, qtf);
+                       static_cast<const uint16_t*>(p.q), p.D, qtf);
     hipLaunchKernelGGL((backward_rows_kernel<H, DP>), dim3(rows), dim3(kWave), 0, p.stream, L, p.w, p.indices,
                        p.grad, p.B, p.S, p.Skv, p.ratio, p.ks, p.ke, p.topk, p.dq, p.dw);
     const dim3 grid((unsigned)((p.Skv + kKeysPerGroup - 1) / kKeysPerGroup), (unsigned)p.B,

@@ -14,14 +14,22 @@ Test infrastructure.  Tolerances:
 * V4.1 scores: within 2 bf16 ulp of the oracle, or inside the interval the
   oracle derives for float32 accumulation in any order; -inf exactly where
   hidden.
-* Backward (dq, dk, dw): |g - o| <= (2**-7 + 2**-12) * mag + amb + 1e-6,
-  with mag and amb from the oracle: the kernel's gradient GEMMs take up to two
-  bfloat16-rounded factors per term (g for dq; G and w q for dk), each with
-  relative error <= 2**-8 (bf16 keeps 8 significant bits), so a term is off by
-  at most 2 * 2**-8 + 2**-16 of its size, and they add in float32 (<= 2**-24
-  per addition: below 2**-13 of mag for the term counts here); amb covers
-  (head, key) pairs whose dot product a float32 sum may put on the other side
-  of 0.
+* Backward (dq, dk, dw): |g - o| <= (2**-8 + 2**-11) * mag + amb + 1e-6,
+  with mag and amb from the oracle.  Each term of a gradient product carries
+  one bfloat16 rounding, as in a bfloat16 autograd graph of the forward (the
+  upstream factor: g for dq, g * w_h for dk; q and k are the exact bf16
+  inputs): round-to-nearest to 8 significant bits is off by at most 2**-8 of
+  the value.  A few float32 roundings per term (the product g * w_h, the
+  final scaling by w in dq) add at most ~2**-22.  The terms of one output
+  element are summed in float32 in some order; for n terms, the probabilistic
+  bound of Higham and Mary ("A new approach to probabilistic rounding error
+  analysis", SIAM J. Sci. Comput. 41(5), 2019, Theorem 3.1) gives
+  |error| <= lambda * sqrt(n) * 2**-24 * sum |terms| with probability at least
+  1 - 2n exp(-lambda**2 / 2); with lambda = 9 and n <= 2**18 (4096 queries x 64
+  heads into one dk element, the largest count checked element by element)
+  that is 2.8e-4 < 2**-11, failing with probability below 2e-12 per element.
+  amb covers (head, key) pairs whose dot product a float32 sum may put on the
+  other side of 0, and, for dw, the float32 error of each dot product itself.
 """
 
 import numpy as np
@@ -121,7 +129,7 @@ def check_v41(gpu_bits, ora, lo, hi, where=""):
     return int((~near & inside).sum())
 
 
-BACKWARD_REL = 2.0 ** -7 + 2.0 ** -12
+BACKWARD_REL = 2.0 ** -8 + 2.0 ** -11
 
 
 def check_backward_one(got, name, ora, bound, where=""):
