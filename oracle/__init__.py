@@ -13,7 +13,6 @@ holds the backward pass (gradients of the selected scores).
 from .indexer import (  # noqa: F401
     NEG_INF,
     bf16_bits_to_f64,
-    f32_bits_to_f64,
     f64_to_bf16_bits,
     rne_bf16,
     ulp_bf16,

@@ -57,11 +57,6 @@ def bf16_bits_to_f64(bits):
     return u.view(np.float32).astype(np.float64)
 
 
-def f32_bits_to_f64(bits):
-    """float32 bit patterns (uint32) -> float64, exactly."""
-    return np.asarray(bits, dtype=np.uint32).view(np.float32).astype(np.float64)
-
-
 def _f64(a):
     """Exact upcast of an input array to float64 (uint16 means bf16 bits)."""
     a = np.asarray(a)

@@ -8,6 +8,8 @@ from ._lib import LixError, load, status_string, LIB_PATH, LIX_FUSED_TOPK_MAX  #
 from .ops import (  # noqa: F401
     indexer_logits,
     topk,
+    fused_topk_supported,
+    select_topk,
     topk_from_logits,
     topk_scores,
     indexer_scores_at,

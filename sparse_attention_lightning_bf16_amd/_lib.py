@@ -23,6 +23,7 @@ SIGNATURES = {
     "lix_version": (_I, []),
     "lix_indexer_logits": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P]),
     "lix_topk": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P]),
+    "lix_topk_fused_supported": (_I, [_I, _I, _I, _I]),
     "lix_topk_scores": (_I, [_P, _P, _I, _I, _I, _I, _P, _P]),
     "lix_indexer_scores_v41": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
     "lix_indexer_scores_at": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P]),

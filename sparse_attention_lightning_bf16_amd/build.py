@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblix.so")
-SOURCES = ["api.cpp", "score.hip", "topk.hip", "fused.hip", "sparse.hip", "backward.hip"]
+SOURCES = ["api.cpp", "limits.cpp", "score.hip", "topk.hip", "fused.hip", "sparse.hip", "backward.hip"]
 # Units whose MFMA accumulators may live in AGPRs (more than 256 registers of
 # accumulators and operands at one wave per SIMD).
 AGPR_SOURCES = {"backward.hip"}

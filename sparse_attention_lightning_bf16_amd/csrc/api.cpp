@@ -6,7 +6,9 @@
 // device check.
 #include <stdint.h>
 
-#include <hip/hip_runtime.h>
+#include <initializer_list>
+
+#include <hip/hip_runtime_api.h>
 
 #include "lix.h"
 #include "launch.h"
@@ -33,12 +35,22 @@ bool fits(long long a, long long b, long long c = 1, long long d = 1) {
 // One workgroup per row or per query block: the row count must fit a 1-D grid.
 bool rows_fit(int B, int S) { return (long long)B * S <= (1LL << 30); }
 
+// The key-stage loads form key-row offsets as 24-bit products of a row
+// (< 128) and the key row stride B * index_dim: that stride must stay below 2^24.
+bool key_stride_fits(int B, int D) { return (long long)B * D < (1LL << 24); }
+
 int check_dims_v4(int B, int S, int Skv, int H, int D, int ratio, const int32_t* ks, const int32_t* ke) {
     if (B <= 0 || S <= 0 || Skv <= 0 || H <= 0 || D <= 0 || ratio < 1) return LIX_ERR_SHAPE;
     if ((ks == nullptr) != (ke == nullptr)) return LIX_ERR_SHAPE;
     if (!is_pow2_le128(H) || D % 16 != 0 || D > 256) return LIX_ERR_UNSUPPORTED;
     if (!fits(S, B, H, D) || !fits(B, S, Skv) || !fits(Skv, B, D) || !rows_fit(B, S)) return LIX_ERR_UNSUPPORTED;
+    if (!key_stride_fits(B, D)) return LIX_ERR_UNSUPPORTED;
     return LIX_OK;
+}
+
+// Sizes the fused top-k kernel accepts (beyond check_dims_v4).
+bool fused_fits(int Skv, int H, int D, int topk) {
+    return topk >= 1 && topk <= LIX_FUSED_TOPK_MAX && Skv <= lix::kFusedMaxSkv && lix::fused_supported(H, D, topk);
 }
 
 // Every pointer must be device (or managed) memory of the current device.
@@ -125,12 +137,18 @@ int lix_topk(const void* q, const void* k, const float* w, const float* logits, 
     }
     int st = check_dims_v4(B, S, Skv, H, D, compress_ratio, ks, ke);
     if (st != LIX_OK) return st;
-    if (topk > LIX_FUSED_TOPK_MAX || Skv > 65536 || !lix::fused_supported(H, D, topk)) return LIX_ERR_UNSUPPORTED;
+    if (!fused_fits(Skv, H, D, topk)) return LIX_ERR_UNSUPPORTED;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(w, 4)) return LIX_ERR_UNSUPPORTED;
     st = check_device({q, k, w, ks, ke, scores, indices});
     if (st != LIX_OK) return st;
     lix::FusedArgs a{q, k, w, B, S, Skv, H, D, compress_ratio, topk, ks, ke, scores, indices, stream};
     return launch_status(lix::launch_fused_topk(a));
+}
+
+int lix_topk_fused_supported(int Skv, int H, int D, int topk) {
+    if (Skv <= 0 || H <= 0 || D <= 0 || topk < 1 || topk > Skv) return 0;
+    if (!is_pow2_le128(H) || D % 16 != 0 || D > 256) return 0;
+    return fused_fits(Skv, H, D, topk) ? 1 : 0;
 }
 
 int lix_topk_scores(const float* logits, const int32_t* indices, int B, int S, int Skv, int topk, float* scores,

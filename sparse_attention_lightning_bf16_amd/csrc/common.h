@@ -4,13 +4,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "tiling.h"
+
 namespace lix {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kWave = 64;
 
 // 32x32x16 bf16 MFMA (CDNA4).  Operand layout, lane l = 0..63:
 //   A (32 x 16): a[j] = A[l % 32][8 * (l / 32) + j], j = 0..7
@@ -21,9 +21,6 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(const bf16x8& a, const bf16x8& b
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
-
-// Row of the 32x32 C tile held in accumulator slot i by a lane in half `hf` (l / 32).
-__host__ __device__ constexpr int c_row(int i, int hf) { return 8 * (i / 4) + 4 * hf + (i % 4); }
 
 // float <-> order-preserving unsigned key: a < b (as floats) iff key(a) < key(b).
 // -0.0 is folded onto +0.0 so that equal floats have equal keys.

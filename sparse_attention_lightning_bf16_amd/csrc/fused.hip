@@ -21,8 +21,6 @@
 
 namespace lix {
 
-constexpr int kFusedLdsBudget = 160 * 1024;
-
 __device__ __forceinline__ int lanes_below_f(unsigned long long mask, int lane) {
     return __popcll(mask & ((1ull << lane) - 1ull));
 }
@@ -191,12 +189,6 @@ __device__ int wave_prune(uint32_t* keys, uint16_t* idx, int cnt, int want, int 
     return run;
 }
 
-// Key stages of 128 keys for 64 heads (index_dim <= 128; four queries per
-// workgroup), else 64, so that the candidate buffers of the workgroup's
-// queries keep room for topk up to 2048 next to the two stage buffers.
-template <int H, int DP>
-using FusedTiling = Tiling<H, DP, (H == 64 && DP <= 128) ? 128 : 64>;
-
 template <int H, int DP>
 __global__ __launch_bounds__(256) void v4_fused_topk_kernel(InLayout L, const float* __restrict__ w, int B, int S,
                                                             int skv, int ratio, const int32_t* __restrict__ ks,
@@ -339,23 +331,10 @@ __global__ __launch_bounds__(256) void v4_fused_topk_kernel(InLayout L, const fl
     }
 }
 
-// Largest candidate capacity (multiple of 64) that fits next to the staging tiles.
-template <int H, int DP>
-static int fused_cap(int topk) {
-    using T = FusedTiling<H, DP>;
-    const long fixed = 2L * T::STAGE_BYTES + T::NWAVE * 256 * 4;
-    const long per_entry = (long)T::QB * 6;
-    long max_cap = ((kFusedLdsBudget - fixed) / per_entry) & ~63L;
-    long want = ((2L * topk + 63) / 64) * 64;
-    if (want < topk + 64) want = topk + 64;
-    long cap = want < max_cap ? want : max_cap;
-    return cap >= topk + 64 ? (int)cap : -1;
-}
-
 template <int H, int DP>
 static hipError_t launch_fused_t(const FusedArgs& p) {
     using T = FusedTiling<H, DP>;
-    const int cap = fused_cap<H, DP>(p.topk);
+    const long cap = fused_cap<H, DP>(p.topk);
     if (cap < 0) return hipErrorInvalidValue;
     const size_t dyn = (size_t)T::QB * cap * 6;
     auto kern = v4_fused_topk_kernel<H, DP>;
@@ -367,7 +346,7 @@ static hipError_t launch_fused_t(const FusedArgs& p) {
     const int nqb = (p.S + T::QB - 1) / T::QB;
     dim3 grid((unsigned)((long)nqb * p.B));
     hipLaunchKernelGGL(kern, grid, dim3(T::THREADS), dyn, p.stream, L, p.w, p.B, p.S, p.Skv, p.ratio, p.ks, p.ke,
-                       p.topk, cap, p.scores, p.indices);
+                       p.topk, (int)cap, p.scores, p.indices);
     return hipGetLastError();
 }
 
@@ -379,28 +358,6 @@ static hipError_t dispatch_fused_dp(const FusedArgs& p) {
         case 128: return launch_fused_t<H, 128>(p);
         case 256: return launch_fused_t<H, 256>(p);
         default: return hipErrorInvalidValue;
-    }
-}
-
-template <int H>
-static int fused_cap_dp(int D, int topk) {
-    switch (padded_dim(D)) {
-        case 32: return fused_cap<H, 32>(topk);
-        case 64: return fused_cap<H, 64>(topk);
-        case 128: return fused_cap<H, 128>(topk);
-        case 256: return fused_cap<H, 256>(topk);
-        default: return -1;
-    }
-}
-
-int fused_supported(int H, int D, int topk) {
-    switch (H) {
-        case 8: return fused_cap_dp<8>(D, topk) > 0;
-        case 16: return fused_cap_dp<16>(D, topk) > 0;
-        case 32: return fused_cap_dp<32>(D, topk) > 0;
-        case 64: return fused_cap_dp<64>(D, topk) > 0;
-        case 128: return fused_cap_dp<128>(D, topk) > 0;
-        default: return 0;
     }
 }
 

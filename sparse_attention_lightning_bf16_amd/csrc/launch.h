@@ -2,13 +2,12 @@
 // Arguments have been validated by the caller; launchers only enqueue.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
-namespace lix {
+#include "tiling.h"
 
-// index_dim rounded up to the compiled fragment depth (zero-padded in the kernels).
-inline int padded_dim(int D) { return D <= 32 ? 32 : D <= 64 ? 64 : D <= 128 ? 128 : 256; }
+namespace lix {
 
 struct LogitsArgs {
     const void* q;
@@ -100,6 +99,9 @@ struct BackwardArgs {
     void* workspace;          // backward_workspace_bytes(B, S, Skv, H, D) bytes
     hipStream_t stream;
 };
+// Workspace of the backward: G [B,S,Skv] fp32 (rounded up to 256 bytes), then
+// q re-laid for the dk product (backward_qt_bytes per (t, b)).
+long backward_g_bytes(int B, int S, int Skv);
 long backward_workspace_bytes(int B, int S, int Skv, int H, int D);
 hipError_t launch_indexer_backward(const BackwardArgs& p);
 hipError_t launch_topk_rows(const TopkArgs& p);
@@ -109,7 +111,9 @@ hipError_t launch_gather(const GatherArgs& p);
 hipError_t launch_v41_scores(const V41Args& p);
 
 // Nonzero when the fused kernel can hold topk candidates per query on chip
-// for this head count and index_dim.
+// for this head count and index_dim (limits.cpp).
 int fused_supported(int H, int D, int topk);
+// Candidate capacity per query the fused kernel uses (tiling.h, fused_cap).
+long fused_capacity(int H, int D, int topk);
 
 }  // namespace lix

@@ -1,0 +1,45 @@
+// Host-side size limits of the kernels: which shapes the fused top-k keeps
+// on chip, and how much workspace the backward needs.  Plain C++ over the
+// constants of tiling.h (no HIP types), shared by the C ABI's validation and
+// the launchers.
+#include "launch.h"
+
+namespace lix {
+
+namespace {
+
+template <int H>
+long fused_cap_dp(int D, int topk) {
+    switch (padded_dim(D)) {
+        case 32: return fused_cap<H, 32>(topk);
+        case 64: return fused_cap<H, 64>(topk);
+        case 128: return fused_cap<H, 128>(topk);
+        case 256: return fused_cap<H, 256>(topk);
+        default: return -1;
+    }
+}
+
+}  // namespace
+
+long fused_capacity(int H, int D, int topk) {
+    if (topk < 1 || D < 1 || D > 256) return -1;
+    switch (H) {
+        case 8: return fused_cap_dp<8>(D, topk);
+        case 16: return fused_cap_dp<16>(D, topk);
+        case 32: return fused_cap_dp<32>(D, topk);
+        case 64: return fused_cap_dp<64>(D, topk);
+        case 128: return fused_cap_dp<128>(D, topk);
+        default: return -1;   // the fused kernel keeps each query inside one lane pair: H >= 8
+    }
+}
+
+int fused_supported(int H, int D, int topk) { return fused_capacity(H, D, topk) > 0; }
+
+long backward_g_bytes(int B, int S, int Skv) { return ((long)B * S * Skv * 4 + 255) & ~255L; }
+
+long backward_workspace_bytes(int B, int S, int Skv, int H, int D) {
+    const int nrt = H > 32 ? 2 : 1, ndt = padded_dim(D) / 32;
+    return backward_g_bytes(B, S, Skv) + (long)S * B * (2 * nrt) * ndt * 1024;
+}
+
+}  // namespace lix

@@ -16,39 +16,6 @@
 
 namespace lix {
 
-// Keys per LDS stage: 128 where the rolling epilogue pipeline fits two
-// waves per SIMD (H <= 64, index_dim <= 128), else 64.
-constexpr int default_kt(int H, int DP) { return (H <= 64 && DP <= 128) ? 128 : 64; }
-// Waves per SIMD the register allocator is held to for those shapes.
-constexpr int stage_min_waves(int H, int DP) { return (H >= 16 && default_kt(H, DP) == 128) ? 2 : 1; }
-
-template <int H_, int DP_, int KT_ = default_kt(H_, DP_)>
-struct Tiling {
-    static constexpr int H = H_;                    // heads (power of two, <= 128)
-    static constexpr int DP = DP_;                  // index_dim padded up to 32/64/128/256
-    static constexpr int NRT = (H >= 128) ? 4 : 2;  // 32-row MFMA tiles per wave
-    static constexpr int ROWS = 32 * NRT;           // (query, head) rows per wave
-    static constexpr int QW = ROWS / H;             // queries per wave
-    static constexpr int NSTEP = DP / 16;           // MFMA k-steps over index_dim
-    static constexpr int NWAVE = 4;
-    static constexpr int THREADS = NWAVE * kWave;
-    static constexpr int QB = QW * NWAVE;           // queries per workgroup
-    static constexpr int KT = KT_;                  // keys per LDS stage
-    static constexpr int NCB = KT / 32;             // 32-key column blocks per stage
-    static constexpr int STAGE_BYTES = KT * DP * 2;
-    static constexpr int CHUNKS = KT * DP / 8;      // 16-byte chunks per stage
-    static constexpr int CPT = CHUNKS / THREADS;    // chunks staged per thread
-    static constexpr int CPK = DP / 8;              // chunks per key row
-    static_assert(CPT >= 1 && CHUNKS % THREADS == 0, "stage must split evenly over the workgroup");
-    static_assert(ROWS % H == 0, "a wave holds whole queries");
-
-    // Query slot (0..QW-1) of accumulator i of row tile r, for a lane in the
-    // lower half.  For H >= 8 both halves map to the same query; for H < 8
-    // the upper half's query is this slot + 4 / H.
-    static constexpr int slot(int r, int i) { return (32 * r + c_row(i, 0)) / H; }
-    static constexpr int half_step() { return H >= 8 ? 0 : 4 / H; }
-};
-
 // Strides (in elements) of the three input tensors; the head stride of q is D.
 struct InLayout {
     const uint16_t* q;

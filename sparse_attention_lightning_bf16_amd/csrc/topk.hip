@@ -367,7 +367,10 @@ __global__ __launch_bounds__(kRowThreads, MINB) void topk_rows_reg_kernel(
         for (int i = lane; i < kBins + 64; i += 64) sh.hist[i] = 0u;
     }
     const float span = vmax - vmin;
-    const bool binned = span > 0.0f && span < 3.0e38f;       // finite, non-degenerate range
+    // Finite, non-degenerate range whose bin scale kBins / span stays finite
+    // (a span below ~6e-36 would overflow it to inf, and the elements equal to
+    // vmin would then bin as (0 * inf) = NaN); other rows take the radix path.
+    const bool binned = span > 1.0e-30f && span < 3.0e38f;
     const float scale = binned ? (float)kBins / span : 0.0f;
     const int trash = kBins + 64 * wr + lane;
     auto bin_with = [&](float v, float org, float sc) -> int {

@@ -80,7 +80,8 @@ def indexer_logits(q, k, weights, compress_ratio, cu_seqlen_ks=None, cu_seqlen_k
 
 
 def topk(q, k, weights, compress_ratio, topk, logits=None, cu_seqlen_ks=None, cu_seqlen_ke=None):
-    """lix_topk.  With logits=None: fused scoring + top-k from q, k, weights.
+    """lix_topk.  With logits=None: fused scoring + top-k from q, k, weights (within the on-chip limits
+    of include/lix.h; LixError LIX_ERR_UNSUPPORTED beyond them, see fused_topk_supported).
     With logits [B,S,Skv] fp32: top-k of the given logits (q, k, weights may
     be None).  Ranges are causal for compress_ratio unless cu_seqlen_ks/ke
     are given.
@@ -106,6 +107,24 @@ def topk(q, k, weights, compress_ratio, topk, logits=None, cu_seqlen_ks=None, cu
                               indices.data_ptr(), _stream(dev))
     _lib.check(st, "lix_topk")
     return scores, indices
+
+
+def fused_topk_supported(seqlen_kv, heads, index_dim, topk):
+    """lix_topk_fused_supported: whether lix_topk's fused path takes these sizes (the on-chip limits are
+    listed in include/lix.h at lix_topk)."""
+    return bool(_lib.load().lix_topk_fused_supported(int(seqlen_kv), int(heads), int(index_dim), int(topk)))
+
+
+def select_topk(q, k, weights, compress_ratio, topk):
+    """Top-k of the causal indexer scores by whichever route the library offers for these sizes: the
+    fused kernel (lix_topk with no logits) where it holds the candidates on chip, else the
+    materialized route (lix_indexer_logits into a [B,S,Skv] fp32 buffer, then lix_topk over it).
+    Both routes select the same keys and return the same bits."""
+    S, B, H, D, Skv = _v4_shapes(q, k, weights)
+    if fused_topk_supported(Skv, H, D, topk):
+        return globals()["topk"](q, k, weights, compress_ratio, topk)
+    logits = indexer_logits(q, k, weights, compress_ratio)
+    return topk_from_logits(logits, compress_ratio, topk)
 
 
 def topk_from_logits(logits, compress_ratio, k, cu_seqlen_ks=None, cu_seqlen_ke=None):
@@ -186,8 +205,9 @@ class V4IndexerFunction(torch.autograd.Function):
     """Autograd Function of the indexer (page "...tilelang_indexer", class V4IndexerFunction).
 
     forward(index_q, index_k, weights, compress_ratio, topk, topk_indices=None) returns
-    (scores, indices): the top-k of the fused kernel when topk_indices is None, else the scores at
-    topk_indices (returned unchanged as the indices).  backward(grad_scores, grad_indices) gives the
+    (scores, indices): the top-k (select_topk: the fused kernel, or the materialized route for sizes
+    the fused kernel cannot hold on chip) when topk_indices is None, else the scores at topk_indices
+    (returned unchanged as the indices).  backward(grad_scores, grad_indices) gives the
     gradients of q, k and weights through the selected scores (lix_indexer_backward), in their dtypes;
     the indices and the integer arguments get none.
     """
@@ -195,7 +215,7 @@ class V4IndexerFunction(torch.autograd.Function):
     @staticmethod
     def forward(ctx, index_q, index_k, weights, compress_ratio, topk, topk_indices=None):
         if topk_indices is None:
-            scores, indices = globals()["topk"](index_q, index_k, weights, compress_ratio, topk)
+            scores, indices = select_topk(index_q, index_k, weights, compress_ratio, topk)
         else:
             indices = topk_indices
             scores = indexer_scores_at(index_q, index_k, weights, compress_ratio, indices)
@@ -249,7 +269,9 @@ def topk_bf16(scores, topk):
 def v4_lighting_indexer(index_q, index_k, weights, compress_ratio, topk, topk_indices=None):
     """The pages' main entry point (the misspelt name is the pages' own).
 
-    Without topk_indices: fused scoring + top-k, returns (scores, indices).
+    Without topk_indices: scoring + top-k, returns (scores, indices): the fused kernel, or for sizes
+    it cannot hold on chip (heads < 8, seqlen_kv > 65536, topk above the per-head capacity listed in
+    include/lix.h) the materialized logits then the row top-k; both give the same bits.
     With topk_indices [B,S,topk] int32: the scores at those indices, scored
     directly (lix_indexer_scores_at; equal bit for bit to gathering the
     materialized logits), returns scores.  Both go through V4IndexerFunction,

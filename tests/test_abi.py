@@ -27,7 +27,8 @@ def test_library_exports_every_declared_function():
     names = declared_functions()
     assert set(names) == {"lix_status_string", "lix_version", "lix_indexer_logits", "lix_topk",
                           "lix_topk_scores", "lix_indexer_scores_v41", "lix_indexer_scores_at", "lix_topk_bf16",
-                          "lix_indexer_backward", "lix_indexer_backward_workspace_bytes"}
+                          "lix_indexer_backward", "lix_indexer_backward_workspace_bytes",
+                          "lix_topk_fused_supported"}
     for name in names:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES
@@ -52,6 +53,8 @@ def logits_call(q=P, k=P, w=P, B=1, S=8, Skv=2, H=64, D=128, c=4, ks=None, ke=No
     (dict(q=P + 8), UNSUP), (dict(k=P + 2), UNSUP), (dict(w=P + 2), UNSUP), (dict(out=P + 1), UNSUP),
     (dict(ks=P + 1, ke=P), UNSUP),
     (dict(B=1 << 16, S=1 << 16, Skv=1 << 16), UNSUP),
+    (dict(B=131072, S=8, D=128), UNSUP),           # key row stride B * index_dim = 2^24
+    (dict(B=131071, S=8, D=128), DEVICE),          # just below: passes validation
 ])
 def test_indexer_logits_validation(kw, code):
     assert logits_call(**kw) == code
@@ -71,10 +74,46 @@ def topk_call(q=P, k=P, w=P, logits=None, B=1, S=8, Skv=4, H=64, D=128, c=4, ks=
     (dict(Skv=4096, topk=4096), UNSUP),            # fused: above the on-chip capacity
     (dict(H=4), UNSUP),                            # fused path needs heads >= 8
     (dict(Skv=70000, topk=16), UNSUP),             # fused: index above 16 bits
+    (dict(H=8, Skv=4096, topk=1024), UNSUP),       # fused: candidates of 32 queries do not fit in LDS
+    (dict(H=8, Skv=4096, topk=576), DEVICE),       # ... up to the documented capacity
+    (dict(H=8, Skv=4096, topk=577), UNSUP),
+    (dict(H=16, Skv=4096, topk=1217), UNSUP),
+    (dict(H=32, D=256, Skv=4096, topk=1857), UNSUP),
+    (dict(H=64, Skv=4096, topk=2048), DEVICE),
+    (dict(B=131072, S=8, Skv=4, D=128), UNSUP),    # key row stride
     (dict(scores=P + 2), UNSUP), (dict(q=P + 4), UNSUP),
 ])
 def test_topk_validation(kw, code):
     assert topk_call(**kw) == code
+
+
+# (heads, index_dim) -> largest topk of the fused path, as listed in include/lix.h
+FUSED_CAPACITY = {
+    8: {32: 704, 64: 640, 128: 576, 256: 384},
+    16: {32: 1472, 64: 1408, 128: 1216, 256: 896},
+    32: {32: 2048, 64: 2048, 128: 2048, 256: 1856},
+    64: {32: 2048, 64: 2048, 128: 2048, 256: 2048},
+    128: {32: 2048, 64: 2048, 128: 2048, 256: 2048},
+}
+
+
+def test_topk_fused_supported_matches_the_documented_limits_and_validation():
+    lib = lx.load()
+    for H in (1, 2, 4, 8, 16, 32, 64, 128):
+        for D in (16, 32, 48, 64, 128, 256):
+            dp = 32 if D <= 32 else 64 if D <= 64 else 128 if D <= 128 else 256
+            cap = FUSED_CAPACITY.get(H, {}).get(dp, 0)
+            for tk in sorted({1, 64, cap, cap + 1, 2048, 2049}):
+                if tk < 1:
+                    continue
+                want = 1 if 1 <= tk <= cap else 0
+                assert lib.lix_topk_fused_supported(65536, H, D, tk) == want, (H, D, tk)
+                code = topk_call(H=H, D=D, Skv=65536, topk=tk)
+                assert code == (DEVICE if want else UNSUP), (H, D, tk, code)
+    assert lib.lix_topk_fused_supported(65537, 64, 128, 16) == 0
+    assert lib.lix_topk_fused_supported(16, 64, 128, 17) == 0          # topk > Skv
+    assert lib.lix_topk_fused_supported(4096, 48, 128, 16) == 0        # heads not a power of two
+    assert lib.lix_topk_fused_supported(4096, 64, 24, 16) == 0         # index_dim not a multiple of 16
 
 
 def test_topk_from_logits_ignores_q_k_w_shapes():
@@ -122,6 +161,7 @@ def scores_at_call(q=P, k=P, w=P, idx=P, B=1, S=8, Skv=4, H=64, D=128, c=4, ks=N
     (dict(H=48), UNSUP), (dict(D=40), UNSUP), (dict(q=P + 4), UNSUP), (dict(k=P + 8), UNSUP),
     (dict(idx=P + 2), UNSUP), (dict(out=P + 1), UNSUP),
     (dict(B=1 << 16, S=1 << 16, topk=1 << 16), UNSUP),
+    (dict(B=131072, S=2, D=128), UNSUP),           # key row stride B * index_dim = 2^24
 ])
 def test_scores_at_validation(kw, code):
     # topk may exceed Skv here (given indices need not be distinct)
@@ -142,6 +182,7 @@ def backward_call(q=P, k=P, w=P, idx=P, g=P, B=1, S=8, Skv=4, H=64, D=128, c=4, 
     (dict(H=128), UNSUP), (dict(H=48), UNSUP), (dict(D=32), UNSUP), (dict(D=144), UNSUP), (dict(D=40), UNSUP),
     (dict(q=P + 4), UNSUP), (dict(g=P + 2), UNSUP), (dict(dk=P + 4), UNSUP), (dict(dq=P + 2), UNSUP),
     (dict(dw=P + 1), UNSUP), (dict(B=1 << 16, S=1 << 16, topk=1 << 16), UNSUP),
+    (dict(B=262144, S=2, D=64), UNSUP),            # key row stride B * index_dim = 2^24
     (dict(ws=None), NULL), (dict(ws_bytes=1000), SHAPE), (dict(ws=P + 16), UNSUP), (dict(Skv=32769), UNSUP),
 ])
 def test_backward_validation(kw, code):

@@ -667,9 +667,15 @@ def test_topk_from_logits_edge_rows_bitwise(Skv):
     lg[:, 6, : Skv // 2] = 1.0 + torch.randn(B, Skv // 2, generator=g) * 1e-5   # one crowded bin
     lg[:, 7] = 1000.0 + torch.randn(B, Skv, generator=g) * 0.01   # range far from zero relative to its width
     lg[:, 8] = -1000.0 + torch.randn(B, Skv, generator=g) * 0.01  # (the row kernel's subtract-first binning)
+    lg[:, 9] = 0.0                                       # zeros plus two tiny values (set below, inside
+    lg[:, 10] = -3e-38                                   # the range): spans near 1e-37, whose bin scale
+                                                         # would overflow
     ks = torch.randint(0, max(1, Skv // 5), (S,), generator=g, dtype=torch.int32)
     ks[::3] |= 1
     ke = torch.clamp(ks + torch.randint(Skv // 3, Skv + 10, (S,), generator=g, dtype=torch.int32), max=Skv)
+    lg[:, 9, int(ks[9]) + 1] = 1e-37
+    lg[:, 9, int(ke[9]) - 2] = 2e-37
+    lg[:, 10, int(ks[10]) + 3] = 0.0
     for tk in (1, 17, min(1000, Skv // 3), min(2048, Skv // 2), 3 * Skv // 4):
         log(f"Skv={Skv} topk={tk}")
         sc, ix = lx.topk_from_logits(dev(lg), 1, tk, dev(ks), dev(ke))
@@ -678,3 +684,153 @@ def test_topk_from_logits_edge_rows_bitwise(Skv):
             want_s, want_i = oracle.topk_select(lg[b].numpy().astype(np.float64), ks.numpy(), ke.numpy(), tk)
             assert np.array_equal(ix[b], want_i), (Skv, tk, b)
             assert np.array_equal(sc[b].astype(np.float64), want_s), (Skv, tk, b)
+
+
+# ------------------------------------------------------------------ fused top-k: forced branches
+
+def _fused_case(name):
+    """Inputs that drive the fused kernel's candidate buffer through each of its branches.
+
+    Returns (inp, H, D, B, S, Skv, topk, ks, ke) with ks/ke None for causal c=1 ranges.
+    """
+    g = torch.Generator().manual_seed(sum(map(ord, name)))
+    if name == "zero_weights":              # every score +0: the pruning pass sees a zero span
+        inp, _ = v4_case(1, 3000, 2800, 64, 128, seed=400)
+        inp["w"] = torch.zeros_like(inp["w"])
+        return inp, 64, 128, 1, 3000, 2800, 2048, None, None
+    if name == "zero_query_rows":           # every 3rd query all-zero: all-zero rows next to normal ones
+        inp, _ = v4_case(2, 2500, 2400, 64, 128, seed=401)
+        inp["q"][::3] = 0
+        return inp, 64, 128, 2, 2500, 2400, 1500, None, None
+    if name == "duplicate_keys":            # three distinct key rows: a crowded boundary bin everywhere
+        inp, _ = v4_case(1, 3000, 2900, 64, 128, seed=402)
+        pool = inp["k"][:3].clone()
+        inp["k"] = pool[torch.randint(0, 3, (2900,), generator=g)].contiguous()
+        return inp, 64, 128, 1, 3000, 2900, 2048, None, None
+    if name == "small_integers":            # exact small-integer scores: many ties, crowded bins
+        inp, _ = v4_case(1, 3000, 2900, 64, 128, seed=403, exact=True)
+        return inp, 64, 128, 1, 3000, 2900, 2048, None, None
+    if name == "long_rows":                 # 16384 keys per row, topk 2048: the buffer is pruned again and again
+        inp, _ = v4_case(1, 40, 16384, 64, 128, seed=404)
+        ks = torch.zeros(40, dtype=torch.int32)
+        ke = torch.full((40,), 16384, dtype=torch.int32)
+        ke[::5] = torch.randint(8000, 16384, (8,), generator=g, dtype=torch.int32)
+        return inp, 64, 128, 1, 40, 16384, 2048, ks, ke
+    if name == "heads128_topk256":          # capacity 512: frequent pruning
+        inp, _ = v4_case(1, 2000, 3000, 128, 128, seed=405)
+        return inp, 128, 128, 1, 2000, 3000, 256, None, None
+    if name == "heads8_capacity":           # heads 8 at the largest topk its LDS holds
+        inp, _ = v4_case(2, 1500, 3000, 8, 128, seed=406)
+        return inp, 8, 128, 2, 1500, 3000, 576, None, None
+    if name == "given_ranges":              # ks > 0, odd starts, ke < ks, empty rows
+        S, Skv = 900, 2600
+        inp, _ = v4_case(2, S, Skv, 64, 128, seed=407)
+        ks = torch.randint(0, 2000, (S,), generator=g, dtype=torch.int32)
+        ks[::2] |= 1
+        ke = ks + torch.randint(-50, 1500, (S,), generator=g, dtype=torch.int32)
+        ke[::11] = ks[::11]                  # empty
+        ke[5::13] = ks[5::13] - 7            # ke < ks: empty
+        ke[7::17] = 100_000                  # clamped to Skv
+        return inp, 64, 128, 2, S, Skv, 300, ks, ke
+    raise KeyError(name)
+
+
+@pytest.mark.parametrize("name", ["zero_weights", "zero_query_rows", "duplicate_keys", "small_integers", "long_rows",
+                                  "heads128_topk256", "heads8_capacity", "given_ranges"])
+def test_fused_branches_bitwise_vs_materialized_and_oracle(name):
+    inp, H, D, B, S, Skv, tk, ks, ke = _fused_case(name)
+    log(f"fused branch case {name}: H={H} D={D} B={B} S={S} Skv={Skv} topk={tk}")
+    q, k, w = dev(inp["q"]), dev(inp["k"]), dev(inp["w"])
+    kd = None if ks is None else dev(ks)
+    ked = None if ke is None else dev(ke)
+    sc_f, ix_f = lx.topk(q, k, w, 1, tk, cu_seqlen_ks=kd, cu_seqlen_ke=ked)
+    logits = lx.indexer_logits(q, k, w, 1, kd, ked)
+    sc_m, ix_m = lx.topk_from_logits(logits, 1, tk, kd, ked)
+    assert torch.equal(ix_f, ix_m) and torch.equal(sc_f, sc_m), name
+    ksn, ken = ranges(S, Skv, 1, ks, ke)
+    lg = logits.cpu().numpy()
+    for b in range(B):
+        want_s, want_i = oracle.topk_select(lg[b].astype(np.float64), ksn, ken, tk)
+        assert np.array_equal(ix_f[b].cpu().numpy(), want_i), (name, b)
+        assert np.array_equal(sc_f[b].cpu().numpy().astype(np.float64), want_s), (name, b)
+
+
+def test_select_topk_routes_unsupported_fused_shapes_to_the_materialized_path():
+    # heads 4 (no fused kernel) and heads 8 above its capacity: the pages' entry point still answers
+    for H, tk in ((4, 40), (8, 700)):
+        inp, nb = v4_case(1, 400, 1000, H, 64, seed=410 + H)
+        q, k, w = dev(inp["q"]), dev(inp["k"]), dev(inp["w"])
+        assert not lx.fused_topk_supported(1000, H, 64, tk)
+        sc, ix = lx.v4_lighting_indexer(q, k, w, 1, tk)
+        ks, ke = oracle.causal_ranges(400, 1000, 1)
+        rows = np.arange(400)
+        _check_topk_vs_oracle(sc[0].detach().cpu().numpy(), ix[0].cpu().numpy(), nb, 0, rows, ks, ke, tk,
+                              f"select_topk H={H}")
+
+
+# ------------------------------------------------------------------ canaries around every output
+
+def _guarded(n, dtype, fill):
+    buf = torch.full((n + 2048,), fill, dtype=dtype, device=DEV)
+    return buf, buf[1024:1024 + n]
+
+
+def _intact(buf, n, fill):
+    torch.cuda.synchronize()
+    return bool((buf[:1024] == fill).all()) and bool((buf[1024 + n:] == fill).all())
+
+
+def test_every_output_leaves_memory_around_it_untouched():
+    # Each entry point writes into the middle of a larger buffer filled with a
+    # sentinel; the sentinel before and after the output must survive.
+    lib = lx.load()
+    st = torch.cuda.current_stream().cuda_stream
+    B, S, Skv, H, D, c, tk = 2, 77, 50, 64, 128, 1, 20
+    inp, _ = v4_case(B, S, Skv, H, D, seed=420)
+    q, k, w = dev(inp["q"]), dev(inp["k"]), dev(inp["w"])
+    n = B * S * tk
+    logits = lx.indexer_logits(q, k, w, c)
+    idx_given = dev(torch.randint(-2, Skv + 2, (B, S, tk), generator=torch.Generator().manual_seed(421),
+                                  dtype=torch.int32))
+    grad = dev(synth.upstream_gradient(B, S, tk, 422))
+    F, I = 12345.0, 0x5A5A5A5A
+    for route in ("fused", "materialized"):
+        sbuf, so = _guarded(n, torch.float32, F)
+        ibuf, io = _guarded(n, torch.int32, I)
+        lp = None if route == "fused" else logits.data_ptr()
+        rc = lib.lix_topk(q.data_ptr(), k.data_ptr(), w.data_ptr(), lp, B, S, Skv, H, D, c, None, None, tk,
+                          so.data_ptr(), io.data_ptr(), st)
+        assert rc == 0 and _intact(sbuf, n, F) and _intact(ibuf, n, I), route
+    sbuf, so = _guarded(n, torch.float32, F)
+    assert lib.lix_topk_scores(logits.data_ptr(), idx_given.data_ptr(), B, S, Skv, tk, so.data_ptr(), st) == 0
+    assert _intact(sbuf, n, F), "gather"
+    sbuf, so = _guarded(n, torch.float32, F)
+    assert lib.lix_indexer_scores_at(q.data_ptr(), k.data_ptr(), w.data_ptr(), idx_given.data_ptr(), B, S, Skv, H,
+                                     D, c, None, None, tk, so.data_ptr(), st) == 0
+    assert _intact(sbuf, n, F), "scores_at"
+    ws_bytes = lib.lix_indexer_backward_workspace_bytes(B, S, Skv, H, D)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    bufs = {name: _guarded(m, torch.float32, F) for name, m in
+            (("dq", S * B * H * D), ("dk", Skv * B * D), ("dw", S * B * H))}
+    # dk needs 16-byte alignment: the guard of 1024 floats keeps it
+    assert lib.lix_indexer_backward(q.data_ptr(), k.data_ptr(), w.data_ptr(), idx_given.data_ptr(), grad.data_ptr(),
+                                    B, S, Skv, H, D, c, None, None, tk, bufs["dq"][1].data_ptr(),
+                                    bufs["dk"][1].data_ptr(), bufs["dw"][1].data_ptr(), ws.data_ptr(), ws_bytes,
+                                    st) == 0
+    for name, (buf, view) in bufs.items():
+        assert _intact(buf, view.numel(), F), f"backward {name}"
+    vin = synth.v41_inputs(batch=2, local_sequence=70, global_compressed=45, heads=64, index_dim=128, seed=423,
+                           doc_min=10, doc_max=40)
+    vq, vk, vw, va = (dev(vin[x]) for x in ("queries", "keys", "weights", "allowed"))
+    nv = 2 * 70 * 45
+    hb = torch.tensor([0x1234], dtype=torch.int16).view(torch.bfloat16).item()
+    vbuf, vo = _guarded(nv, torch.bfloat16, hb)
+    assert lib.lix_indexer_scores_v41(vq.data_ptr(), vk.data_ptr(), vw.data_ptr(), va.data_ptr(), 2, 70, 45, 64, 128,
+                                      vo.data_ptr(), st) == 0
+    assert _intact(vbuf, nv, hb), "v41"
+    v41 = vo.view(2, 70, 45).clone()
+    nt = 2 * 70 * 9
+    tbuf, to = _guarded(nt, torch.bfloat16, hb)
+    ibuf, io = _guarded(nt, torch.int32, I)
+    assert lib.lix_topk_bf16(v41.data_ptr(), 2, 70, 45, 9, to.data_ptr(), io.data_ptr(), st) == 0
+    assert _intact(tbuf, nt, hb) and _intact(ibuf, nt, I), "topk_bf16"
