@@ -1,6 +1,7 @@
 """Benchmark of the lightning-indexer hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
+                    [--part NAME]
 
 A step is one forward of the V4 lightning indexer on the 32K workload
 (batch 1, seqlen 32768, seqlen_kv 8192, 64 heads, index_dim 128,
@@ -8,23 +9,32 @@ compress_ratio 4, topk 2048): causally masked scoring of every valid
 (query, key) pair plus the per-query top-k.  Two routes compute it and both
 are timed on the same inputs: lix_topk's fused path (no logits in HBM) and
 the materialized path (lix_indexer_logits, then lix_topk over the logits);
-the step is the faster one, named in config.path.  The same run also times
-the gather lix_topk_scores at the selected indices, the direct scoring at
-those indices (lix_indexer_scores_at), the backward of those scores
-(lix_indexer_backward, seeded upstream gradient), lix_indexer_scores_v41 and a top-512 of its
-bf16 scores (lix_topk_bf16) on the V4.1 workload (batch 1, 16384 queries, 4096
-keys, packed documents), a 1 GiB device copy (achievable HBM bandwidth), the
-4K workload cold (L2 and MALL flushed by a 1 GiB write before each call) and
-warm, the fused step on the 131K workload, and a bf16 8192^3 GEMM through
-torch (hipBLASLt) as the achievable dense MFMA rate beside the published one.
+the step is the faster one, named in config.path.  Each timing is the median
+of K launches bracketed by HIP events on the stream the library launches on,
+after W untimed warm-ups; inputs are resident in HBM before timing starts.
+
+The same run also times, in `parts`: both routes cold (L2 and MALL flushed by
+a 1 GiB write before each call, outside the timed region); the gather at the
+selected indices (lix_topk_scores); the direct scoring at those indices
+(lix_indexer_scores_at); the backward of those scores (lix_indexer_backward);
+lix_indexer_scores_v41 and a top-512 of its scores (lix_topk_bf16) on the
+V4.1 workload (batch 1, 16384 queries, 4096 keys, packed documents); and with
+the extras, the achievable peaks on this machine (a pure bf16 MFMA loop and
+streaming copy / read kernels from bench_peaks.hip, a bf16 8192^3 GEMM and a
+1 GiB copy through torch), the 4K workload cold and warm, and the fused step
+on the 131K workload.  `cpu_baseline` times the float64 oracle on bounded
+samples of every workload on the host's cores.
 
 Prints one JSON line.  `value` is causally valid TFLOP/s (2*H*D per visible
-pair) over the whole step; queries/s are reported beside it.  Kernel
-durations come from HIP events on the stream the library launches on.
-Inputs are resident in HBM before timing starts.
+pair) over the whole step; queries/s are reported beside it.
+
+--part NAME launches only one kernel's call in a loop (for profiler runs) and
+prints its median duration: logits, topk, fused, gather, scores_at,
+backward, v41, topk_bf16, copy.
 """
 
 import argparse
+import ctypes
 import json
 import os
 import platform
@@ -37,9 +47,12 @@ import torch
 import synth
 import sparse_attention_lightning_bf16_amd as lx
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "indexer TFLOP/s (causal-valid) + queries/s incl. top-k, 32K ctx, 1 MI355X"
 PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, published
+TRAFFIC_SUMMARY = "profiles/hbm_traffic_32k_workload.md"
+PARTS = ("logits", "topk", "fused", "gather", "scores_at", "backward", "v41", "topk_bf16", "copy")
 
 
 def log(msg):
@@ -51,88 +64,104 @@ def causal_valid_pairs(S, Skv, c):
     return int(np.minimum((p + 1) // c, Skv).sum())
 
 
-class EventTimer:
-    """Average duration of a repeated launch, measured with HIP events on the current stream."""
-
-    def __init__(self):
-        self.pairs = []
-
-    def __enter__(self):
-        self.start = torch.cuda.Event(enable_timing=True)
-        self.end = torch.cuda.Event(enable_timing=True)
-        self.start.record()
-        return self
-
-    def __exit__(self, *exc):
-        self.end.record()
-        self.pairs.append((self.start, self.end))
-
-    def mean_ms(self):
-        torch.cuda.synchronize()
-        return float(np.mean([s.elapsed_time(e) for s, e in self.pairs]))
-
-
-def time_loop(fn, steps, warmup):
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
-    t = EventTimer()
-    wall0 = time.perf_counter()
-    for _ in range(steps):
-        with t:
-            fn()
-    torch.cuda.synchronize()
-    wall = (time.perf_counter() - wall0) * 1e3 / steps
-    return t.mean_ms(), wall
-
-
-def time_each(fn, steps, warmup, between=None):
-    """Mean per-call time with HIP events around each call; `between` runs untimed before each call."""
+def time_calls(fn, steps, warmup, between=None):
+    """Median and mean duration (ms) of `steps` calls of fn, each bracketed by HIP events on torch's
+    current stream (the stream the library launches on); `between` runs untimed before each call."""
     for _ in range(warmup):
         if between is not None:
             between()
         fn()
     torch.cuda.synchronize()
-    t = EventTimer()
+    pairs = []
     for _ in range(steps):
         if between is not None:
             between()
-        with t:
-            fn()
-    return t.mean_ms()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        pairs.append((s, e))
+    torch.cuda.synchronize()
+    ms = np.array([s.elapsed_time(e) for s, e in pairs])
+    return float(np.median(ms)), float(np.mean(ms))
 
 
-def extra_parts(dev, steps, warmup):
-    """Achievable copy bandwidth, the 4K materialized step cold and warm, the 131K fused step."""
+def median_ms(fn, steps, warmup, between=None):
+    return time_calls(fn, steps, warmup, between)[0]
+
+
+# ---------------------------------------------------------------- achievable peaks
+
+def measured_peaks(dev, steps, warmup):
+    """Peaks this box reaches: bench_peaks.so kernels (pure MFMA loop, streaming copy and read) and
+    torch's library GEMM and copy."""
     out = {}
-    # achievable dense bf16 rate on this box: a large library GEMM (hipBLASLt through torch)
+    path = os.path.join(ROOT, "bench_peaks.so")
+    if os.path.exists(path):
+        pk = ctypes.CDLL(path)
+        pk.peak_mfma_flop.restype = ctypes.c_double
+        pk.peak_mfma_flop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        pk.peak_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        pk.peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_long, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_void_p]
+        pk.peak_read.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        st = torch.cuda.current_stream(dev).cuda_stream
+        blocks, iters = 8192, 512
+        sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+        best = 0.0
+        for chains in (4, 8):
+            ms = median_ms(lambda: pk.peak_mfma_bf16(blocks, iters, chains, sink.data_ptr(), st), steps, warmup)
+            best = max(best, pk.peak_mfma_flop(blocks, iters, chains) / ms / 1e9)
+        out["mfma_loop_bf16_tflops"] = best
+        n = 1 << 28                                                      # 1 GiB of fp32
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        best = 0.0
+        for blocks_c in (2048, 8192, 32768):
+            for nt in (0, 1):
+                ms = median_ms(lambda: pk.peak_copy(src.data_ptr(), dst.data_ptr(), n // 4, blocks_c, nt, st),
+                               steps, warmup)
+                best = max(best, 2.0 * n * 4 / ms / 1e6)
+        out["copy_kernel_gbs"] = best                                    # read + write
+        rsink = torch.empty(32768 * 256, dtype=torch.float32, device=dev)
+        best = 0.0
+        for blocks_r in (2048, 8192, 32768):
+            ms = median_ms(lambda: pk.peak_read(src.data_ptr(), n // 4, blocks_r, rsink.data_ptr(), st), steps,
+                           warmup)
+            best = max(best, n * 4 / ms / 1e6)
+        out["read_kernel_gbs"] = best
+        del src, dst, sink, rsink
     a = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
     bm = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
-    gemm_ms = time_each(lambda: torch.matmul(a, bm), steps, warmup)
-    out["gemm_bf16_8192_ms"] = gemm_ms
-    out["gemm_bf16_tflops"] = 2.0 * 8192 ** 3 / gemm_ms / 1e9
+    gemm_ms = median_ms(lambda: torch.matmul(a, bm), steps, warmup)
+    out["gemm_bf16_8192_tflops"] = 2.0 * 8192 ** 3 / gemm_ms / 1e9
     del a, bm
-    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
-    copy_ms = time_each(lambda: dst.copy_(src), steps, warmup)
-    out["copy_1gib_ms"] = copy_ms
-    out["copy_gbs"] = 2.0 * src.numel() * 4 / copy_ms / 1e6             # read + write
-    flush = lambda: dst.fill_(0.0)                                        # 1 GiB write: evicts L2 and MALL
-    del src
+    out["torch_copy_1gib_gbs"] = 2.0 * src.numel() * 4 / median_ms(lambda: dst.copy_(src), steps, warmup) / 1e6
+    return out
 
+
+# ---------------------------------------------------------------- other workloads
+
+def extra_workloads(dev, steps, warmup, flush):
+    """4K materialized and fused steps warm and cold; the 131K fused step."""
+    out = {}
     cfg = synth.WORKLOADS["4k"]
     inp = synth.v4_inputs(**cfg)
     q, k, w = (inp[x].to(dev) for x in "qkw")
     c, tk = cfg["compress_ratio"], cfg["topk"]
     logits = torch.empty(cfg["batch"], cfg["seqlen"], cfg["seqlen_kv"], dtype=torch.float32, device=dev)
+
     def step4k():
         lx.indexer_logits(q, k, w, c, out=logits)
         return lx.topk_from_logits(logits, c, tk)
-    out["4k_materialized_warm_ms"] = time_each(step4k, steps, warmup)
-    out["4k_materialized_cold_ms"] = time_each(step4k, steps, warmup, between=flush)
-    out["4k_fused_warm_ms"] = time_each(lambda: lx.topk(q, k, w, c, tk), steps, warmup)
-    out["4k_fused_cold_ms"] = time_each(lambda: lx.topk(q, k, w, c, tk), steps, warmup, between=flush)
-    del q, k, w, logits, dst
+    out["4k_materialized_warm_ms"] = median_ms(step4k, steps, warmup)
+    out["4k_materialized_cold_ms"] = median_ms(step4k, steps, warmup, between=flush)
+    out["4k_fused_warm_ms"] = median_ms(lambda: lx.topk(q, k, w, c, tk), steps, warmup)
+    out["4k_fused_cold_ms"] = median_ms(lambda: lx.topk(q, k, w, c, tk), steps, warmup, between=flush)
+    del q, k, w, logits
 
     log("timing the 131K fused step")
     cfg = synth.WORKLOADS["131k"]
@@ -140,18 +169,21 @@ def extra_parts(dev, steps, warmup):
     q, k, w = (inp[x].to(dev) for x in "qkw")
     del inp
     c, tk = cfg["compress_ratio"], cfg["topk"]
-    ms = time_each(lambda: lx.topk(q, k, w, c, tk), max(3, steps // 4), 2)
+    ms = median_ms(lambda: lx.topk(q, k, w, c, tk), max(3, steps // 4), 2)
     pairs = cfg["batch"] * causal_valid_pairs(cfg["seqlen"], cfg["seqlen_kv"], c)
     out["131k_fused_ms"] = ms
     out["131k_fused_tflops"] = 2.0 * cfg["heads"] * cfg["index_dim"] * pairs / ms / 1e9
+    out["131k_fused_mfma_frac"] = out["131k_fused_tflops"] / PEAK_BF16_TFLOPS
     out["131k_queries_per_s"] = cfg["batch"] * cfg["seqlen"] / (ms * 1e-3)
     return out
 
 
+# ---------------------------------------------------------------- recorded traffic
+
 def source_digest():
     """sha256 over the library's kernel and ABI sources (csrc/*)."""
     import hashlib
-    root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sparse_attention_lightning_bf16_amd", "csrc")
+    root = os.path.join(ROOT, "sparse_attention_lightning_bf16_amd", "csrc")
     h = hashlib.sha256()
     for name in sorted(os.listdir(root)):
         if name.endswith((".hip", ".h", ".cpp")):
@@ -163,7 +195,7 @@ def source_digest():
 def recorded_traffic(kernel):
     """HBM bytes per launch of `kernel` from the committed FETCH_SIZE/WRITE_SIZE summary, or None when
     that summary was taken on other kernel sources than the ones built here."""
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "indexer_32k_hbm_traffic.md")
+    path = os.path.join(ROOT, TRAFFIC_SUMMARY)
     try:
         lines = open(path).read().splitlines()
     except OSError:
@@ -178,60 +210,115 @@ def recorded_traffic(kernel):
                 return None
             return {"read_bytes": k["read_bytes"], "written_bytes": k["written_bytes"],
                     "total_bytes": k["read_bytes"] + k["written_bytes"],
-                    "algorithmic_bytes": k.get("algorithmic_bytes"), "source": "profiles/indexer_32k_hbm_traffic.md"}
+                    "algorithmic_bytes": k.get("algorithmic_bytes"), "source": TRAFFIC_SUMMARY}
     return None
 
 
-def cpu_baseline(inp, cfg, sample_every):
-    """The float64 oracle on a stratified sample of the workload's query rows."""
+# ---------------------------------------------------------------- CPU oracle
+
+def cpu_baseline(inp32, every32):
+    """The float64 oracle (as it stands) on the host's cores: a stratified sample of the 32K workload's
+    query rows (the headline), and bounded samples of the other workloads."""
     import oracle
     from threadpoolctl import threadpool_info
-    S, Skv, c, tk = cfg["seqlen"], cfg["seqlen_kv"], cfg["compress_ratio"], cfg["topk"]
-    H, D = cfg["heads"], cfg["index_dim"]
-    nb = {x: synth.bits(inp[x]) for x in "qkw"}
-    ks, ke = oracle.causal_ranges(S, Skv, c)
-    rows = np.arange(sample_every - 1, S, sample_every)
+
+    def v4_sample(inp, cfg, rows):
+        S, Skv, c, tk = cfg["seqlen"], cfg["seqlen_kv"], cfg["compress_ratio"], cfg["topk"]
+        nb = {x: synth.bits(inp[x]) for x in "qkw"}
+        ks, ke = oracle.causal_ranges(S, Skv, c)
+        t0 = time.perf_counter()
+        for b in range(cfg["batch"]):
+            lg = oracle.indexer_logits_rows(nb["q"], nb["k"], nb["w"], b, rows, ks, ke)
+            oracle.topk_select(lg, ks[rows], ke[rows], tk)
+        dt = time.perf_counter() - t0
+        flop = 2.0 * cfg["heads"] * cfg["index_dim"] * float(ke[rows].sum()) * cfg["batch"]
+        return {"rows": int(len(rows) * cfg["batch"]), "seconds": dt, "tflops": flop / dt / 1e12,
+                "queries_per_s": len(rows) * cfg["batch"] / dt}
+
+    cfg = synth.WORKLOADS["32k"]
+    rows = np.arange(every32 - 1, cfg["seqlen"], every32)
+    head = v4_sample(inp32, cfg, rows)
+    others = {}
+    cfg1 = synth.WORKLOADS["tiny"]
+    others["tiny (full)"] = v4_sample(synth.v4_inputs(**cfg1), cfg1, np.arange(cfg1["seqlen"]))
+    cfg2 = synth.WORKLOADS["4k"]
+    others["4k (every 8th row)"] = v4_sample(synth.v4_inputs(**cfg2), cfg2, np.arange(7, cfg2["seqlen"], 8))
+    cfg5 = synth.WORKLOADS["131k"]
+    inp5 = synth.v4_inputs(**cfg5)
+    others["131k (every 1024th row)"] = v4_sample(inp5, cfg5, np.arange(1023, cfg5["seqlen"], 1024))
+    del inp5
+    cfgv = synth.WORKLOADS["v41"]
+    vin = synth.v41_inputs(**cfgv)
+    vnb = {x: synth.bits(vin[x]) for x in ("queries", "keys", "weights", "allowed")}
+    vrows = np.arange(63, cfgv["local_sequence"], 64)
     t0 = time.perf_counter()
-    lg = oracle.indexer_logits_rows(nb["q"], nb["k"], nb["w"], 0, rows, ks, ke)
-    oracle.topk_select(lg, ks[rows], ke[rows], tk)
+    oracle.indexer_scores_v41_rows(vnb["queries"], vnb["keys"], vnb["weights"], vnb["allowed"], 0, vrows)
     dt = time.perf_counter() - t0
-    flop = 2.0 * H * D * float(ke[rows].sum())
+    allowed = float(vnb["allowed"][0][vrows].sum())
+    others["v41 (every 64th row)"] = {"rows": int(len(vrows)), "seconds": dt,
+                                      "allowed_tflops": 2.0 * cfgv["heads"] * cfgv["index_dim"] * allowed / dt / 1e12,
+                                      "queries_per_s": len(vrows) / dt}
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {
-        "value": flop / dt / 1e12,
+        "value": head["tflops"],
         "unit": "TFLOP/s",
-        "queries_per_s": len(rows) / dt,
+        "queries_per_s": head["queries_per_s"],
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"{len(rows)} query rows (every {sample_every}th of {S}) of the 32K workload: "
-                   f"float64 logits of each visible key, then top-{tk}; {dt:.1f} s"),
+        "sample": (f"{head['rows']} query rows (every {every32}th of {cfg['seqlen']}) of the 32K workload: "
+                   f"float64 logits of each visible key, then top-{cfg['topk']}; {head['seconds']:.1f} s"),
+        "other_workloads": others,
         "host_cpu": platform.processor() or platform.machine(),
         "os_cpu_count": os.cpu_count(),
     }
 
 
+# ---------------------------------------------------------------- one kernel, for profiler runs
+
 def profile_part(args, dev, q, k, w, cfg):
-    """Launch one kernel only, for profiler runs; prints its mean duration."""
+    """Launch one kernel's call in a loop; prints its median duration."""
     c, tk = cfg["compress_ratio"], cfg["topk"]
     B, S, Skv = cfg["batch"], cfg["seqlen"], cfg["seqlen_kv"]
-    if args.part == "copy":
+    part = args.part
+    if part == "copy":
         # plain device copy of a known size: the reference for scaling HBM counters
-        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
-        ms, _ = time_loop(lambda: dst.copy_(src), args.steps, args.warmup)
-    elif args.part == "v41":
+        fn = lambda: dst.copy_(src)
+    elif part in ("v41", "topk_bf16"):
         vin = synth.v41_inputs(**synth.WORKLOADS["v41"])
         vq, vk, vw, va = (vin[x].to(dev) for x in ("queries", "keys", "weights", "allowed"))
-        ms, _ = time_loop(lambda: lx.indexer_scores_v41(vq, vk, vw, va), args.steps, args.warmup)
+        if part == "v41":
+            fn = lambda: lx.indexer_scores_v41(vq, vk, vw, va)
+        else:
+            v41 = lx.indexer_scores_v41(vq, vk, vw, va)
+            fn = lambda: lx.topk_bf16(v41, 512)
+    elif part == "fused":
+        fn = lambda: lx.topk(q, k, w, c, tk)
     else:
         logits = torch.empty(B, S, Skv, dtype=torch.float32, device=dev)
         lx.indexer_logits(q, k, w, c, out=logits)
-        if args.part == "logits":
-            ms, _ = time_loop(lambda: lx.indexer_logits(q, k, w, c, out=logits), args.steps, args.warmup)
+        if part == "logits":
+            fn = lambda: lx.indexer_logits(q, k, w, c, out=logits)
+        elif part == "topk":
+            fn = lambda: lx.topk_from_logits(logits, c, tk)
         else:
-            ms, _ = time_loop(lambda: lx.topk_from_logits(logits, c, tk), args.steps, args.warmup)
-    print(json.dumps({"part": args.part, "ms": ms, "steps": args.steps, "warmup": args.warmup}), flush=True)
+            _, ix = lx.topk_from_logits(logits, c, tk)
+            if part == "gather":
+                fn = lambda: lx.topk_scores(logits, ix)
+            elif part == "scores_at":
+                del logits
+                fn = lambda: lx.indexer_scores_at(q, k, w, c, ix)
+            else:                                                        # backward
+                del logits
+                g_up = synth.upstream_gradient(B, S, tk, 346).to(dev)
+                fn = lambda: lx.indexer_backward(q, k, w, c, ix, g_up)
+    ms, mean = time_calls(fn, args.steps, args.warmup)
+    print(json.dumps({"part": part, "ms": ms, "mean_ms": mean, "steps": args.steps, "warmup": args.warmup}),
+          flush=True)
 
+
+# ---------------------------------------------------------------- main
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
@@ -240,10 +327,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the copy-bandwidth, 4K cold/warm and 131K fused parts")
-    ap.add_argument("--cpu-sample-every", type=int, default=3)
-    ap.add_argument("--part", choices=["all", "fused", "logits", "topk", "v41", "copy"], default="all",
-                    help="time one kernel only (for profiler runs); the JSON line then covers that part")
+                    help="skip the achievable peaks, the 4K cold/warm and the 131K fused parts")
+    ap.add_argument("--cpu-sample-every", type=int, default=6)
+    ap.add_argument("--part", choices=("all",) + PARTS, default="all",
+                    help="time one kernel's call only (for profiler runs); the JSON line then covers that part")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -267,108 +354,124 @@ def main():
     torch.cuda.synchronize()
     pairs = B * causal_valid_pairs(S, Skv, c)
     flop = 2.0 * H * D * pairs
-
-    # ---- the step: fused scoring + top-k
-    if args.part in ("logits", "topk", "v41", "copy"):
+    if args.part != "all":
         profile_part(args, dev, q, k, w, cfg)
         return
+
+    flush_buf = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    flush = lambda: flush_buf.fill_(0.0)                                 # 1 GiB write: evicts L2 and MALL
+
     log("timing the fused step")
-    fused_ms, _ = time_loop(lambda: lx.topk(q, k, w, c, tk), args.steps, args.warmup)
+    fused_ms, fused_mean = time_calls(lambda: lx.topk(q, k, w, c, tk), args.steps, args.warmup)
     sc_f, ix_f = lx.topk(q, k, w, c, tk)
 
-    parts = {"fused_topk_ms": fused_ms}
-    roof_kernel = {"name": "v4_fused_topk_kernel", "ms": fused_ms}
-    if args.part == "all":
-        log("timing the materialized path")
-        logits = torch.empty(B, S, Skv, dtype=torch.float32, device=dev)
-        def materialized_step():
-            lx.indexer_logits(q, k, w, c, out=logits)
-            return lx.topk_from_logits(logits, c, tk)
-        step_m_ms, _ = time_loop(materialized_step, args.steps, args.warmup)
-        score_ms, _ = time_loop(lambda: lx.indexer_logits(q, k, w, c, out=logits), args.steps, args.warmup)
-        topk_ms, _ = time_loop(lambda: lx.topk_from_logits(logits, c, tk), args.steps, args.warmup)
-        sc_m, ix_m = lx.topk_from_logits(logits, c, tk)
-        same = bool(torch.equal(ix_m, ix_f) and torch.equal(sc_m, sc_f))
-        gather_ms, _ = time_loop(lambda: lx.topk_scores(logits, ix_f), args.steps, args.warmup)
-        # scores at given indices straight from q, k, w (the topk_indices branch of the pages' entry point)
-        at_ms, _ = time_loop(lambda: lx.indexer_scores_at(q, k, w, c, ix_f), args.steps, args.warmup)
-        at_same = bool(torch.equal(lx.indexer_scores_at(q, k, w, c, ix_f), sc_f))
-        at_pairs = int((ix_f >= 0).sum())
-        # algorithmic bytes of the row top-k: read the visible logits, write scores+indices
-        topk_bytes = 4.0 * pairs + 8.0 * B * S * tk
-        logits_bytes = 4.0 * B * S * Skv + 2.0 * B * S * H * D + 4.0 * B * S * H
-        gather_bytes = 4.0 * 2 * B * S * tk + 4.0 * B * S * tk          # idx + value read, scores write
-        parts.update({
-            "materialized_logits_ms": score_ms,
-            "materialized_topk_ms": topk_ms,
-            "materialized_step_ms": step_m_ms,
-            "materialized_sum_of_parts_ms": score_ms + topk_ms,
-            "materialized_scoring_tflops": flop / score_ms / 1e9,
-            "materialized_logits_store_gbs": logits_bytes / score_ms / 1e6,
-            "topk_from_logits_gbs": topk_bytes / topk_ms / 1e6,
-            "topk_from_logits_hbm_frac": topk_bytes / topk_ms / 1e6 / PEAK_HBM_GBS,
-            "topk_bytes": topk_bytes,
-            "gather_ms": gather_ms,
-            "gather_gbs": gather_bytes / gather_ms / 1e6,
-            "fused_equals_materialized": same,
-            "scores_at_ms": at_ms,
-            "scores_at_tflops": 2.0 * H * D * at_pairs / at_ms / 1e9,
-            "scores_at_equals_topk_scores": at_same,
-            "logits_then_gather_ms": score_ms + gather_ms,
-        })
-        del logits
+    log("timing the materialized path")
+    logits = torch.empty(B, S, Skv, dtype=torch.float32, device=dev)
 
-        # backward of the selected scores (lix_indexer_backward) with a seeded upstream gradient
-        log("timing the backward")
-        g_up = synth.upstream_gradient(B, S, tk, 346).to(dev)
-        bw_ms, _ = time_loop(lambda: lx.indexer_backward(q, k, w, c, ix_f, g_up), max(3, args.steps // 4), 2)
-        parts.update({
-            "backward_ms": bw_ms,
-            # algorithmic work: four GEMM passes over the selected entries (d twice, dq, dk)
-            "backward_gemm_tflops": 4 * 2.0 * H * D * at_pairs / bw_ms / 1e9,
-        })
-        del g_up
+    def materialized_step():
+        lx.indexer_logits(q, k, w, c, out=logits)
+        return lx.topk_from_logits(logits, c, tk)
+    step_m_ms, step_m_mean = time_calls(materialized_step, args.steps, args.warmup)
+    score_ms = median_ms(lambda: lx.indexer_logits(q, k, w, c, out=logits), args.steps, args.warmup)
+    topk_ms = median_ms(lambda: lx.topk_from_logits(logits, c, tk), args.steps, args.warmup)
+    sc_m, ix_m = lx.topk_from_logits(logits, c, tk)
+    same = bool(torch.equal(ix_m, ix_f) and torch.equal(sc_m, sc_f))
+    log("timing both routes cold")
+    step_m_cold = median_ms(materialized_step, args.steps, args.warmup, between=flush)
+    fused_cold = median_ms(lambda: lx.topk(q, k, w, c, tk), args.steps, args.warmup, between=flush)
+    gather_ms = median_ms(lambda: lx.topk_scores(logits, ix_f), args.steps, args.warmup)
+    # scores at given indices straight from q, k, w (the topk_indices branch of the pages' entry point)
+    at_ms = median_ms(lambda: lx.indexer_scores_at(q, k, w, c, ix_f), args.steps, args.warmup)
+    at_same = bool(torch.equal(lx.indexer_scores_at(q, k, w, c, ix_f), sc_f))
+    at_pairs = int((ix_f >= 0).sum())
+    # algorithmic bytes: the row top-k reads the visible logits and writes scores + indices; the
+    # scoring kernel reads q, k, w and writes the full [B,S,Skv] logits (the -inf half included)
+    topk_bytes = 4.0 * pairs + 8.0 * B * S * tk
+    logits_bytes = 4.0 * B * S * Skv + 2.0 * B * S * H * D + 2.0 * B * Skv * D + 4.0 * B * S * H
+    gather_bytes = 4.0 * 2 * B * S * tk + 4.0 * B * S * tk           # idx + value read, scores write
+    parts = {
+        "fused_topk_ms": fused_ms,
+        "fused_topk_mean_ms": fused_mean,
+        "fused_topk_cold_ms": fused_cold,
+        "fused_topk_tflops": flop / fused_ms / 1e9,
+        "materialized_step_ms": step_m_ms,
+        "materialized_step_mean_ms": step_m_mean,
+        "materialized_step_cold_ms": step_m_cold,
+        "materialized_logits_ms": score_ms,
+        "materialized_topk_ms": topk_ms,
+        "materialized_sum_of_parts_ms": score_ms + topk_ms,
+        "materialized_scoring_tflops": flop / score_ms / 1e9,
+        "materialized_scoring_mfma_frac": flop / score_ms / 1e9 / PEAK_BF16_TFLOPS,
+        "materialized_logits_store_gbs": logits_bytes / score_ms / 1e6,
+        "topk_from_logits_gbs": topk_bytes / topk_ms / 1e6,
+        "topk_from_logits_hbm_frac": topk_bytes / topk_ms / 1e6 / PEAK_HBM_GBS,
+        "topk_bytes": topk_bytes,
+        "gather_ms": gather_ms,
+        "gather_gbs": gather_bytes / gather_ms / 1e6,
+        "fused_equals_materialized": same,
+        "scores_at_ms": at_ms,
+        "scores_at_tflops": 2.0 * H * D * at_pairs / at_ms / 1e9,
+        "scores_at_equals_topk_scores": at_same,
+        "logits_then_gather_ms": score_ms + gather_ms,
+    }
+    del logits
 
-        log("timing the V4.1 workload")
-        vcfg = synth.WORKLOADS["v41"]
-        vin = synth.v41_inputs(**vcfg)
-        vq, vk, vw, va = (vin[x].to(dev) for x in ("queries", "keys", "weights", "allowed"))
-        v41_ms, _ = time_loop(lambda: lx.indexer_scores_v41(vq, vk, vw, va), args.steps, args.warmup)
-        v41_scores = lx.indexer_scores_v41(vq, vk, vw, va)
-        v41_topk_ms, _ = time_loop(lambda: lx.topk_bf16(v41_scores, 512), args.steps, args.warmup)
-        Lq, G = vcfg["local_sequence"], vcfg["global_compressed"]
-        v41_bytes = (2.0 * Lq * H * D + 2.0 * G * D + 2.0 * Lq * H + 1.0 * Lq * G + 2.0 * Lq * G)
-        allowed_pairs = int(vin["allowed"].sum())
-        parts.update({
-            "v41_ms": v41_ms,
-            "v41_gbs": v41_bytes / v41_ms / 1e6,
-            "v41_hbm_frac": v41_bytes / v41_ms / 1e6 / PEAK_HBM_GBS,
-            "v41_allowed_fraction": allowed_pairs / (Lq * G),
-            "v41_allowed_tflops": 2.0 * H * D * allowed_pairs / v41_ms / 1e9,
-            "v41_topk512_ms": v41_topk_ms,
-            "v41_topk512_gbs": (2.0 * Lq * G + 6.0 * Lq * 512) / v41_topk_ms / 1e6,
-        })
+    # backward of the selected scores (lix_indexer_backward) with a seeded upstream gradient
+    log("timing the backward")
+    g_up = synth.upstream_gradient(B, S, tk, 346).to(dev)
+    bw_ms = median_ms(lambda: lx.indexer_backward(q, k, w, c, ix_f, g_up), max(5, args.steps // 2), 2)
+    parts.update({
+        "backward_ms": bw_ms,
+        # algorithmic work: four GEMM passes over the selected entries (d twice, dq, dk)
+        "backward_gemm_tflops": 4 * 2.0 * H * D * at_pairs / bw_ms / 1e9,
+    })
+    del g_up
 
-        if not args.no_extra:
-            log("timing a library GEMM, copy bandwidth and the 4K workload")
-            parts.update(extra_parts(dev, args.steps, args.warmup))
-            parts["topk_frac_of_copy"] = topk_bytes / topk_ms / 1e6 / parts["copy_gbs"]
+    log("timing the V4.1 workload")
+    vcfg = synth.WORKLOADS["v41"]
+    vin = synth.v41_inputs(**vcfg)
+    vq, vk, vw, va = (vin[x].to(dev) for x in ("queries", "keys", "weights", "allowed"))
+    v41_ms = median_ms(lambda: lx.indexer_scores_v41(vq, vk, vw, va), args.steps, args.warmup)
+    v41_scores = lx.indexer_scores_v41(vq, vk, vw, va)
+    v41_topk_ms = median_ms(lambda: lx.topk_bf16(v41_scores, 512), args.steps, args.warmup)
+    Lq, G = vcfg["local_sequence"], vcfg["global_compressed"]
+    v41_bytes = (2.0 * Lq * H * D + 2.0 * G * D + 2.0 * Lq * H + 1.0 * Lq * G + 2.0 * Lq * G)
+    allowed_pairs = int(vin["allowed"].sum())
+    parts.update({
+        "v41_ms": v41_ms,
+        "v41_bytes": v41_bytes,
+        "v41_gbs": v41_bytes / v41_ms / 1e6,
+        "v41_hbm_frac": v41_bytes / v41_ms / 1e6 / PEAK_HBM_GBS,
+        "v41_allowed_fraction": allowed_pairs / (Lq * G),
+        "v41_allowed_tflops": 2.0 * H * D * allowed_pairs / v41_ms / 1e9,
+        "v41_topk512_ms": v41_topk_ms,
+        "v41_topk512_gbs": (2.0 * Lq * G + 6.0 * Lq * 512) / v41_topk_ms / 1e6,
+    })
+    del vq, vk, vw, va, v41_scores
+
+    measured = {}
+    if not args.no_extra:
+        log("timing the achievable peaks, the 4K workload and the 131K fused step")
+        measured = measured_peaks(dev, args.steps, args.warmup)
+        parts.update(extra_workloads(dev, args.steps, args.warmup, flush))
+        if "copy_kernel_gbs" in measured:
+            parts["topk_frac_of_copy_kernel"] = parts["topk_from_logits_gbs"] / measured["copy_kernel_gbs"]
+        if "mfma_loop_bf16_tflops" in measured:
+            parts["scoring_frac_of_mfma_loop"] = parts["materialized_scoring_tflops"] / measured[
+                "mfma_loop_bf16_tflops"]
+    del flush_buf
 
     # The step is the faster of the two routes to the same forward; both are reported.
-    if args.part == "all" and parts["materialized_step_ms"] < fused_ms:
-        step_ms = parts["materialized_step_ms"]
+    if step_m_ms < fused_ms:
+        step_ms = step_m_ms
         path = "materialized: lix_indexer_logits then lix_topk over the logits"
-        roof_kernel = {"name": "v4_logits_kernel", "ms": parts["materialized_logits_ms"]}
+        roof_kernel = {"name": "v4_logits_kernel", "ms": score_ms}
     else:
         step_ms = fused_ms
         path = "fused: lix_topk scoring and selecting on chip"
+        roof_kernel = {"name": "v4_fused_topk_kernel", "ms": fused_ms}
     value = flop / step_ms / 1e9
     achieved = flop / roof_kernel["ms"] / 1e9
-    traffic = recorded_traffic(roof_kernel["name"])
-    measured = {}
-    if "gemm_bf16_tflops" in parts:
-        measured = {"gemm_bf16_tflops": parts["gemm_bf16_tflops"], "copy_gbs": parts["copy_gbs"],
-                    "frac_of_gemm": achieved / parts["gemm_bf16_tflops"]}
     result = {
         "metric": METRIC,
         "value": value,
@@ -384,16 +487,16 @@ def main():
         "data": "synthetic",
         "config": {"workload": "32k lightning-indexer forward (scoring + top-k)", "path": path, "batch": B,
                    "seqlen": S, "seqlen_kv": Skv, "heads": H, "index_dim": D, "compress_ratio": c,
-                   "topk": tk, "causal_valid_pairs": pairs},
+                   "topk": tk, "causal_valid_pairs": pairs, "timing": f"median of {args.steps} HIP-event pairs"},
         "queries_per_s": B * S / (step_ms * 1e-3),
         "roofline": {"bound": "mfma", "kernel": roof_kernel["name"], "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": traffic, "measured_peaks": measured},
+                     "traffic": recorded_traffic(roof_kernel["name"]), "measured_peaks": measured},
         "parts": parts,
     }
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle sample")
-        result["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_sample_every)
+        log("timing the CPU oracle samples")
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_every)
     print(json.dumps(result), flush=True)
 
 
