@@ -234,6 +234,30 @@ int lix_indexer_backward(const void* q, const void* k, const float* w, const int
 long long lix_indexer_backward_workspace_bytes(int B, int S, int Skv, int H, int D);
 
 /*
+ * lix_indexer_backward_noalloc - lix_indexer_backward without a workspace
+ * argument and without any allocation.
+ *
+ * For callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving or training loops, harnesses that
+ * forbid hipMalloc.  Same arguments, semantics, outputs and errors as
+ * lix_indexer_backward, minus workspace / workspace_bytes: the workspace is a
+ * static device array of LIX_NOALLOC_SCRATCH_BYTES bytes that each GPU the
+ * library runs on holds until the process ends (its device address is looked
+ * up once per device).  Sizes whose workspace
+ * (lix_indexer_backward_workspace_bytes) exceeds LIX_NOALLOC_SCRATCH_BYTES:
+ * LIX_ERR_UNSUPPORTED.  The call allocates nothing and frees nothing.  Every
+ * call on one GPU uses the same array and leaves its contents behind (nothing
+ * in it needs to start at zero): calls that overlap on one GPU (concurrent
+ * streams or threads) race and are not allowed; calls ordered on one stream
+ * are fine.
+ */
+#define LIX_NOALLOC_SCRATCH_BYTES (64L << 20)
+int lix_indexer_backward_noalloc(const void* q, const void* k, const float* w, const int32_t* indices,
+                                 const float* grad_scores, int B, int S, int Skv, int H, int D,
+                                 int compress_ratio, const int32_t* ks, const int32_t* ke, int topk,
+                                 float* dq, float* dk, float* dw, hipStream_t stream);
+
+/*
  * lix_indexer_scores_v41 - V4.1 BF16-rounded scores with a visibility mask.
  *
  * Page "...deepseek_v41.indexer", module description (the GEMM output and

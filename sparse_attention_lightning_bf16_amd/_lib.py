@@ -13,6 +13,7 @@ LIX_ERR_UNSUPPORTED = -3
 LIX_ERR_DEVICE = -4
 LIX_ERR_LAUNCH = -5
 LIX_FUSED_TOPK_MAX = 2048
+LIX_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # Symbols exported by liblix.so, with their C signatures (include/lix.h).
 _P = ctypes.c_void_p
@@ -31,6 +32,8 @@ SIGNATURES = {
     "lix_indexer_backward": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P, _P, _LL,
                                   _P]),
     "lix_indexer_backward_workspace_bytes": (_LL, [_I, _I, _I, _I, _I]),
+    "lix_indexer_backward_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P,
+                                          _P]),
 }
 
 _lib = None

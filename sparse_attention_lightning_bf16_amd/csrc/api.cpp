@@ -204,6 +204,27 @@ int lix_indexer_backward(const void* q, const void* k, const float* w, const int
     return launch_status(lix::launch_indexer_backward(a));
 }
 
+int lix_indexer_backward_noalloc(const void* q, const void* k, const float* w, const int32_t* indices,
+                                 const float* grad_scores, int B, int S, int Skv, int H, int D, int compress_ratio,
+                                 const int32_t* ks, const int32_t* ke, int topk, float* dq, float* dk, float* dw,
+                                 hipStream_t stream) {
+    if (!q || !k || !w || !indices || !grad_scores || !dq || !dk || !dw) return LIX_ERR_NULL;
+    int st = check_dims_backward(B, S, Skv, H, D, compress_ratio, ks, ke, topk);
+    if (st != LIX_OK) return st;
+    if (lix::backward_workspace_bytes(B, S, Skv, H, D) > (long)LIX_NOALLOC_SCRATCH_BYTES) return LIX_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(w, 4) || !aligned(indices, 4) || !aligned(grad_scores, 4) ||
+        !aligned(dq, 4) || !aligned(dk, 16) || !aligned(dw, 4) || !aligned(ks, 4) || !aligned(ke, 4))
+        return LIX_ERR_UNSUPPORTED;
+    st = check_device({q, k, w, indices, grad_scores, dq, dk, dw, ks, ke});
+    if (st != LIX_OK) return st;
+    void* ws = nullptr;
+    long ws_bytes = 0;
+    if (lix::noalloc_workspace(&ws, &ws_bytes) != hipSuccess) return LIX_ERR_DEVICE;
+    lix::BackwardArgs a{q, k, w, indices, grad_scores, B, S, Skv, H, D, compress_ratio, topk, ks, ke, dq, dk, dw,
+                        ws, stream};
+    return launch_status(lix::launch_indexer_backward(a));
+}
+
 int lix_topk_bf16(const void* scores, int B, int L, int G, int topk, void* out_scores, int32_t* indices,
                   hipStream_t stream) {
     if (!scores || !out_scores || !indices) return LIX_ERR_NULL;

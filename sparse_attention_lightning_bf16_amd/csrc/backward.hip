@@ -40,9 +40,12 @@
 // rounded (g for dq, with w applied in float32 at the end; the key's summed g
 // times w_h for dk), the other operand (k for dq, q for dk) is the exact bf16
 // input, and the products accumulate in float32; dw is float32 throughout.
+#include <mutex>
+
 #include "score_core.h"
 #include "gathered_block.h"
 #include "launch.h"
+#include "lix.h"
 
 namespace lix {
 
@@ -561,6 +564,37 @@ static hipError_t dispatch_dp_backward(const BackwardArgs& p) {
         case 128: return launch_backward_t<H, 128>(p);
         default: return hipErrorInvalidValue;
     }
+}
+
+// ---------------------------------------------------------------- allocation-free workspace
+
+// The workspace of lix_indexer_backward_noalloc: one static device array,
+// which every GPU the library runs on holds (its own copy) until the process
+// ends.  In host code `scratch` names a host-side stand-in, not device
+// memory: the launchers only ever receive the device address that
+// hipGetSymbolAddress returns for the current device, taken once per device.
+static __device__ __align__(256) uint8_t scratch[LIX_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+hipError_t noalloc_workspace(void** ptr, long* bytes) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    *bytes = LIX_NOALLOC_SCRATCH_BYTES;
+    return hipSuccess;
 }
 
 hipError_t launch_indexer_backward(const BackwardArgs& p) {

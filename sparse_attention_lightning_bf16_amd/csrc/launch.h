@@ -104,6 +104,9 @@ struct BackwardArgs {
 long backward_g_bytes(int B, int S, int Skv);
 long backward_workspace_bytes(int B, int S, int Skv, int H, int D);
 hipError_t launch_indexer_backward(const BackwardArgs& p);
+// Device address and size of the current device's static backward workspace
+// (lix_indexer_backward_noalloc); taken with hipGetSymbolAddress once per device.
+hipError_t noalloc_workspace(void** ptr, long* bytes);
 hipError_t launch_topk_rows(const TopkArgs& p);
 hipError_t launch_topk_bf16(const TopkBf16Args& p);
 hipError_t launch_fused_topk(const FusedArgs& p);

@@ -23,5 +23,6 @@ hipError_t launch_topk_bf16(const TopkBf16Args&) { return reached("launch_topk_b
 hipError_t launch_fused_topk(const FusedArgs&) { return reached("launch_fused_topk"); }
 hipError_t launch_gather(const GatherArgs&) { return reached("launch_gather"); }
 hipError_t launch_v41_scores(const V41Args&) { return reached("launch_v41_scores"); }
+hipError_t noalloc_workspace(void**, long*) { return reached("noalloc_workspace"); }
 
 }  // namespace lix

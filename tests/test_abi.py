@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == {"lix_status_string", "lix_version", "lix_indexer_logits", "lix_topk",
                           "lix_topk_scores", "lix_indexer_scores_v41", "lix_indexer_scores_at", "lix_topk_bf16",
                           "lix_indexer_backward", "lix_indexer_backward_workspace_bytes",
-                          "lix_topk_fused_supported"}
+                          "lix_topk_fused_supported", "lix_indexer_backward_noalloc"}
     for name in names:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES
@@ -222,3 +222,30 @@ def test_python_binding_rejects_bad_tensors_before_the_library():
         lx.indexer_logits(q, k, w, 4)
     with pytest.raises(TypeError):
         lx.indexer_logits(q.float(), k, w, 4)
+
+
+def backward_noalloc_call(q=P, k=P, w=P, idx=P, g=P, B=1, S=8, Skv=4, H=64, D=128, c=4, ks=None, ke=None, topk=2,
+                          dq=P, dk=P, dw=P):
+    return lx.load().lix_indexer_backward_noalloc(q, k, w, idx, g, B, S, Skv, H, D, c, ks, ke, topk, dq, dk, dw,
+                                                  None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(idx=None), NULL), (dict(g=None), NULL), (dict(dk=None), NULL),
+    (dict(B=0), SHAPE), (dict(topk=0), SHAPE), (dict(ke=P), SHAPE),
+    (dict(H=128), UNSUP), (dict(D=32), UNSUP), (dict(dk=P + 4), UNSUP), (dict(Skv=32769), UNSUP),
+    # workspace above the static array: G alone is 1 GiB here
+    (dict(B=1, S=32768, Skv=8192), UNSUP),
+    (dict(B=1, S=1024, Skv=1024), DEVICE),       # 4 MiB + 16 MiB: fits, stops at the device check
+])
+def test_backward_noalloc_validation(kw, code):
+    assert backward_noalloc_call(**kw) == code
+
+
+def test_backward_noalloc_limit_matches_the_workspace_size():
+    lib = lx.load()
+    cap = _lib.LIX_NOALLOC_SCRATCH_BYTES
+    assert lib.lix_indexer_backward_workspace_bytes(1, 2048, 2048, 64, 128) <= cap
+    assert backward_noalloc_call(B=1, S=2048, Skv=2048) == DEVICE
+    assert lib.lix_indexer_backward_workspace_bytes(1, 4096, 4096, 64, 128) > cap
+    assert backward_noalloc_call(B=1, S=4096, Skv=4096) == UNSUP
