@@ -258,11 +258,27 @@ __device__ __forceinline__ float v41_pair_terms(float d0, float d1, float w0, fl
     return __builtin_amdgcn_fdot2_f32_bf16(e, ones, acc, false);
 }
 
+// Key stages of the V4.1 kernel: 64 keys.  On the packed-document mask most
+// of a workgroup's time is its own memory traffic (queries, mask rows, the
+// -inf fill) around a few stages, so it runs three waves per SIMD where the
+// registers allow (index_dim <= 128, heads >= 8: plain_stage, no rolling
+// epilogue) to overlap one workgroup's loads with another's MFMAs.
 template <int H, int DP>
-__global__ __launch_bounds__(256, stage_min_waves(H, DP)) void v41_scores_kernel(InLayout L, const uint16_t* __restrict__ wts,
+using V41Tiling = Tiling<H, DP, 64>;
+constexpr int v41_min_waves(int H, int DP) {
+    return H < 8 ? 1                                     // rolling_stage: its own register budget
+         : H == 128 ? (DP <= 64 ? 2 : 1)                 // 128 heads: the query fragments alone are large
+         : DP > 128 ? 1
+         : (H == 8 && DP > 64) ? 2                       // 8 heads, index_dim 128: spills at three
+         : 3;
+}
+
+template <int H, int DP>
+__global__ __launch_bounds__(256, v41_min_waves(H, DP)) void v41_scores_kernel(InLayout L, const uint16_t* __restrict__ wts,
                                                          const uint8_t* __restrict__ allowed, int B, int Lq,
                                                          int G, uint16_t* __restrict__ out) {
-    using T = Tiling<H, DP>;
+    using T = V41Tiling<H, DP>;
+    constexpr bool PAIRS = H >= 8;           // a query's heads fill lane pairs: the paired epilogue
     __shared__ __attribute__((aligned(16))) uint8_t lds0[T::STAGE_BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t lds1[T::STAGE_BYTES];
     __shared__ int span_lo, span_hi;
@@ -280,8 +296,8 @@ __global__ __launch_bounds__(256, stage_min_waves(H, DP)) void v41_scores_kernel
     // Query fragments and weights are requested first so their latency
     // overlaps the span scan.
     bf16x8 a[T::NRT][T::NSTEP];
-    float wr[T::NRT][16];
     load_q_frags<T>(a, L, b, tq0, Lq, lane);
+    float wr[T::NRT][16];
 #pragma unroll
     for (int r = 0; r < T::NRT; ++r)
 #pragma unroll
@@ -335,6 +351,17 @@ __global__ __launch_bounds__(256, stage_min_waves(H, DP)) void v41_scores_kernel
             }
             if (it + 1 < ntile) load_vis(s0 + T::KT);
             const bool active = __ballot(any) != 0ull;
+            // Column blocks with no key visible to any of the wave's queries
+            // skip their epilogue (their MFMAs run in the pipeline regardless;
+            // every output of such a block is -inf).
+            bool blk_live[T::NCB];
+#pragma unroll
+            for (int cb = 0; cb < T::NCB; ++cb) {
+                bool v = false;
+#pragma unroll
+                for (int j = 0; j < T::QW; ++j) v |= vis[cb][j];
+                blk_live[cb] = __ballot(v) != 0ull;
+            }
 
             float part[T::NCB][T::QW];
 #pragma unroll
@@ -342,44 +369,57 @@ __global__ __launch_bounds__(256, stage_min_waves(H, DP)) void v41_scores_kernel
 #pragma unroll
                 for (int j = 0; j < T::QW; ++j) part[cb][j] = 0.0f;
             if (active) {
-                auto term = [&](float acc_v, float w_v) {
-                    const float rr = round_bf16(relu(acc_v));    // bf16(d); ReLU commutes with rounding
-                    return round_bf16(w_v * rr);                  // exact product, then bf16
-                };
-                if constexpr (H >= 8) {
-                    // heads in pairs (elements i - 1, i share a query): packed
-                    // roundings and one dot2 add per pair
-                    rolling_stage<T>(a, stage, lane, [&](int cb, const f32x16 (&acc)[T::NRT], int r, int i) {
-                        if (i & 1)
-                            part[cb][T::slot(r, i)] = v41_pair_terms(acc[r][i - 1], acc[r][i], wr[r][i - 1],
-                                                                     wr[r][i], part[cb][T::slot(r, i)]);
+                if constexpr (PAIRS) {
+                    // heads in pairs (elements i, i + 1 share a query)
+                    plain_stage<T>(a, stage, lane, [&](int cb, const f32x16 (&acc)[T::NRT]) {
+                        if (!blk_live[cb]) return;
+#pragma unroll
+                        for (int r = 0; r < T::NRT; ++r)
+#pragma unroll
+                            for (int i = 0; i < 16; i += 2)
+                                part[cb][T::slot(r, i)] = v41_pair_terms(acc[r][i], acc[r][i + 1], wr[r][i],
+                                                                         wr[r][i + 1], part[cb][T::slot(r, i)]);
                     });
-                } else {
-                    rolling_stage<T>(a, stage, lane, [&](int cb, const f32x16 (&acc)[T::NRT], int r, int i) {
-                        part[cb][T::slot(r, i)] += term(acc[r][i], wr[r][i]);
-                    });
-                }
-                if constexpr (H >= 8) {
 #pragma unroll
                     for (int cb = 0; cb < T::NCB; ++cb)
 #pragma unroll
                         for (int j = 0; j < T::QW; ++j) part[cb][j] = xor32_add(part[cb][j]);
+                } else {
+                    rolling_stage<T>(a, stage, lane, [&](int cb, const f32x16 (&acc)[T::NRT], int r, int i) {
+                        if (blk_live[cb]) {
+                            const float rr = round_bf16(relu(acc[r][i]));    // bf16(d); ReLU commutes with rounding
+                            part[cb][T::slot(r, i)] += round_bf16(wr[r][i] * rr);   // exact product, then bf16
+                        }
+                    });
                 }
             }
 
+            if constexpr (PAIRS) {
+                // Per pair of column blocks lane l holds key s0 + 64 cp + l (the
+                // lower half's sums are block 2cp's, the upper half's block
+                // 2cp+1's): one store of 64 consecutive keys per query.
 #pragma unroll
-            for (int cb = 0; cb < T::NCB; ++cb) {
-                const int s = s0 + 32 * cb + (lane & 31);
+                for (int cp = 0; cp < T::NCB / 2; ++cp) {
+                    const int s = s0 + 64 * cp + lane;
 #pragma unroll
-                for (int j = 0; j < T::QW; ++j) {
-                    if constexpr (H >= 8) {
-                        if (hf != (cb & 1)) continue;      // lower half stores even blocks, upper half odd
-                    } else {
-                        if ((j % (2 * T::half_step())) >= T::half_step()) continue;
+                    for (int j = 0; j < T::QW; ++j) {
+                        const int t = tq0 + j;
+                        const float v = pick(hf != 0, part[2 * cp + 1][j], part[2 * cp][j]);
+                        const bool vv = hf ? vis[2 * cp + 1][j] : vis[2 * cp][j];
+                        if (t < Lq && s < G) out[((long)b * Lq + t) * G + s] = vv ? bf16_bits(v) : kNegInfBf16;
                     }
-                    const int t = slot_query<T>(tq0, j, hf);
-                    if (t < Lq && s < G)
-                        out[((long)b * Lq + t) * G + s] = vis[cb][j] ? bf16_bits(part[cb][j]) : kNegInfBf16;
+                }
+            } else {
+#pragma unroll
+                for (int cb = 0; cb < T::NCB; ++cb) {
+                    const int s = s0 + 32 * cb + (lane & 31);
+#pragma unroll
+                    for (int j = 0; j < T::QW; ++j) {
+                        if ((j % (2 * T::half_step())) >= T::half_step()) continue;
+                        const int t = slot_query<T>(tq0, j, hf);
+                        if (t < Lq && s < G)
+                            out[((long)b * Lq + t) * G + s] = vis[cb][j] ? bf16_bits(part[cb][j]) : kNegInfBf16;
+                    }
                 }
             }
         });
@@ -408,7 +448,7 @@ static hipError_t launch_v4_logits_t(const LogitsArgs& p) {
 
 template <int H, int DP>
 static hipError_t launch_v41_t(const V41Args& p) {
-    using T = Tiling<H, DP>;
+    using T = V41Tiling<H, DP>;
     InLayout L{static_cast<const uint16_t*>(p.queries), (long)H * p.D, (long)p.L * H * p.D,
                static_cast<const uint16_t*>(p.keys), (long)p.D, (long)p.G * p.D, p.D};
     const int nqb = (p.L + T::QB - 1) / T::QB;

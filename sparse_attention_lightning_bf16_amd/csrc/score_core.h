@@ -205,6 +205,29 @@ __device__ __forceinline__ void rolling_stage(const bf16x8 (&a)[T::NRT][T::NSTEP
             for (int i = st * PER; i < (st + 1) * PER; ++i) epi(T::NCB - 1, accp, r, i);
 }
 
+// One stage block by block: each 32-key column block's MFMA chains (B
+// fragments read one k-step ahead), then that block's epilogue, with no
+// second set of accumulators.  For kernels run at three or more waves per
+// SIMD, where other waves' MFMAs overlap a wave's epilogue.  epi(cb, acc)
+// handles block cb's finished accumulators.
+template <class T, class Epi>
+__device__ __forceinline__ void plain_stage(const bf16x8 (&a)[T::NRT][T::NSTEP], const uint8_t* stage, int lane,
+                                            Epi&& epi) {
+#pragma unroll
+    for (int cb = 0; cb < T::NCB; ++cb) {
+        f32x16 acc[T::NRT];
+        bf16x8 bn = b_frag<T>(stage, cb, 0, lane);
+#pragma unroll
+        for (int st = 0; st < T::NSTEP; ++st) {
+            const bf16x8 bc = bn;
+            if (st + 1 < T::NSTEP) bn = b_frag<T>(stage, cb, st + 1, lane);
+#pragma unroll
+            for (int r = 0; r < T::NRT; ++r) acc[r] = mfma_32x32x16(a[r][st], bc, st == 0 ? f32x16{} : acc[r]);
+        }
+        epi(cb, acc);
+    }
+}
+
 // Query handled by slot j of this lane.
 template <class T>
 __device__ __forceinline__ int slot_query(int tq0, int j, int hf) {

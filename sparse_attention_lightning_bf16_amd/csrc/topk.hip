@@ -758,18 +758,41 @@ __global__ __launch_bounds__(kBinThreads) void topk_rows_bin_kernel(const void* 
     for (int j = 0; j < NCH; ++j)
 #pragma unroll
         for (int m = 0; m < 4; ++m) x[j][m] = qnan;           // chunks past the row
+    // Loads first (the partial chunk's addresses clamped into the row), then
+    // the partial chunk's slots past the row set to NaN in a pass of their
+    // own: consuming a loaded value before every chunk's loads are issued
+    // would make each chunk wait for the one before it.  (The masking is a
+    // select on bit patterns: a select of the two values lets the optimiser
+    // turn the load into a select of addresses, through a generic pointer and
+    // a private NaN.)
+    // (bf16 inputs: the raw 16 bits are loaded and converted in the second
+    // pass, for the same reason.)
     visit_chunks<NCH, false>(jmax, jpart, [&](int j, auto partial) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int e = key_of(j, m);
-            if constexpr (decltype(partial)::value) {
-                const float v = cvt(row[min(e, n - 1)]);
-                x[j][m] = (e < n) ? v : qnan;
-            } else {
-                x[j][m] = cvt(row[e]);
-            }
+            const In raw = row[decltype(partial)::value ? min(e, n - 1) : e];
+            if constexpr (BF16) x[j][m] = __uint_as_float((uint32_t)raw);
+            else x[j][m] = raw;
         }
     });
+    if constexpr (BF16) {
+        visit_chunks<NCH, true>(jmax, jpart, [&](int j, auto) {
+            const bool partial = j == jpart;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const float v = cvt((uint16_t)__float_as_uint(x[j][m]));
+                x[j][m] = partial ? pick(key_of(j, m) < n, v, qnan) : v;
+            }
+        });
+    } else {
+        visit_chunks<NCH, false>(jmax, jpart, [&](int j, auto partial) {
+            if constexpr (decltype(partial)::value) {
+#pragma unroll
+                for (int m = 0; m < 4; ++m) x[j][m] = pick(key_of(j, m) < n, x[j][m], qnan);
+            }
+        });
+    }
 
     // ---- bf16 rows: count the visible keys; at most topk of them means all
     int visible = n;
