@@ -52,7 +52,7 @@ METRIC = "indexer TFLOP/s (causal-valid) + queries/s incl. top-k, 32K ctx, 1 MI3
 PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, published
 TRAFFIC_SUMMARY = "profiles/hbm_traffic_32k_workload.md"
-PARTS = ("logits", "topk", "fused", "gather", "scores_at", "backward", "v41", "topk_bf16", "copy")
+PARTS = ("logits", "topk", "fused", "streaming", "gather", "scores_at", "backward", "v41", "topk_bf16", "copy")
 
 
 def log(msg):
@@ -146,7 +146,7 @@ def measured_peaks(dev, steps, warmup):
 # ---------------------------------------------------------------- other workloads
 
 def extra_workloads(dev, steps, warmup, flush):
-    """4K materialized and fused steps warm and cold; the 131K fused step."""
+    """4K materialized, fused and streaming steps warm and cold; the 131K fused and materialized steps."""
     out = {}
     cfg = synth.WORKLOADS["4k"]
     inp = synth.v4_inputs(**cfg)
@@ -161,7 +161,12 @@ def extra_workloads(dev, steps, warmup, flush):
     out["4k_materialized_cold_ms"] = median_ms(step4k, steps, warmup, between=flush)
     out["4k_fused_warm_ms"] = median_ms(lambda: lx.topk(q, k, w, c, tk), steps, warmup)
     out["4k_fused_cold_ms"] = median_ms(lambda: lx.topk(q, k, w, c, tk), steps, warmup, between=flush)
-    del q, k, w, logits
+    ws = torch.empty(lx.streaming_workspace_bytes(cfg["batch"], cfg["seqlen"], cfg["seqlen_kv"], cfg["heads"],
+                                                  cfg["index_dim"]), dtype=torch.uint8, device=dev)
+    out["4k_streaming_warm_ms"] = median_ms(lambda: lx.topk_streaming(q, k, w, c, tk, workspace=ws), steps, warmup)
+    out["4k_streaming_cold_ms"] = median_ms(lambda: lx.topk_streaming(q, k, w, c, tk, workspace=ws), steps, warmup,
+                                            between=flush)
+    del q, k, w, logits, ws
 
     log("timing the 131K fused step")
     cfg = synth.WORKLOADS["131k"]
@@ -175,6 +180,24 @@ def extra_workloads(dev, steps, warmup, flush):
     out["131k_fused_tflops"] = 2.0 * cfg["heads"] * cfg["index_dim"] * pairs / ms / 1e9
     out["131k_fused_mfma_frac"] = out["131k_fused_tflops"] / PEAK_BF16_TFLOPS
     out["131k_queries_per_s"] = cfg["batch"] * cfg["seqlen"] / (ms * 1e-3)
+    # the materialized route at 131K: a [B,S,Skv] fp32 buffer of 16 GiB, then the row top-k
+    log("timing the 131K materialized step")
+    logits = torch.empty(cfg["batch"], cfg["seqlen"], cfg["seqlen_kv"], dtype=torch.float32, device=dev)
+    n = max(3, steps // 4)
+    lg_ms = median_ms(lambda: lx.indexer_logits(q, k, w, c, out=logits), n, 2)
+    tk_ms = median_ms(lambda: lx.topk_from_logits(logits, c, tk), n, 2)
+
+    def step131k():
+        lx.indexer_logits(q, k, w, c, out=logits)
+        return lx.topk_from_logits(logits, c, tk)
+    ms_m = median_ms(step131k, n, 2)
+    sc_m, ix_m = step131k()
+    sc_f, ix_f = lx.topk(q, k, w, c, tk)
+    out["131k_materialized_ms"] = ms_m
+    out["131k_materialized_logits_ms"] = lg_ms
+    out["131k_materialized_topk_ms"] = tk_ms
+    out["131k_materialized_tflops"] = 2.0 * cfg["heads"] * cfg["index_dim"] * pairs / ms_m / 1e9
+    out["131k_fused_equals_materialized"] = bool(torch.equal(ix_m, ix_f) and torch.equal(sc_m, sc_f))
     return out
 
 
@@ -278,7 +301,7 @@ def cpu_baseline(inp32, every32):
 def profile_part(args, dev, q, k, w, cfg):
     """Launch one kernel's call in a loop; prints its median duration."""
     c, tk = cfg["compress_ratio"], cfg["topk"]
-    B, S, Skv = cfg["batch"], cfg["seqlen"], cfg["seqlen_kv"]
+    B, S, Skv, H, D = cfg["batch"], cfg["seqlen"], cfg["seqlen_kv"], cfg["heads"], cfg["index_dim"]
     part = args.part
     if part == "copy":
         # plain device copy of a known size: the reference for scaling HBM counters
@@ -295,6 +318,9 @@ def profile_part(args, dev, q, k, w, cfg):
             fn = lambda: lx.topk_bf16(v41, 512)
     elif part == "fused":
         fn = lambda: lx.topk(q, k, w, c, tk)
+    elif part == "streaming":
+        ws = torch.empty(lx.streaming_workspace_bytes(B, S, Skv, H, D), dtype=torch.uint8, device=dev)
+        fn = lambda: lx.topk_streaming(q, k, w, c, tk, workspace=ws)
     else:
         logits = torch.empty(B, S, Skv, dtype=torch.float32, device=dev)
         lx.indexer_logits(q, k, w, c, out=logits)
@@ -365,6 +391,14 @@ def main():
     fused_ms, fused_mean = time_calls(lambda: lx.topk(q, k, w, c, tk), args.steps, args.warmup)
     sc_f, ix_f = lx.topk(q, k, w, c, tk)
 
+    log("timing the streaming step")
+    ws_s = torch.empty(lx.streaming_workspace_bytes(B, S, Skv, H, D), dtype=torch.uint8, device=dev)
+    streaming_step = lambda: lx.topk_streaming(q, k, w, c, tk, workspace=ws_s)
+    stream_ms, stream_mean = time_calls(streaming_step, args.steps, args.warmup)
+    sc_s, ix_s = streaming_step()
+    stream_same = bool(torch.equal(ix_s, ix_f) and torch.equal(sc_s, sc_f))
+    del sc_s, ix_s
+
     log("timing the materialized path")
     logits = torch.empty(B, S, Skv, dtype=torch.float32, device=dev)
 
@@ -379,6 +413,7 @@ def main():
     log("timing both routes cold")
     step_m_cold = median_ms(materialized_step, args.steps, args.warmup, between=flush)
     fused_cold = median_ms(lambda: lx.topk(q, k, w, c, tk), args.steps, args.warmup, between=flush)
+    stream_cold = median_ms(streaming_step, args.steps, args.warmup, between=flush)
     gather_ms = median_ms(lambda: lx.topk_scores(logits, ix_f), args.steps, args.warmup)
     # scores at given indices straight from q, k, w (the topk_indices branch of the pages' entry point)
     at_ms = median_ms(lambda: lx.indexer_scores_at(q, k, w, c, ix_f), args.steps, args.warmup)
@@ -394,6 +429,12 @@ def main():
         "fused_topk_mean_ms": fused_mean,
         "fused_topk_cold_ms": fused_cold,
         "fused_topk_tflops": flop / fused_ms / 1e9,
+        "streaming_step_ms": stream_ms,
+        "streaming_step_mean_ms": stream_mean,
+        "streaming_step_cold_ms": stream_cold,
+        "streaming_tflops": flop / stream_ms / 1e9,
+        "streaming_workspace_bytes": ws_s.numel(),
+        "streaming_equals_fused": stream_same,
         "materialized_step_ms": step_m_ms,
         "materialized_step_mean_ms": step_m_mean,
         "materialized_step_cold_ms": step_m_cold,
@@ -461,15 +502,17 @@ def main():
                 "mfma_loop_bf16_tflops"]
     del flush_buf
 
-    # The step is the faster of the two routes to the same forward; both are reported.
-    if step_m_ms < fused_ms:
-        step_ms = step_m_ms
-        path = "materialized: lix_indexer_logits then lix_topk over the logits"
-        roof_kernel = {"name": "v4_logits_kernel", "ms": score_ms}
-    else:
-        step_ms = fused_ms
-        path = "fused: lix_topk scoring and selecting on chip"
-        roof_kernel = {"name": "v4_fused_topk_kernel", "ms": fused_ms}
+    del ws_s
+    # The step is the fastest of the three routes to the same forward; all are reported.
+    routes = [
+        (step_m_ms, "materialized: lix_indexer_logits then lix_topk over the logits",
+         {"name": "v4_logits_kernel<64, 128, false>", "ms": score_ms}),
+        (fused_ms, "fused: lix_topk scoring and selecting on chip",
+         {"name": "v4_fused_topk_kernel", "ms": fused_ms}),
+        (stream_ms, "streaming: lix_topk_streaming, each query block selected right after it is scored",
+         {"name": "v4_logits_kernel<64, 128, true>", "ms": stream_ms}),
+    ]
+    step_ms, path, roof_kernel = min(routes, key=lambda r: r[0])
     value = flop / step_ms / 1e9
     achieved = flop / roof_kernel["ms"] / 1e9
     result = {

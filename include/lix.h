@@ -146,6 +146,48 @@ int lix_topk(const void* q, const void* k, const float* w, const float* logits,
 int lix_topk_fused_supported(int Skv, int H, int D, int topk);
 
 /*
+ * lix_topk_streaming - per-query top-k of the indexer scores, selected block
+ * by block as the scores are produced.
+ *
+ * Same selection, outputs and bits as lix_topk (page
+ * "...deepseek_v4.kernels.tilelang_indexer", v4_lighting_indexer), from q,
+ * k, w as in lix_indexer_logits, without the fused path's on-chip limits and
+ * without writing the [B,S,Skv] logits: a persistent grid scores one query
+ * block at a time into its own slot of `workspace` (the block's rows of Skv
+ * fp32, written over each row's visible span only) and selects each of that
+ * block's rows from the slot at once, while the rows are still in the L2
+ * cache.  Every output equals lix_indexer_logits followed by lix_topk on the
+ * logits, bit for bit.
+ *
+ *   q, k, w, ks, ke, compress_ratio  as in lix_indexer_logits
+ *   topk       1 <= topk <= Skv
+ *   scores     fp32  [B, S, topk]  out
+ *   indices    int32 [B, S, topk]  out
+ *   workspace  device memory owned by the caller, 256-byte aligned; its
+ *              contents on entry do not matter and on return are
+ *              unspecified.  lix_topk_streaming_workspace_bytes gives the
+ *              size that keeps every resident workgroup busy; a smaller one
+ *              (at least one block's rows) runs fewer workgroups, a smaller
+ *              still is LIX_ERR_SHAPE.
+ * Requires Skv <= 8192 (a row sits in registers while it is selected):
+ * LIX_ERR_UNSUPPORTED otherwise.
+ */
+int lix_topk_streaming(const void* q, const void* k, const float* w,
+                       int B, int S, int Skv, int H, int D, int compress_ratio,
+                       const int32_t* ks, const int32_t* ke, int topk,
+                       float* scores, int32_t* indices,
+                       void* workspace, long long workspace_bytes, hipStream_t stream);
+
+/*
+ * lix_topk_streaming_workspace_bytes - workspace lix_topk_streaming uses at
+ * full occupancy on the current device for these sizes: (workgroups resident
+ * at once, at most one per query block) x (queries per block) x Skv x 4
+ * bytes.  -1 when the sizes are outside what lix_topk_streaming accepts or
+ * the device query fails.
+ */
+long long lix_topk_streaming_workspace_bytes(int B, int S, int Skv, int H, int D);
+
+/*
  * lix_topk_scores - scores at given key indices.
  *
  * Page "...deepseek_v4.kernels.tilelang_indexer", section

@@ -9,6 +9,8 @@ from .ops import (  # noqa: F401
     indexer_logits,
     topk,
     fused_topk_supported,
+    topk_streaming,
+    streaming_workspace_bytes,
     select_topk,
     topk_from_logits,
     topk_scores,

@@ -25,6 +25,8 @@ SIGNATURES = {
     "lix_indexer_logits": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P]),
     "lix_topk": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P]),
     "lix_topk_fused_supported": (_I, [_I, _I, _I, _I]),
+    "lix_topk_streaming": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P, _LL, _P]),
+    "lix_topk_streaming_workspace_bytes": (_LL, [_I, _I, _I, _I, _I]),
     "lix_topk_scores": (_I, [_P, _P, _I, _I, _I, _I, _P, _P]),
     "lix_indexer_scores_v41": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
     "lix_indexer_scores_at": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P]),

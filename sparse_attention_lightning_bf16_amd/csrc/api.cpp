@@ -151,6 +151,36 @@ int lix_topk_fused_supported(int Skv, int H, int D, int topk) {
     return fused_fits(Skv, H, D, topk) ? 1 : 0;
 }
 
+long long lix_topk_streaming_workspace_bytes(int B, int S, int Skv, int H, int D) {
+    if (check_dims_v4(B, S, Skv, H, D, 1, nullptr, nullptr) != LIX_OK) return -1;
+    if (Skv > lix::kStreamMaxSkv) return -1;
+    long grid = 0;
+    if (lix::streaming_grid(B, S, H, D, &grid) != hipSuccess) {
+        (void)hipGetLastError();
+        return -1;
+    }
+    return (long long)grid * lix::streaming_slot_bytes(H, D, Skv);
+}
+
+int lix_topk_streaming(const void* q, const void* k, const float* w, int B, int S, int Skv, int H, int D,
+                       int compress_ratio, const int32_t* ks, const int32_t* ke, int topk, float* scores,
+                       int32_t* indices, void* workspace, long long workspace_bytes, hipStream_t stream) {
+    if (!q || !k || !w || !scores || !indices || !workspace) return LIX_ERR_NULL;
+    int st = check_dims_v4(B, S, Skv, H, D, compress_ratio, ks, ke);
+    if (st != LIX_OK) return st;
+    if (topk < 1 || topk > Skv) return LIX_ERR_SHAPE;
+    if (Skv > lix::kStreamMaxSkv || !fits(B, S, topk)) return LIX_ERR_UNSUPPORTED;
+    if (workspace_bytes < lix::streaming_slot_bytes(H, D, Skv)) return LIX_ERR_SHAPE;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(w, 4) || !aligned(scores, 4) || !aligned(indices, 4) ||
+        !aligned(ks, 4) || !aligned(ke, 4) || !aligned(workspace, 256))
+        return LIX_ERR_UNSUPPORTED;
+    st = check_device({q, k, w, ks, ke, scores, indices, workspace});
+    if (st != LIX_OK) return st;
+    lix::StreamArgs a{q, k, w, B, S, Skv, H, D, compress_ratio, topk, ks, ke, static_cast<float*>(workspace),
+                      (long)workspace_bytes, scores, indices, stream};
+    return launch_status(lix::launch_topk_streaming(a));
+}
+
 int lix_topk_scores(const float* logits, const int32_t* indices, int B, int S, int Skv, int topk, float* scores,
                     hipStream_t stream) {
     if (!logits || !indices || !scores) return LIX_ERR_NULL;

@@ -81,6 +81,30 @@ struct SparseArgs {
 };
 
 hipError_t launch_v4_logits(const LogitsArgs& p);
+
+// Scoring with the top-k selected right after each query block is scored
+// (lix_topk_streaming): a persistent grid, each workgroup owning one slot of
+// the workspace (streaming_slot_bytes) for the rows of its current block.
+struct StreamArgs {
+    const void* q;
+    const void* k;
+    const float* w;
+    int B, S, Skv, H, D, ratio, topk;
+    const int32_t* ks;
+    const int32_t* ke;
+    float* workspace;         // workspace_bytes / streaming_slot_bytes slots (at least one)
+    long workspace_bytes;
+    float* scores;            // [B,S,topk]
+    int32_t* indices;         // [B,S,topk]
+    hipStream_t stream;
+};
+constexpr int kStreamMaxSkv = 8192;   // a row of the block in registers during its selection
+// Bytes of one slot: the scores of one query block (QB rows of Skv fp32).
+long streaming_slot_bytes(int H, int D, int Skv);
+// Workgroups of the persistent grid on the current device: min(query blocks,
+// resident workgroups).
+hipError_t streaming_grid(int B, int S, int H, int D, long* grid);
+hipError_t launch_topk_streaming(const StreamArgs& p);
 hipError_t launch_sparse_scores(const SparseArgs& p);
 
 // Gradients of the scores at given indices (dk is cleared, then accumulated).

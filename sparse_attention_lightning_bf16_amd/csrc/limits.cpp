@@ -35,6 +35,23 @@ long fused_capacity(int H, int D, int topk) {
 
 int fused_supported(int H, int D, int topk) { return fused_capacity(H, D, topk) > 0; }
 
+long streaming_slot_bytes(int H, int D, int Skv) {
+    int qb = 0;
+    switch (H) {
+        case 1: qb = Tiling<1, 64>::QB; break;
+        case 2: qb = Tiling<2, 64>::QB; break;
+        case 4: qb = Tiling<4, 64>::QB; break;
+        case 8: qb = Tiling<8, 64>::QB; break;
+        case 16: qb = Tiling<16, 64>::QB; break;
+        case 32: qb = Tiling<32, 64>::QB; break;
+        case 64: qb = Tiling<64, 64>::QB; break;
+        case 128: qb = Tiling<128, 64>::QB; break;
+        default: return -1;
+    }
+    (void)D;   // queries per workgroup do not depend on index_dim
+    return (long)qb * Skv * 4;
+}
+
 long backward_g_bytes(int B, int S, int Skv) { return ((long)B * S * Skv * 4 + 255) & ~255L; }
 
 long backward_workspace_bytes(int B, int S, int Skv, int H, int D) {

@@ -12,6 +12,7 @@
 // Key stages [s0, s0+KT) that lie outside every range of the workgroup are
 // never computed (causal tile skip); their logits are filled with -inf.
 #include "score_core.h"
+#include "row_select.h"
 #include "launch.h"
 
 namespace lix {
@@ -33,13 +34,30 @@ __device__ __forceinline__ void load_weights_f32(float (&wr)[T::NRT][16], const 
 
 // ---------------------------------------------------------------- V4 logits
 
-template <int H, int DP>
+// SELECT = false (lix_indexer_logits): out is the [B,S,Skv] logits; each
+// workgroup handles one query block; positions outside the staged span are
+// filled with -inf.
+// SELECT = true (lix_topk_streaming): out is the workspace, one slot of
+// QB rows of skv floats per workgroup; the grid is persistent (workgroup w
+// handles blocks sched_block(w, gridDim.x, i)), a block's scores go to the
+// workgroup's slot (only the staged span is written), and right after the
+// block's stage loop the workgroup selects each of its rows' top-k from the
+// slot (select_row_binned, the selection of the row top-k kernel; the rows
+// are still in L2) into scores / indices [B,S,topk].  Requires skv <= 8192.
+template <int H, int DP, bool SELECT>
 __global__ __launch_bounds__(256, stage_min_waves(H, DP)) void v4_logits_kernel(InLayout L, const float* __restrict__ w, int B, int S,
                                                         int skv, int ratio, const int32_t* __restrict__ ks,
-                                                        const int32_t* __restrict__ ke, float* __restrict__ out) {
+                                                        const int32_t* __restrict__ ke, float* __restrict__ out,
+                                                        int topk, float* __restrict__ scores,
+                                                        int32_t* __restrict__ indices) {
     using T = Tiling<H, DP>;
-    __shared__ __attribute__((aligned(16))) uint8_t lds0[T::STAGE_BYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t lds1[T::STAGE_BYTES];
+    // The two stage buffers; in SELECT mode the selection state reuses them
+    // (the array grows where it is larger than both).
+    constexpr int kStages = 2 * T::STAGE_BYTES;
+    constexpr int kBytes = (SELECT && (int)sizeof(BinShared) > kStages) ? (int)sizeof(BinShared) : kStages;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kBytes];
+    uint8_t* const lds0 = lds;
+    uint8_t* const lds1 = lds + T::STAGE_BYTES;
 
     const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -83,7 +101,17 @@ __global__ __launch_bounds__(256, stage_min_waves(H, DP)) void v4_logits_kernel(
             if (hi > lo) { wave_lo = min(wave_lo, lo); wave_hi = max(wave_hi, hi); }
         }
 
-        float* out_b = out + (long)b * S * skv;
+        // Row of query t: its logits row, or its row in the workgroup's slot.
+        auto row_off = [&](int t) -> long {
+            if constexpr (SELECT) return ((long)blockIdx.x * T::QB + (t - t0)) * skv;
+            else return ((long)b * S + t) * skv;
+        };
+        // Logits go past the caches (nothing reads them back soon); slot
+        // rows are read back by this workgroup right after the block.
+        auto put = [](float v, float* p) {
+            if constexpr (SELECT) *p = v;
+            else __builtin_nontemporal_store(v, p);
+        };
         // Results of a stage are stored at the start of the next one (see
         // stream_key_stages): pend[cb][q], first key of that stage pend_s0.
         float pend[T::NCB][T::QW];
@@ -106,8 +134,8 @@ __global__ __launch_bounds__(256, stage_min_waves(H, DP)) void v4_logits_kernel(
                         const int s = pend_s0 + 64 * cp + lane;
 #pragma unroll
                         for (int q = 0; q < T::QW; ++q)
-                            __builtin_nontemporal_store(pick(hf != 0, pend[2 * cp + 1][q], pend[2 * cp][q]),
-                                                        out_b + (long)(tq0 + q) * skv + s);
+                            put(pick(hf != 0, pend[2 * cp + 1][q], pend[2 * cp][q]),
+                                                        out + row_off(tq0 + q) + s);
                     }
                     return;
                 }
@@ -119,8 +147,8 @@ __global__ __launch_bounds__(256, stage_min_waves(H, DP)) void v4_logits_kernel(
                         const int t = tq0 + q;
                         if (t < S && s < skv) {
                             const float v = pick(hf != 0, pend[2 * cp + 1][q], pend[2 * cp][q]);
-                            __builtin_nontemporal_store((s >= lo_s[q] && s < hi_s[q]) ? v : neg_inf(),
-                                                        out_b + (long)t * skv + s);
+                            put((s >= lo_s[q] && s < hi_s[q]) ? v : neg_inf(),
+                                                        out + row_off(t) + s);
                         }
                     }
                 }
@@ -133,8 +161,8 @@ __global__ __launch_bounds__(256, stage_min_waves(H, DP)) void v4_logits_kernel(
                         if ((q % (2 * T::half_step())) >= T::half_step()) continue;   // slot owned via hf
                         const int t = slot_query<T>(tq0, q, hf);
                         if (t < S && s < skv)
-                            __builtin_nontemporal_store((s >= lo_s[q] && s < hi_s[q]) ? pend[cb][q] : neg_inf(),
-                                                        out_b + (long)t * skv + s);
+                            put((s >= lo_s[q] && s < hi_s[q]) ? pend[cb][q] : neg_inf(),
+                                                        out + row_off(t) + s);
                     }
                 }
             }
@@ -163,13 +191,35 @@ __global__ __launch_bounds__(256, stage_min_waves(H, DP)) void v4_logits_kernel(
             });
             flush();
         }
-        // -inf outside the staged span: no query of the block sees those keys.
-        for (int q = 0; q < T::QB; ++q) {
-            const int t = t0 + q;
-            if (t >= S) break;
-            float* row = out_b + (long)t * skv;
-            fill_neg_inf(row, span_lo, tid, T::THREADS);
-            fill_neg_inf(row + span_hi, skv - span_hi, tid, T::THREADS);
+        if constexpr (!SELECT) {
+            // -inf outside the staged span: no query of the block sees those keys.
+            for (int q = 0; q < T::QB; ++q) {
+                const int t = t0 + q;
+                if (t >= S) break;
+                float* row = out + row_off(t);
+                fill_neg_inf(row, span_lo, tid, T::THREADS);
+                fill_neg_inf(row + span_hi, skv - span_hi, tid, T::THREADS);
+            }
+        } else {
+            // The block's rows are in the slot (every store of the workgroup
+            // has completed at the barrier); select each row's top-k.  The
+            // selection state reuses the stage buffers.
+            BinShared& sh = *reinterpret_cast<BinShared*>(lds);
+            for (int q = 0; q < T::QB; ++q) {
+                const int t = t0 + q;
+                if (t >= S) break;
+                __syncthreads();
+                int lo, hi;
+                key_range(ks, ke, t, S, skv, ratio, lo, hi);
+                // The range is the same in every lane; loaded after this
+                // workgroup's stores it arrives in vector registers.
+                lo = __builtin_amdgcn_readfirstlane(lo);
+                hi = __builtin_amdgcn_readfirstlane(hi);
+                const long o = ((long)b * S + t) * topk;
+                select_row_binned<8, false>(out + row_off(t) + lo, hi - lo, lo, topk, scores + o, indices + o, sh,
+                                            tid);
+            }
+            __syncthreads();      // before the next block writes the stage buffers and the slot
         }
     }
 }
@@ -441,8 +491,42 @@ static hipError_t launch_v4_logits_t(const LogitsArgs& p) {
                static_cast<const uint16_t*>(p.k), (long)p.B * p.D, (long)p.D, p.D};
     const long nblk = (long)((p.S + T::QB - 1) / T::QB) * p.B;
     dim3 grid((unsigned)nblk);                 // one block per workgroup (see sched_block)
-    hipLaunchKernelGGL((v4_logits_kernel<H, DP>), grid, dim3(T::THREADS), 0, p.stream, L, p.w, p.B, p.S, p.Skv,
-                       p.ratio, p.ks, p.ke, p.logits);
+    hipLaunchKernelGGL((v4_logits_kernel<H, DP, false>), grid, dim3(T::THREADS), 0, p.stream, L, p.w, p.B, p.S,
+                       p.Skv, p.ratio, p.ks, p.ke, p.logits, 0, nullptr, nullptr);
+    return hipGetLastError();
+}
+
+// Persistent grid of the streaming top-k: as many workgroups as are resident
+// at once on the device (occupancy x compute units), at most one per block.
+template <int H, int DP>
+static hipError_t streaming_grid_t(int B, int S, long* grid) {
+    using T = Tiling<H, DP>;
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, v4_logits_kernel<H, DP, true>, T::THREADS, 0);
+    if (e != hipSuccess) return e;
+    const long nblk = (long)((S + T::QB - 1) / T::QB) * B;
+    const long resident = (long)(cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
+    *grid = nblk < resident ? nblk : resident;
+    return hipSuccess;
+}
+
+template <int H, int DP>
+static hipError_t launch_streaming_t(const StreamArgs& p) {
+    using T = Tiling<H, DP>;
+    InLayout L{static_cast<const uint16_t*>(p.q), (long)p.B * H * p.D, (long)H * p.D,
+               static_cast<const uint16_t*>(p.k), (long)p.B * p.D, (long)p.D, p.D};
+    long grid = 0;
+    const hipError_t e = streaming_grid_t<H, DP>(p.B, p.S, &grid);
+    if (e != hipSuccess) return e;
+    const long slot = (long)T::QB * p.Skv * 4;
+    const long fit = p.workspace_bytes / slot;
+    if (fit < grid) grid = fit;
+    if (grid < 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((v4_logits_kernel<H, DP, true>), dim3((unsigned)grid), dim3(T::THREADS), 0, p.stream, L,
+                       p.w, p.B, p.S, p.Skv, p.ratio, p.ks, p.ke, p.workspace, p.topk, p.scores, p.indices);
     return hipGetLastError();
 }
 
@@ -494,6 +578,40 @@ hipError_t launch_v4_logits(const LogitsArgs& p) {
         default: return hipErrorInvalidValue;
     }
 }
+
+template <int H>
+static hipError_t dispatch_dp_streaming(const StreamArgs& p, long* grid) {
+    switch (padded_dim(p.D)) {
+        case 32: return grid ? streaming_grid_t<H, 32>(p.B, p.S, grid) : launch_streaming_t<H, 32>(p);
+        case 64: return grid ? streaming_grid_t<H, 64>(p.B, p.S, grid) : launch_streaming_t<H, 64>(p);
+        case 128: return grid ? streaming_grid_t<H, 128>(p.B, p.S, grid) : launch_streaming_t<H, 128>(p);
+        case 256: return grid ? streaming_grid_t<H, 256>(p.B, p.S, grid) : launch_streaming_t<H, 256>(p);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+// grid == nullptr: launch; else: store the persistent grid size only.
+static hipError_t dispatch_streaming(const StreamArgs& p, long* grid) {
+    switch (p.H) {
+        case 1: return dispatch_dp_streaming<1>(p, grid);
+        case 2: return dispatch_dp_streaming<2>(p, grid);
+        case 4: return dispatch_dp_streaming<4>(p, grid);
+        case 8: return dispatch_dp_streaming<8>(p, grid);
+        case 16: return dispatch_dp_streaming<16>(p, grid);
+        case 32: return dispatch_dp_streaming<32>(p, grid);
+        case 64: return dispatch_dp_streaming<64>(p, grid);
+        case 128: return dispatch_dp_streaming<128>(p, grid);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t streaming_grid(int B, int S, int H, int D, long* grid) {
+    StreamArgs p{};
+    p.B = B; p.S = S; p.H = H; p.D = D;
+    return dispatch_streaming(p, grid);
+}
+
+hipError_t launch_topk_streaming(const StreamArgs& p) { return dispatch_streaming(p, nullptr); }
 
 hipError_t launch_v41_scores(const V41Args& p) {
     switch (p.H) {

@@ -115,12 +115,49 @@ def fused_topk_supported(seqlen_kv, heads, index_dim, topk):
     return bool(_lib.load().lix_topk_fused_supported(int(seqlen_kv), int(heads), int(index_dim), int(topk)))
 
 
-def select_topk(q, k, weights, compress_ratio, topk):
-    """Top-k of the causal indexer scores by whichever route the library offers for these sizes: the
-    fused kernel (lix_topk with no logits) where it holds the candidates on chip, else the
-    materialized route (lix_indexer_logits into a [B,S,Skv] fp32 buffer, then lix_topk over it).
-    Both routes select the same keys and return the same bits."""
+STREAMING_MAX_SEQLEN_KV = 8192       # lix_topk_streaming: a row sits in registers while it is selected
+
+
+def streaming_workspace_bytes(batch, seqlen, seqlen_kv, heads, index_dim):
+    """lix_topk_streaming_workspace_bytes: the workspace lix_topk_streaming uses at full occupancy on the
+    current device (-1 for sizes it does not take)."""
+    return int(_lib.load().lix_topk_streaming_workspace_bytes(int(batch), int(seqlen), int(seqlen_kv), int(heads),
+                                                              int(index_dim)))
+
+
+def topk_streaming(q, k, weights, compress_ratio, topk, cu_seqlen_ks=None, cu_seqlen_ke=None, workspace=None):
+    """lix_topk_streaming: scoring with each query block's top-k selected as soon as the block is scored
+    (seqlen_kv <= 8192; no [B,S,Skv] tensor).  Same results, bit for bit, as indexer_logits followed by
+    topk_from_logits.  workspace: an optional uint8 GPU tensor (allocated at the full-occupancy size when
+    None).  Returns (scores fp32 [B,S,topk], indices int32 [B,S,topk])."""
     S, B, H, D, Skv = _v4_shapes(q, k, weights)
+    ks, ke = _ranges(cu_seqlen_ks, cu_seqlen_ke, S)
+    lib = _lib.load()
+    if workspace is None:
+        nbytes = int(lib.lix_topk_streaming_workspace_bytes(B, S, Skv, H, D))
+        if nbytes < 0:
+            raise _lib.LixError(_lib.LIX_ERR_UNSUPPORTED, "lix_topk_streaming_workspace_bytes")
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    else:
+        _need(workspace, "workspace", torch.uint8, 1)
+    scores = torch.empty(B, S, topk, dtype=torch.float32, device=q.device)
+    indices = torch.empty(B, S, topk, dtype=torch.int32, device=q.device)
+    st = lib.lix_topk_streaming(q.data_ptr(), k.data_ptr(), weights.data_ptr(), B, S, Skv, H, D,
+                                int(compress_ratio), _ptr(ks), _ptr(ke), int(topk), scores.data_ptr(),
+                                indices.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(q.device))
+    _lib.check(st, "lix_topk_streaming")
+    return scores, indices
+
+
+def select_topk(q, k, weights, compress_ratio, topk):
+    """Top-k of the causal indexer scores by the route the library offers for these sizes without a
+    [B,S,Skv] buffer where it can: the streaming kernel (lix_topk_streaming) for seqlen_kv <= 8192,
+    else the fused kernel (lix_topk with no logits) where it holds the candidates on chip, else the
+    materialized route (lix_indexer_logits into a [B,S,Skv] fp32 buffer, then lix_topk over it).
+    Every route selects the same keys and returns the same bits."""
+    S, B, H, D, Skv = _v4_shapes(q, k, weights)
+    if Skv <= STREAMING_MAX_SEQLEN_KV:
+        return topk_streaming(q, k, weights, compress_ratio, topk)
     if fused_topk_supported(Skv, H, D, topk):
         return globals()["topk"](q, k, weights, compress_ratio, topk)
     logits = indexer_logits(q, k, weights, compress_ratio)
@@ -205,8 +242,8 @@ class V4IndexerFunction(torch.autograd.Function):
     """Autograd Function of the indexer (page "...tilelang_indexer", class V4IndexerFunction).
 
     forward(index_q, index_k, weights, compress_ratio, topk, topk_indices=None) returns
-    (scores, indices): the top-k (select_topk: the fused kernel, or the materialized route for sizes
-    the fused kernel cannot hold on chip) when topk_indices is None, else the scores at topk_indices
+    (scores, indices): the top-k (select_topk: the streaming kernel, the fused kernel or the
+    materialized route, by size) when topk_indices is None, else the scores at topk_indices
     (returned unchanged as the indices).  backward(grad_scores, grad_indices) gives the
     gradients of q, k and weights through the selected scores (lix_indexer_backward), in their dtypes;
     the indices and the integer arguments get none.
@@ -269,9 +306,10 @@ def topk_bf16(scores, topk):
 def v4_lighting_indexer(index_q, index_k, weights, compress_ratio, topk, topk_indices=None):
     """The pages' main entry point (the misspelt name is the pages' own).
 
-    Without topk_indices: scoring + top-k, returns (scores, indices): the fused kernel, or for sizes
-    it cannot hold on chip (heads < 8, seqlen_kv > 65536, topk above the per-head capacity listed in
-    include/lix.h) the materialized logits then the row top-k; both give the same bits.
+    Without topk_indices: scoring + top-k, returns (scores, indices): the streaming kernel for
+    seqlen_kv <= 8192, else the fused kernel, or for sizes it cannot hold on chip (heads < 8,
+    seqlen_kv > 65536, topk above the per-head capacity listed in include/lix.h) the materialized
+    logits then the row top-k; all give the same bits.
     With topk_indices [B,S,topk] int32: the scores at those indices, scored
     directly (lix_indexer_scores_at; equal bit for bit to gathering the
     materialized logits), returns scores.  Both go through V4IndexerFunction,

@@ -143,13 +143,25 @@ int main() {
     const uint8_t* al = P<const uint8_t>();
     EXPECT(lix_indexer_scores_v41(p, p, p, al, 1, 4, 2, 6, 128, p, nullptr), UNS);
     EXPECT(lix_indexer_scores_v41(p, p, p, al, 1, 4, 2, 64, 128, p, nullptr), DEV);
+    auto streaming = [&](int B, int S, int Skv, int H, int D, int tk, void* w, long long wb) {
+        return lix_topk_streaming(p, p, fp, B, S, Skv, H, D, 4, nullptr, nullptr, tk, fp, op, w, wb, nullptr);
+    };
+    EXPECT(streaming(1, 8, 4, 64, 128, 2, nullptr, 1 << 20), NUL);
+    EXPECT(streaming(1, 8, 4, 64, 128, 5, p, 1 << 20), SHP);
+    EXPECT(streaming(1, 8, 8193, 64, 128, 5, p, 1 << 20), UNS);
+    EXPECT(streaming(1, 8, 8192, 64, 128, 5, p, 4 * 8192 * 4 - 1), SHP);
+    EXPECT(streaming(1, 8, 8192, 64, 128, 5, fake(128), 4 * 8192 * 4), UNS);
+    EXPECT(streaming(1, 8, 8192, 64, 128, 5, p, 4 * 8192 * 4), DEV);
+    EXPECT(streaming(INT_MAX, INT_MAX, 8192, 128, 256, 5, p, 1LL << 40), UNS);
+    if (lix_topk_streaming_workspace_bytes(1, 8, 8193, 64, 128) != -1) ++g_failures;
+    if (lix_topk_streaming_workspace_bytes(INT_MAX, INT_MAX, 8192, 64, 128) != -1) ++g_failures;
     EXPECT(lix_topk_bf16(p, 1, 8, 8193, 4, p, op, nullptr), UNS);
     EXPECT(lix_topk_bf16(p, 1, 8, 16, 4, p, op, nullptr), DEV);
 
     // ---- seeded sweep over extreme sizes and pointers: only documented statuses, no sanitizer report
     for (int it = 0; it < 20000; ++it) {
         int st;
-        switch (it % 7) {
+        switch (it % 8) {
             case 0:
                 st = lix_indexer_logits(pick_ptr(), pick_ptr(), (float*)pick_ptr(), pick_int(), pick_int(), pick_int(),
                                         pick_int(), pick_int(), pick_int(), nullptr, nullptr, (float*)pick_ptr(),
@@ -182,6 +194,12 @@ int main() {
             case 5:
                 st = lix_indexer_scores_v41(pick_ptr(), pick_ptr(), pick_ptr(), (uint8_t*)pick_ptr(), pick_int(),
                                             pick_int(), pick_int(), pick_int(), pick_int(), pick_ptr(), nullptr);
+                break;
+            case 6:
+                st = lix_topk_streaming(pick_ptr(), pick_ptr(), (float*)pick_ptr(), pick_int(), pick_int(), pick_int(),
+                                        pick_int(), pick_int(), pick_int(), nullptr, nullptr, pick_int(),
+                                        (float*)pick_ptr(), (int32_t*)pick_ptr(), pick_ptr(),
+                                        (long long)pick_int() * 64, nullptr);
                 break;
             default:
                 st = lix_topk_bf16(pick_ptr(), pick_int(), pick_int(), pick_int(), pick_int(), pick_ptr(),

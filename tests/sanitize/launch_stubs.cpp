@@ -24,5 +24,7 @@ hipError_t launch_fused_topk(const FusedArgs&) { return reached("launch_fused_to
 hipError_t launch_gather(const GatherArgs&) { return reached("launch_gather"); }
 hipError_t launch_v41_scores(const V41Args&) { return reached("launch_v41_scores"); }
 hipError_t noalloc_workspace(void**, long*) { return reached("noalloc_workspace"); }
+hipError_t launch_topk_streaming(const StreamArgs&) { return reached("launch_topk_streaming"); }
+hipError_t streaming_grid(int, int, int, int, long*) { return reached("streaming_grid"); }
 
 }  // namespace lix

@@ -28,7 +28,8 @@ def test_library_exports_every_declared_function():
     assert set(names) == {"lix_status_string", "lix_version", "lix_indexer_logits", "lix_topk",
                           "lix_topk_scores", "lix_indexer_scores_v41", "lix_indexer_scores_at", "lix_topk_bf16",
                           "lix_indexer_backward", "lix_indexer_backward_workspace_bytes",
-                          "lix_topk_fused_supported", "lix_indexer_backward_noalloc"}
+                          "lix_topk_fused_supported", "lix_indexer_backward_noalloc", "lix_topk_streaming",
+                          "lix_topk_streaming_workspace_bytes"}
     for name in names:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES
@@ -85,6 +86,35 @@ def topk_call(q=P, k=P, w=P, logits=None, B=1, S=8, Skv=4, H=64, D=128, c=4, ks=
 ])
 def test_topk_validation(kw, code):
     assert topk_call(**kw) == code
+
+
+def streaming_call(q=P, k=P, w=P, B=1, S=8, Skv=4, H=64, D=128, c=4, ks=None, ke=None, topk=2, scores=P, idx=P,
+                   ws=P, ws_bytes=1 << 20):
+    return lx.load().lix_topk_streaming(q, k, w, B, S, Skv, H, D, c, ks, ke, topk, scores, idx, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(w=None), NULL), (dict(scores=None), NULL),
+    (dict(idx=None), NULL), (dict(ws=None), NULL),
+    (dict(topk=0), SHAPE), (dict(topk=5), SHAPE), (dict(c=0), SHAPE), (dict(S=0), SHAPE), (dict(ks=P), SHAPE),
+    (dict(H=5), UNSUP), (dict(D=20), UNSUP), (dict(H=256), UNSUP),
+    (dict(Skv=8193, topk=16), UNSUP),              # a row must fit the in-register selection
+    (dict(Skv=8192, topk=8192, ws_bytes=4 * 8192 * 4), DEVICE),   # one slot of four queries (64 heads)
+    (dict(Skv=8192, topk=16, ws_bytes=4 * 8192 * 4 - 1), SHAPE),  # less than one slot
+    (dict(H=4, Skv=100, topk=50, ws_bytes=64 * 100 * 4), DEVICE),  # heads 4: 64 queries per block
+    (dict(H=4, Skv=100, topk=50, ws_bytes=64 * 100 * 4 - 4), SHAPE),
+    (dict(B=131072, S=8, D=128), UNSUP),           # key row stride
+    (dict(scores=P + 2), UNSUP), (dict(q=P + 4), UNSUP), (dict(ws=P + 128), UNSUP), (dict(ks=P + 1, ke=P), UNSUP),
+])
+def test_topk_streaming_validation(kw, code):
+    assert streaming_call(**kw) == code
+
+
+def test_streaming_workspace_bytes_rejects_unsupported_sizes():
+    f = lx.load().lix_topk_streaming_workspace_bytes
+    for args in ((0, 8, 4, 64, 128), (1, 8, 8193, 64, 128), (1, 8, 4, 48, 128), (1, 8, 4, 64, 24),
+                 (131072, 8, 4, 64, 128)):
+        assert f(*args) == -1, args
 
 
 # (heads, index_dim) -> largest topk of the fused path, as listed in include/lix.h

@@ -548,6 +548,9 @@ def test_32k_workload_sampled_rows():
     logits = lx.indexer_logits(q, k, w, 4)
     sc_m, ix_m = lx.topk_from_logits(logits, 4, tk)
     assert torch.equal(ix_f, ix_m) and torch.equal(sc_f, sc_m)
+    log("32k: streaming top-k")
+    sc_s, ix_s = lx.topk_streaming(q, k, w, 4, tk)
+    assert torch.equal(ix_s, ix_m) and torch.equal(sc_s, sc_m)
     rows = np.arange(31, S, 64)
     ks, ke = oracle.causal_ranges(S, Skv, 4)
     ora, mag = oracle.indexer_logits_rows(nb["q"], nb["k"], nb["w"], 0, rows, ks, ke, with_magnitude=True)
@@ -755,17 +758,89 @@ def test_fused_branches_bitwise_vs_materialized_and_oracle(name):
         assert np.array_equal(sc_f[b].cpu().numpy().astype(np.float64), want_s), (name, b)
 
 
-def test_select_topk_routes_unsupported_fused_shapes_to_the_materialized_path():
-    # heads 4 (no fused kernel) and heads 8 above its capacity: the pages' entry point still answers
-    for H, tk in ((4, 40), (8, 700)):
-        inp, nb = v4_case(1, 400, 1000, H, 64, seed=410 + H)
-        q, k, w = dev(inp["q"]), dev(inp["k"]), dev(inp["w"])
-        assert not lx.fused_topk_supported(1000, H, 64, tk)
-        sc, ix = lx.v4_lighting_indexer(q, k, w, 1, tk)
-        ks, ke = oracle.causal_ranges(400, 1000, 1)
-        rows = np.arange(400)
-        _check_topk_vs_oracle(sc[0].detach().cpu().numpy(), ix[0].cpu().numpy(), nb, 0, rows, ks, ke, tk,
-                              f"select_topk H={H}")
+@pytest.mark.parametrize("H,S,Skv,tk,route", [
+    (4, 400, 1000, 40, "streaming"),      # heads 4: no fused kernel
+    (8, 400, 1000, 700, "streaming"),     # heads 8 above the fused capacity
+    (4, 60, 9000, 100, "materialized"),   # past the streaming row limit, no fused kernel
+    (64, 60, 9000, 100, "fused"),
+])
+def test_select_topk_routes_every_size_to_a_route(H, S, Skv, tk, route):
+    # The pages' entry point answers for every size; each route gives the oracle's selection.
+    inp, nb = v4_case(1, S, Skv, H, 64, seed=410 + H + Skv)
+    q, k, w = dev(inp["q"]), dev(inp["k"]), dev(inp["w"])
+    assert (Skv <= 8192) == (route == "streaming")
+    assert lx.fused_topk_supported(Skv, H, 64, tk) == (route == "fused")
+    log(f"select_topk route {route}: H={H} S={S} Skv={Skv} topk={tk}")
+    sc, ix = lx.v4_lighting_indexer(q, k, w, 1, tk)
+    ks, ke = oracle.causal_ranges(S, Skv, 1)
+    rows = np.arange(S)
+    _check_topk_vs_oracle(sc[0].detach().cpu().numpy(), ix[0].cpu().numpy(), nb, 0, rows, ks, ke, tk,
+                          f"select_topk {route} H={H}")
+
+
+# ------------------------------------------------------------------ streaming top-k
+
+def _streaming_vs_materialized(q, k, w, c, tk, kd=None, ked=None, workspace=None):
+    sc_s, ix_s = lx.topk_streaming(q, k, w, c, tk, kd, ked, workspace=workspace)
+    logits = lx.indexer_logits(q, k, w, c, kd, ked)
+    sc_m, ix_m = lx.topk_from_logits(logits, c, tk, kd, ked)
+    assert torch.equal(ix_s, ix_m) and torch.equal(sc_s, sc_m)
+    return sc_s, ix_s, logits
+
+
+@pytest.mark.parametrize("H,D,B,S,Skv,c,tk", [
+    (64, 128, 1, 256, 64, 4, 16),       # tiny workload shape
+    (64, 128, 3, 333, 100, 3, 40),      # ragged tail in queries and keys; topk above early rows' length
+    (64, 128, 1, 3000, 2900, 1, 2048),
+    (128, 128, 2, 700, 3000, 1, 256),
+    (32, 64, 2, 900, 5000, 1, 1000),
+    (16, 32, 1, 500, 8192, 1, 4000),     # longest rows the route takes, topk half of them
+    (8, 256, 2, 300, 1200, 1, 700),
+    (4, 64, 1, 400, 1000, 1, 40),        # heads below 8: the other store layout
+    (1, 16, 2, 130, 300, 1, 299),
+])
+def test_streaming_topk_bitwise_vs_materialized_and_oracle(H, D, B, S, Skv, c, tk):
+    log(f"streaming H={H} D={D} B={B} S={S} Skv={Skv} c={c} topk={tk}")
+    inp, _ = v4_case(B, S, Skv, H, D, seed=500 + H + D + S)
+    q, k, w = dev(inp["q"]), dev(inp["k"]), dev(inp["w"])
+    sc, ix, logits = _streaming_vs_materialized(q, k, w, c, tk)
+    ksn, ken = oracle.causal_ranges(S, Skv, c)
+    lg = logits.cpu().numpy()
+    for b in range(B):
+        want_s, want_i = oracle.topk_select(lg[b].astype(np.float64), ksn, ken, tk)
+        assert np.array_equal(ix[b].cpu().numpy(), want_i), b
+        assert np.array_equal(sc[b].cpu().numpy().astype(np.float64), want_s), b
+
+
+@pytest.mark.parametrize("name", ["zero_weights", "zero_query_rows", "duplicate_keys", "small_integers",
+                                  "heads128_topk256", "heads8_capacity", "given_ranges"])
+def test_streaming_branch_cases_bitwise_vs_materialized(name):
+    inp, H, D, B, S, Skv, tk, ks, ke = _fused_case(name)
+    log(f"streaming branch case {name}: H={H} D={D} B={B} S={S} Skv={Skv} topk={tk}")
+    q, k, w = dev(inp["q"]), dev(inp["k"]), dev(inp["w"])
+    kd = None if ks is None else dev(ks)
+    ked = None if ke is None else dev(ke)
+    _streaming_vs_materialized(q, k, w, 1, tk, kd, ked)
+
+
+def test_streaming_small_workspaces():
+    # One slot (a grid of one workgroup walking every block), a few slots, and
+    # a workspace one byte short of a slot (rejected).
+    B, S, Skv, H, D, tk = 2, 600, 2000, 64, 128, 300
+    inp, _ = v4_case(B, S, Skv, H, D, seed=510)
+    q, k, w = dev(inp["q"]), dev(inp["k"]), dev(inp["w"])
+    slot = 4 * Skv * 4                       # four queries per block at 64 heads
+    for nslot in (1, 3, 7):
+        log(f"streaming workspace of {nslot} slots")
+        ws = torch.empty(nslot * slot, dtype=torch.uint8, device=DEV)
+        _streaming_vs_materialized(q, k, w, 1, tk, workspace=ws)
+    ws = torch.empty(slot - 1, dtype=torch.uint8, device=DEV)
+    with pytest.raises(lx.LixError):
+        lx.topk_streaming(q, k, w, 1, tk, workspace=ws)
+    full = lx.streaming_workspace_bytes(B, S, Skv, H, D)
+    n_blocks = 2 * ((S + 3) // 4)
+    assert full % slot == 0 and slot <= full <= n_blocks * slot
+    assert lx.streaming_workspace_bytes(B, S, 8193, H, D) == -1
 
 
 # ------------------------------------------------------------------ canaries around every output
@@ -801,6 +876,14 @@ def test_every_output_leaves_memory_around_it_untouched():
         rc = lib.lix_topk(q.data_ptr(), k.data_ptr(), w.data_ptr(), lp, B, S, Skv, H, D, c, None, None, tk,
                           so.data_ptr(), io.data_ptr(), st)
         assert rc == 0 and _intact(sbuf, n, F) and _intact(ibuf, n, I), route
+    ws_s = lib.lix_topk_streaming_workspace_bytes(B, S, Skv, H, D)
+    wbuf = torch.full((ws_s + 4096,), 0x5A, dtype=torch.uint8, device=DEV)
+    sbuf, so = _guarded(n, torch.float32, F)
+    ibuf, io = _guarded(n, torch.int32, I)
+    assert lib.lix_topk_streaming(q.data_ptr(), k.data_ptr(), w.data_ptr(), B, S, Skv, H, D, c, None, None, tk,
+                                  so.data_ptr(), io.data_ptr(), wbuf.data_ptr(), ws_s, st) == 0
+    assert _intact(sbuf, n, F) and _intact(ibuf, n, I), "streaming"
+    assert bool((wbuf[ws_s:] == 0x5A).all()), "streaming workspace"
     sbuf, so = _guarded(n, torch.float32, F)
     assert lib.lix_topk_scores(logits.data_ptr(), idx_given.data_ptr(), B, S, Skv, tk, so.data_ptr(), st) == 0
     assert _intact(sbuf, n, F), "gather"
