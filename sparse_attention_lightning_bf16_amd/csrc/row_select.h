@@ -261,29 +261,23 @@ __device__ __forceinline__ void select_row_binned(const RowIn<BF16>* __restrict_
         else return raw;
     };
     float x[NCH][4];
-    static_for<0, NCH>([&](auto jc) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) x[decltype(jc)::value][m] = qnan;   // chunks past the row
-    });
-    // Loads first (the partial chunk's addresses clamped into the row), then
-    // the partial chunk's slots past the row set to NaN in a pass of their
-    // own: consuming a loaded value before every chunk's loads are issued
-    // would make each chunk wait for the one before it.  (The masking is a
-    // select on bit patterns: a select of the two values lets the optimiser
-    // turn the load into a select of addresses, through a generic pointer and
-    // a private NaN.)
-    // (bf16 inputs: the raw 16 bits are loaded and converted in the second
-    // pass, for the same reason.)
-    visit_chunks<NCH, false>(jmax, jpart, [&](int j, auto partial) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int e = key_of(j, m);
-            const In raw = row[decltype(partial)::value ? min(e, n - 1) : e];
-            if constexpr (BF16) x[j][m] = __uint_as_float((uint32_t)raw);
-            else x[j][m] = raw;
-        }
-    });
     if constexpr (BF16) {
+        // The wave's chunks only (bf16 rows are whole rows of the V4.1
+        // scores): the raw 16 bits of every slot are loaded before any is
+        // used (the partial chunk's addresses clamped into the row), then
+        // converted, hidden keys and slots past the row becoming NaN (a select
+        // on bit patterns, which cannot turn into a select of addresses).
+        static_for<0, NCH>([&](auto jc) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) x[decltype(jc)::value][m] = qnan;   // chunks past the row
+        });
+        visit_chunks<NCH, false>(jmax, jpart, [&](int j, auto partial) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int e = key_of(j, m);
+                x[j][m] = __uint_as_float((uint32_t)row[decltype(partial)::value ? min(e, n - 1) : e]);
+            }
+        });
         visit_chunks<NCH, true>(jmax, jpart, [&](int j, auto) {
             const bool partial = j == jpart;
 #pragma unroll
@@ -293,11 +287,19 @@ __device__ __forceinline__ void select_row_binned(const RowIn<BF16>* __restrict_
             }
         });
     } else {
-        visit_chunks<NCH, false>(jmax, jpart, [&](int j, auto partial) {
-            if constexpr (decltype(partial)::value) {
+        // Every slot is loaded, at an address clamped into the row (n > topk
+        // >= 1 here), with no branch between the loads, so all of them are in
+        // flight before the first is used (loads under per-chunk branches are
+        // waited for chunk by chunk); slots past the row then become NaN.
+        static_for<0, NCH>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
 #pragma unroll
-                for (int m = 0; m < 4; ++m) x[j][m] = pick(key_of(j, m) < n, x[j][m], qnan);
-            }
+            for (int m = 0; m < 4; ++m) x[j][m] = row[min(key_of(j, m), n - 1)];
+        });
+        static_for<0, NCH>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) x[j][m] = pick(key_of(j, m) < n, x[j][m], qnan);
         });
     }
 

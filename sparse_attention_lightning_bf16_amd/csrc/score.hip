@@ -44,13 +44,18 @@ __device__ __forceinline__ void load_weights_f32(float (&wr)[T::NRT][16], const 
 // block's stage loop the workgroup selects each of its rows' top-k from the
 // slot (select_row_binned, the selection of the row top-k kernel; the rows
 // are still in L2) into scores / indices [B,S,topk].  Requires skv <= 8192.
+constexpr int logits_wg_waves(int H, int DP, bool select) { return select ? 4 : logits_waves(H, DP); }
+
 template <int H, int DP, bool SELECT>
-__global__ __launch_bounds__(256, stage_min_waves(H, DP)) void v4_logits_kernel(InLayout L, const float* __restrict__ w, int B, int S,
+using LogitsTiling = Tiling<H, DP, default_kt(H, DP), logits_wg_waves(H, DP, SELECT)>;
+
+template <int H, int DP, bool SELECT>
+__global__ __launch_bounds__(kWave * logits_wg_waves(H, DP, SELECT), stage_min_waves(H, DP)) void v4_logits_kernel(InLayout L, const float* __restrict__ w, int B, int S,
                                                         int skv, int ratio, const int32_t* __restrict__ ks,
                                                         const int32_t* __restrict__ ke, float* __restrict__ out,
                                                         int topk, float* __restrict__ scores,
                                                         int32_t* __restrict__ indices) {
-    using T = Tiling<H, DP>;
+    using T = LogitsTiling<H, DP, SELECT>;
     // The two stage buffers; in SELECT mode the selection state reuses them
     // (the array grows where it is larger than both).
     constexpr int kStages = 2 * T::STAGE_BYTES;
@@ -204,6 +209,7 @@ __global__ __launch_bounds__(256, stage_min_waves(H, DP)) void v4_logits_kernel(
             // The block's rows are in the slot (every store of the workgroup
             // has completed at the barrier); select each row's top-k.  The
             // selection state reuses the stage buffers.
+            static_assert(!SELECT || T::THREADS == kBinThreads, "the selection runs on the whole workgroup");
             BinShared& sh = *reinterpret_cast<BinShared*>(lds);
             for (int q = 0; q < T::QB; ++q) {
                 const int t = t0 + q;
@@ -486,7 +492,7 @@ __global__ __launch_bounds__(256, v41_min_waves(H, DP)) void v41_scores_kernel(I
 
 template <int H, int DP>
 static hipError_t launch_v4_logits_t(const LogitsArgs& p) {
-    using T = Tiling<H, DP>;
+    using T = LogitsTiling<H, DP, false>;
     InLayout L{static_cast<const uint16_t*>(p.q), (long)p.B * H * p.D, (long)H * p.D,
                static_cast<const uint16_t*>(p.k), (long)p.B * p.D, (long)p.D, p.D};
     const long nblk = (long)((p.S + T::QB - 1) / T::QB) * p.B;
@@ -500,7 +506,7 @@ static hipError_t launch_v4_logits_t(const LogitsArgs& p) {
 // at once on the device (occupancy x compute units), at most one per block.
 template <int H, int DP>
 static hipError_t streaming_grid_t(int B, int S, long* grid) {
-    using T = Tiling<H, DP>;
+    using T = LogitsTiling<H, DP, true>;
     int dev = 0, cus = 0, per_cu = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -515,7 +521,7 @@ static hipError_t streaming_grid_t(int B, int S, long* grid) {
 
 template <int H, int DP>
 static hipError_t launch_streaming_t(const StreamArgs& p) {
-    using T = Tiling<H, DP>;
+    using T = LogitsTiling<H, DP, true>;
     InLayout L{static_cast<const uint16_t*>(p.q), (long)p.B * H * p.D, (long)H * p.D,
                static_cast<const uint16_t*>(p.k), (long)p.B * p.D, (long)p.D, p.D};
     long grid = 0;

@@ -26,7 +26,7 @@ constexpr int default_kt(int H, int DP) { return (H <= 64 && DP <= 128) ? 128 : 
 // Waves per SIMD the register allocator is held to for those shapes.
 constexpr int stage_min_waves(int H, int DP) { return (H >= 16 && default_kt(H, DP) == 128) ? 2 : 1; }
 
-template <int H_, int DP_, int KT_ = default_kt(H_, DP_)>
+template <int H_, int DP_, int KT_ = default_kt(H_, DP_), int NW_ = 4>
 struct Tiling {
     static constexpr int H = H_;                    // heads (power of two, <= 128)
     static constexpr int DP = DP_;                  // index_dim padded up to 32/64/128/256
@@ -34,7 +34,7 @@ struct Tiling {
     static constexpr int ROWS = 32 * NRT;           // (query, head) rows per wave
     static constexpr int QW = ROWS / H;             // queries per wave
     static constexpr int NSTEP = DP / 16;           // MFMA k-steps over index_dim
-    static constexpr int NWAVE = 4;
+    static constexpr int NWAVE = NW_;               // waves per workgroup, one after another in query order
     static constexpr int THREADS = NWAVE * kWave;
     static constexpr int QB = QW * NWAVE;           // queries per workgroup
     static constexpr int KT = KT_;                  // keys per LDS stage
@@ -52,6 +52,12 @@ struct Tiling {
     static constexpr int slot(int r, int i) { return (32 * r + c_row(i, 0)) / H; }
     static constexpr int half_step() { return H >= 8 ? 0 : 4 / H; }
 };
+
+// Waves per workgroup of the logits kernel (lix_indexer_logits): where two
+// waves per SIMD fit, eight waves (one workgroup per CU) share each key stage,
+// which halves the key traffic from L2 into LDS against two workgroups of
+// four.  The streaming top-k keeps four (its selection runs on 256 threads).
+constexpr int logits_waves(int H, int DP) { return stage_min_waves(H, DP) == 2 ? 8 : 4; }
 
 // ---------------------------------------------------------------- fused top-k
 
