@@ -58,16 +58,17 @@ __device__ __forceinline__ int wave_incl_scan(int x, int /*lane*/) {
 // row whose score range is zero or not finite, falls back to a radix select
 // on order-preserving keys.
 constexpr int kBinCand = 256;
-constexpr int kBinThreads = 256;
-constexpr int kBinChunks = 32;                    // 256-key chunks per row (8192 keys)
+constexpr int kBinThreads = 256;                  // four waves: rows of up to 8192 keys
+constexpr int kBinMaxWaves = 16;                  // sixteen waves: rows of up to 32768 keys
+constexpr int kBinChunks = 128;                   // 256-key chunks per row (32768 keys)
 
 struct BinShared {
     alignas(16) uint32_t hist[kBins];
     alignas(16) float cand_v[kBinCand];
     alignas(16) int cand_i[kBinCand];
     int ccnt[kBinChunks];                         // per-chunk counts, row order
-    float wmin[4], wmax[4];
-    int wtot[4];
+    float wmin[kBinMaxWaves], wmax[kBinMaxWaves];
+    int wtot[kBinMaxWaves];
     int ncand;
     int bstar, rstar;
     float cut_v;
@@ -75,28 +76,31 @@ struct BinShared {
     int cut_ties;                                 // another key has score vT
 };
 
-// Block-wide: the bin holding the need-th largest element of hist[0..NB) and
-// the element's 1-based rank inside it, counted from the top, into sh.bstar /
-// sh.rstar.  Thread tid owns bins [BPT*tid, BPT*tid + BPT), read rotated by
-// tid so a wave's reads spread over the LDS banks; the suffix sums over lanes
-// come from a DPP prefix scan.  Every thread calls it; it ends with a
-// barrier.  Requires 1 <= need <= sum of hist.
-template <int NB>
+// Block-wide (NW waves): the bin holding the need-th largest element of
+// hist[0..NB) and the element's 1-based rank inside it, counted from the top,
+// into sh.bstar / sh.rstar.  Thread tid owns bins [BPT*tid, BPT*tid + BPT)
+// (none past the last bin), read rotated by tid so a wave's reads spread over
+// the LDS banks; the suffix sums over lanes come from a DPP prefix scan.
+// Every thread calls it; it ends with a barrier.  Requires 1 <= need <= sum
+// of hist.
+template <int NB, int NW>
 __device__ void block_find_bin(BinShared& sh, int need, int tid) {
-    constexpr int BPT = NB / kBinThreads;
+    constexpr int BPT = NB >= 64 * NW ? NB / (64 * NW) : 1;
     const int lane = tid & 63, wv = tid >> 6;
     const int base = BPT * tid;
     int local = 0;
+    if (base < NB) {
 #pragma unroll
-    for (int i = 0; i < BPT; ++i) local += (int)sh.hist[base + ((i + tid) & (BPT - 1))];
+        for (int i = 0; i < BPT; ++i) local += (int)sh.hist[base + ((i + tid) & (BPT - 1))];
+    }
     const int incl = wave_incl_scan(local, lane);
     const int wsum = __builtin_amdgcn_readlane(incl, 63);
     const int v = wsum - incl + local;               // inclusive suffix sum over lanes >= this one
     if (lane == 0) sh.wtot[wv] = wsum;
     __syncthreads();
     int above = v - local;
-    for (int w2 = wv + 1; w2 < 4; ++w2) above += sh.wtot[w2];
-    if (above < need && need <= above + local) {
+    for (int w2 = wv + 1; w2 < NW; ++w2) above += sh.wtot[w2];
+    if (base < NB && above < need && need <= above + local) {
         for (int i = BPT - 1; i >= 0; --i) {
             const int h = (int)sh.hist[base + i];
             if (need <= above + h) {
@@ -206,21 +210,23 @@ __device__ __forceinline__ int chunk_offset(const int (&off)[CPL], int cidx) {
 template <bool BF16>
 using RowIn = typename std::conditional<BF16, uint16_t, float>::type;
 
-// Top-k of one row by the whole workgroup (kBinThreads threads, all calling
-// together; it synchronises with barriers).  row: the n visible scores (key
-// lo + e at row[e]); so / io: the topk output slots.  n <= 1024 * NCH.
+// Top-k of one row by the whole workgroup (NW waves, all calling together; it
+// synchronises with barriers).  row: the n visible scores (key lo + e at
+// row[e]); so / io: the topk output slots.  n <= 256 * NW * NCH.
 // BF16 = false: fp32 logits of the causal or given ranges (lix_topk).
 // BF16 = true: V4.1 bf16 scores over whole rows, where bf16 -inf (0xFF80)
 // marks a hidden key: hidden keys are loaded as NaN slots, so they are
 // never binned, ranked or selected; a row with at most topk visible keys
 // selects all of them and pads the rest with (-1, bf16 -inf).  Selected
 // values are written back in the input's type, bit for bit.
-template <int NCH, bool BF16>
+template <int NCH, bool BF16, int NW = 4>
 __device__ __forceinline__ void select_row_binned(const RowIn<BF16>* __restrict__ row, int n, int lo, int topk,
                                                   RowIn<BF16>* __restrict__ so, int32_t* __restrict__ io,
                                                   BinShared& sh, int tid) {
-    static_assert(4 * NCH <= kBinChunks, "chunk table too small");
-    constexpr int CPL = (4 * NCH + 63) / 64;                  // chunks per lane in the chunk prefix
+    static_assert(NW * NCH <= kBinChunks && NW <= kBinMaxWaves, "chunk table too small");
+    static_assert(NW * 64 >= kBinCand, "one thread per boundary candidate");
+    constexpr int NT = 64 * NW;                               // threads of the workgroup
+    constexpr int CPL = (NW * NCH + 63) / 64;                 // chunks per lane in the chunk prefix
     using In = RowIn<BF16>;
     const int lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -232,26 +238,26 @@ __device__ __forceinline__ void select_row_binned(const RowIn<BF16>* __restrict_
 
     if constexpr (!BF16) {
         if (n <= topk) {                                      // everything is selected
-            for (int i0 = 0; i0 < n; i0 += 8 * kBinThreads) {
+            for (int i0 = 0; i0 < n; i0 += 8 * NT) {
                 float v[8];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) v[u] = row[min(i0 + u * kBinThreads + tid, n - 1)];
+                for (int u = 0; u < 8; ++u) v[u] = row[min(i0 + u * NT + tid, n - 1)];
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
-                    const int i = i0 + u * kBinThreads + tid;
+                    const int i = i0 + u * NT + tid;
                     if (i < n) { so[i] = v[u]; io[i] = lo + i; }
                 }
             }
-            for (int i = n + tid; i < topk; i += kBinThreads) { so[i] = pad_val; io[i] = -1; }
+            for (int i = n + tid; i < topk; i += NT) { so[i] = pad_val; io[i] = -1; }
             return;
         }
     }
 
     // ---- chunks: nch of the row, jmax of this wave, jpart the wave's partial one
     const int nch = (n + 255) >> 8;
-    const int jmax = (nch - wv + 3) >> 2;
-    const int jpart = (((nch - 1) & 3) == wv && (n & 255) != 0) ? (nch - 1) >> 2 : -1;
-    auto key_of = [&](int j, int m) { return (4 * j + wv) * 256 + 64 * m + lane; };   // key - lo
+    const int jmax = (nch - wv + NW - 1) / NW;
+    const int jpart = (((nch - 1) % NW) == wv && (n & 255) != 0) ? (nch - 1) / NW : -1;
+    auto key_of = [&](int j, int m) { return (NW * j + wv) * 256 + 64 * m + lane; };  // key - lo
     constexpr bool AP = BF16;                                 // bf16: hidden keys anywhere
 
     // ---- this wave's chunks (every load issues before the first use)
@@ -313,7 +319,9 @@ __device__ __forceinline__ void select_row_binned(const RowIn<BF16>* __restrict_
         });
         if (lane == 0) sh.wtot[wv] = c;
         __syncthreads();
-        visible = sh.wtot[0] + sh.wtot[1] + sh.wtot[2] + sh.wtot[3];
+        visible = 0;
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) visible += sh.wtot[w2];
         __syncthreads();                                      // wtot is reused below
     }
     const bool take_all = visible <= topk;                    // same in every thread
@@ -332,11 +340,13 @@ __device__ __forceinline__ void select_row_binned(const RowIn<BF16>* __restrict_
     }
     if (lane == 0) { sh.wmin[wv] = vmin; sh.wmax[wv] = vmax; }
 #pragma unroll
-    for (int i = 4 * tid; i < kBins; i += 4 * kBinThreads) *reinterpret_cast<uint4*>(&sh.hist[i]) = uint4{0u, 0u, 0u, 0u};
+    for (int i = 4 * tid; i < kBins; i += 4 * NT) *reinterpret_cast<uint4*>(&sh.hist[i]) = uint4{0u, 0u, 0u, 0u};
     if (tid == 0) sh.ncand = 0;
     __syncthreads();
-    vmin = fminf(fminf(sh.wmin[0], sh.wmin[1]), fminf(sh.wmin[2], sh.wmin[3]));
-    vmax = fmaxf(fmaxf(sh.wmax[0], sh.wmax[1]), fmaxf(sh.wmax[2], sh.wmax[3]));
+    vmin = sh.wmin[0];
+    vmax = sh.wmax[0];
+#pragma unroll
+    for (int w2 = 1; w2 < NW; ++w2) { vmin = fminf(vmin, sh.wmin[w2]); vmax = fmaxf(vmax, sh.wmax[w2]); }
     const float span = vmax - vmin;
     // (A span below 1e-30 would overflow the scale; such rows take the radix path.)
     const bool binned = span > 1.0e-30f && span < 3.0e38f;   // same in every thread
@@ -413,7 +423,7 @@ __device__ __forceinline__ void select_row_binned(const RowIn<BF16>* __restrict_
                 ccv = (lane == j) ? above : ccv;
             });
         });
-        if (lane < jmax) sh.ccnt[4 * lane + wv] = ccv;
+        if (lane < jmax) sh.ccnt[NW * lane + wv] = ccv;
         __syncthreads();
         if (tid < cb) {
             // rank = candidates before this one in (score desc, key asc);
@@ -446,7 +456,7 @@ __device__ __forceinline__ void select_row_binned(const RowIn<BF16>* __restrict_
         uint32_t prefix = 0, pmask = 0;
         int need = rstar;
         for (int shift = 24; shift >= 0; shift -= 8) {
-            for (int i = tid; i < 256; i += kBinThreads) sh.hist[i] = 0u;
+            for (int i = tid; i < 256; i += NT) sh.hist[i] = 0u;
             __syncthreads();
             with_form([&](auto one) {
                 visit_chunks<NCH, true>(jmax, jpart, [&](int j, auto) {
@@ -460,7 +470,7 @@ __device__ __forceinline__ void select_row_binned(const RowIn<BF16>* __restrict_
                 });
             });
             __syncthreads();
-            block_find_bin<256>(sh, need, tid);
+            block_find_bin<256, NW>(sh, need, tid);
             prefix |= (uint32_t)sh.bstar << shift;
             pmask |= 255u << shift;
             need = sh.rstar;
@@ -473,13 +483,13 @@ __device__ __forceinline__ void select_row_binned(const RowIn<BF16>* __restrict_
             int c = 0;
 #pragma unroll
             for (int m = 0; m < 4; ++m) c += __popcll(__ballot(x[j][m] == vt));
-            if (lane == 0) sh.ccnt[4 * j + wv] = c;
+            if (lane == 0) sh.ccnt[NW * j + wv] = c;
         });
         __syncthreads();
         int total_eq, off[CPL];
         chunk_offsets<CPL>(sh, nch, lane, off, &total_eq);
         visit_chunks<NCH, true>(jmax, jpart, [&](int j, auto) {
-            int run = chunk_offset<CPL>(off, 4 * j + wv);
+            int run = chunk_offset<CPL>(off, NW * j + wv);
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const unsigned long long mask = __ballot(x[j][m] == vt);
@@ -525,12 +535,12 @@ __device__ __forceinline__ void select_row_binned(const RowIn<BF16>* __restrict_
                 ccv = (lane == j) ? c : ccv;
             });
         });
-        if (lane < jmax) sh.ccnt[4 * lane + wv] = ccv;
+        if (lane < jmax) sh.ccnt[NW * lane + wv] = ccv;
         __syncthreads();
     }
     int total, off[CPL];
     chunk_offsets<CPL>(sh, nch, lane, off, &total);
-    const int key0 = lo + lane + 256 * wv;
+    const int key0 = lo + lane + 256 * wv;                    // key of slot (j, m): key0 + 256 NW j + 64 m
     char* so_b = reinterpret_cast<char*>(so);
     char* io_b = reinterpret_cast<char*>(io);
     {
@@ -538,7 +548,7 @@ __device__ __forceinline__ void select_row_binned(const RowIn<BF16>* __restrict_
         const int iT = sh.cut_i;
         with_ties(sh.cut_ties != 0, [&](auto tie) {
             visit_chunks<NCH, AP>(jmax, jpart, [&](int j, auto) {
-                int run = chunk_offset<CPL>(off, 4 * j + wv);
+                int run = chunk_offset<CPL>(off, NW * j + wv);
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const bool f = selected(tie, j, m, vT, iT);
@@ -546,14 +556,14 @@ __device__ __forceinline__ void select_row_binned(const RowIn<BF16>* __restrict_
                     const uint32_t pos = (uint32_t)mbcnt(mask, run);
                     if (f && pos < (uint32_t)topk) {
                         *reinterpret_cast<In*>(so_b + pos * (uint32_t)sizeof(In)) = out_val(x[j][m]);
-                        *reinterpret_cast<int32_t*>(io_b + pos * 4u) = key0 + 1024 * j + 64 * m;
+                        *reinterpret_cast<int32_t*>(io_b + pos * 4u) = key0 + 256 * NW * j + 64 * m;
                     }
                     run += __popcll(mask);
                 }
             });
         });
     }
-    for (int i = total + tid; i < topk; i += kBinThreads) { so[i] = pad_val; io[i] = -1; }
+    for (int i = total + tid; i < topk; i += NT) { so[i] = pad_val; io[i] = -1; }
 }
 
 }  // namespace lix

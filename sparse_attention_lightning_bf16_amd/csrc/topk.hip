@@ -535,9 +535,9 @@ __global__ __launch_bounds__(kRowThreads, MINB) void topk_rows_reg_kernel(
     }
 }
 
-// One workgroup per row of materialized scores (select_row_binned).
-template <int NCH, bool BF16>
-__global__ __launch_bounds__(kBinThreads) void topk_rows_bin_kernel(const void* __restrict__ logits_v, int B, int S,
+// One workgroup of NW waves per row of materialized scores (select_row_binned).
+template <int NCH, bool BF16, int NW>
+__global__ __launch_bounds__(64 * NW) void topk_rows_bin_kernel(const void* __restrict__ logits_v, int B, int S,
                                                                     int skv, int ratio,
                                                                     const int32_t* __restrict__ ks,
                                                                     const int32_t* __restrict__ ke, int topk,
@@ -552,7 +552,7 @@ __global__ __launch_bounds__(kBinThreads) void topk_rows_bin_kernel(const void* 
     const In* row = static_cast<const In*>(logits_v) + ((long)b * S + t) * skv + lo;
     In* so = static_cast<In*>(scores_v) + ((long)b * S + t) * topk;
     int32_t* io = indices + ((long)b * S + t) * topk;
-    select_row_binned<NCH, BF16>(row, hi - lo, lo, topk, so, io, sh, threadIdx.x);
+    select_row_binned<NCH, BF16, NW>(row, hi - lo, lo, topk, so, io, sh, threadIdx.x);
 }
 
 __global__ __launch_bounds__(256) void gather_kernel(const float* __restrict__ logits,
@@ -577,15 +577,20 @@ static void launch_reg(const TopkArgs& p) {
 hipError_t launch_topk_rows(const TopkArgs& p) {
     // Measured on MI355X: one register-resident wave per row wins for rows of
     // up to 2048 keys; rows up to 8192 keys go to the binned workgroup kernel
-    // (the row in registers), longer ones to the radix kernel that re-reads
-    // the row.  The two-wave register variant (WPR = 2) measured slower at
-    // 8192 keys and is not used.
+    // (the row in the registers of four waves), up to 32768 keys to the same
+    // kernel with sixteen waves (one workgroup per CU), longer ones to the
+    // radix kernel that re-reads the row.  The two-wave register variant
+    // (WPR = 2) measured slower at 8192 keys and is not used.
     if (p.Skv <= 2048) {
         launch_reg<8, 1, 4>(p);
     } else {
         dim3 grid((unsigned)((long)p.B * p.S));
         if (p.Skv <= 8192)
-            hipLaunchKernelGGL((topk_rows_bin_kernel<8, false>), grid, dim3(kBinThreads), 0, p.stream,
+            hipLaunchKernelGGL((topk_rows_bin_kernel<8, false, 4>), grid, dim3(256), 0, p.stream,
+                               static_cast<const void*>(p.logits), p.B, p.S, p.Skv, p.ratio, p.ks, p.ke, p.topk,
+                               static_cast<void*>(p.scores), p.indices);
+        else if (p.Skv <= 32768)
+            hipLaunchKernelGGL((topk_rows_bin_kernel<8, false, 16>), grid, dim3(1024), 0, p.stream,
                                static_cast<const void*>(p.logits), p.B, p.S, p.Skv, p.ratio, p.ks, p.ke, p.topk,
                                static_cast<void*>(p.scores), p.indices);
         else
@@ -597,7 +602,7 @@ hipError_t launch_topk_rows(const TopkArgs& p) {
 
 hipError_t launch_topk_bf16(const TopkBf16Args& p) {
     dim3 grid((unsigned)((long)p.B * p.L));
-    hipLaunchKernelGGL((topk_rows_bin_kernel<8, true>), grid, dim3(kBinThreads), 0, p.stream, p.scores, p.B, p.L,
+    hipLaunchKernelGGL((topk_rows_bin_kernel<8, true, 4>), grid, dim3(256), 0, p.stream, p.scores, p.B, p.L,
                        p.G, 1, nullptr, nullptr, p.topk, p.out_scores, p.indices);
     return hipGetLastError();
 }

@@ -182,14 +182,17 @@ def test_topk_ties_and_padding_bitwise():
             assert np.array_equal(sc[b].astype(np.float64), want_s), tk
 
 
-def test_topk_long_rows_from_logits():
-    # rows longer than the register cache of the row kernel (re-read path)
+@pytest.mark.parametrize("Skv", [20000, 40000])
+def test_topk_long_rows_from_logits(Skv):
+    # rows of the sixteen-wave register kernel (up to 32768 keys) and of the
+    # radix kernel that re-reads the row (longer)
     g = torch.Generator().manual_seed(10)
-    B, S, Skv, tk = 1, 12, 20000, 700
+    B, S, tk = 1, 12, 700
+    step = Skv // 11
     lg = torch.randn(B, S, Skv, generator=g)
     sc, ix = lx.topk_from_logits(dev(lg), 1, tk, dev(torch.zeros(S, dtype=torch.int32)),
-                                 dev(torch.arange(S, dtype=torch.int32) * 1800))
-    want_s, want_i = oracle.topk_select(lg[0].numpy().astype(np.float64), np.zeros(S, int), np.arange(S) * 1800, tk)
+                                 dev(torch.arange(S, dtype=torch.int32) * step))
+    want_s, want_i = oracle.topk_select(lg[0].numpy().astype(np.float64), np.zeros(S, int), np.arange(S) * step, tk)
     assert np.array_equal(ix.cpu().numpy()[0], want_i)
     assert np.array_equal(sc.cpu().numpy()[0].astype(np.float64), want_s)
 
@@ -560,7 +563,7 @@ def test_32k_workload_sampled_rows():
     log(f"  32k: rows with a forced exact set: {exact}/{len(rows)}")
 
 
-def test_131k_workload_fused_sampled_rows():
+def test_131k_workload_fused_and_materialized_sampled_rows():
     cfg = synth.WORKLOADS["131k"]
     S, Skv, tk = cfg["seqlen"], cfg["seqlen_kv"], cfg["topk"]
     log("131k: generating inputs")
@@ -576,6 +579,10 @@ def test_131k_workload_fused_sampled_rows():
     exact = checkers.check_topk_rows(sc[0].cpu().numpy()[rows], ix[0].cpu().numpy()[rows], ora, mag,
                                      ks[rows], ke[rows], tk, "131k")
     log(f"  131k: rows with a forced exact set: {exact}/{len(rows)}")
+    log("131k: materialized logits (16 GiB) + row top-k")
+    logits = lx.indexer_logits(q, k, w, 4)
+    sc_m, ix_m = lx.topk_from_logits(logits, 4, tk)
+    assert torch.equal(ix_m, ix) and torch.equal(sc_m, sc)
 
 
 def test_v41_workload_sampled_rows():
@@ -649,7 +656,7 @@ def test_device_properties_logged():
     assert "gfx950" in getattr(p, "gcnArchName", "gfx950")
 
 
-@pytest.mark.parametrize("Skv", [300, 2048, 3000, 4096, 6000, 8192])
+@pytest.mark.parametrize("Skv", [300, 2048, 3000, 4096, 6000, 8192, 9000, 20000, 32768])
 def test_topk_from_logits_edge_rows_bitwise(Skv):
     # Every size class of the row kernel, with rows that stress each branch:
     # all-equal scores (degenerate range), a few distinct values (large
