@@ -53,7 +53,7 @@ namespace {
 
 constexpr int kBwWaitVmcnt0 = 0x0F70;     // s_waitcnt vmcnt(0), expcnt/lgkmcnt untouched
 constexpr int kKeysPerGroup = 256;        // keys per dk workgroup (64 per wave)
-constexpr int kQueryChunk = 512;          // queries per dk workgroup
+constexpr int kQueryChunk = 128;          // queries per dk workgroup
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
     return (uint32_t)bf16_bits(lo) | ((uint32_t)bf16_bits(hi) << 16);
@@ -66,6 +66,54 @@ __device__ __forceinline__ uint32_t mask_pair(uint32_t v, float a_lo, float a_hi
 }
 
 typedef __attribute__((address_space(1))) float gfloat;
+
+// Work items of the dk kernel, (query chunk z, batch b, key group kg), in the
+// order the workgroups take them.  Workgroups go to the eight XCDs in turn
+// (flat id i to XCD i % 8); XCD x takes the query chunks z = x, x + 8, ...,
+// each with every key group that chunk can see, so the workgroups running on
+// one XCD at a time are mostly the key groups of one query chunk and share
+// that chunk's q through the XCD's L2.  Causal ranges: a chunk sees the key
+// groups below its last query's range end; given ranges: all of them.
+constexpr int kXcds = 8;
+
+__host__ __device__ inline int dk_groups_seen(int z, int S, int skv, int ratio, bool causal, int nkg) {
+    if (!causal) return nkg;
+    const int t1 = min(S, (z + 1) * kQueryChunk);
+    const int hi = min(skv, t1 / ratio);
+    return (hi + kKeysPerGroup - 1) / kKeysPerGroup;
+}
+
+__host__ __device__ inline bool dk_item(long i, int B, int S, int skv, int ratio, bool causal, int& z, int& b,
+                                        int& kg) {
+    const int nkg = (skv + kKeysPerGroup - 1) / kKeysPerGroup;
+    const int nz = (S + kQueryChunk - 1) / kQueryChunk;
+    long m = i / kXcds;
+    for (int zz = (int)(i % kXcds); zz < nz; zz += kXcds) {
+        const int nv = dk_groups_seen(zz, S, skv, ratio, causal, nkg);
+        const long cnt = (long)nv * B;
+        if (m < cnt) {
+            z = zz;
+            b = (int)(m / nv);
+            kg = (int)(m % nv);
+            return true;
+        }
+        m -= cnt;
+    }
+    return false;
+}
+
+// Flat grid of the dk kernel: eight times the longest XCD list.
+inline long dk_grid(int B, int S, int skv, int ratio, bool causal) {
+    const int nkg = (skv + kKeysPerGroup - 1) / kKeysPerGroup;
+    const int nz = (S + kQueryChunk - 1) / kQueryChunk;
+    long longest = 0;
+    for (int x = 0; x < kXcds; ++x) {
+        long n = 0;
+        for (int z = x; z < nz; z += kXcds) n += (long)dk_groups_seen(z, S, skv, ratio, causal, nkg) * B;
+        longest = n > longest ? n : longest;
+    }
+    return longest * kXcds;
+}
 
 }  // namespace
 
@@ -138,42 +186,47 @@ __global__ __launch_bounds__(64) void qt_fragments_kernel(const uint16_t* __rest
 
 // ---------------------------------------------------------------- 3. dq, dw (query-major)
 
-// dq accumulators (H x DP fp32 per query) plus the q fragments need more than
-// 256 registers at 64 heads and index_dim 128: one wave per SIMD there.
-constexpr int rows_min_waves(int H, int DP) { return (H > 32 && DP > 64) ? 1 : 2; }
+// One wave per (query, group of up to 32 heads): the wave's dq accumulators
+// (32 x DP fp32) and q fragments leave room for two waves per SIMD.  The
+// waves of one query gather the same key blocks (from L2: k is small).
+constexpr int rows_heads(int H) { return H > 32 ? 32 : H; }
 
 template <int H, int DP>
-__global__ __launch_bounds__(64, rows_min_waves(H, DP)) void backward_rows_kernel(InLayout L, const float* __restrict__ w,
+__global__ __launch_bounds__(64, 2) void backward_rows_kernel(InLayout L, const float* __restrict__ w,
                                                              const int32_t* __restrict__ indices,
                                                              const float* __restrict__ grad, int B, int S, int skv,
                                                              int ratio, const int32_t* __restrict__ ks,
                                                              const int32_t* __restrict__ ke, int topk,
                                                              float* __restrict__ dq, float* __restrict__ dw) {
-    using T = BwTiling<H, DP>;
+    constexpr int HW = rows_heads(H);                // heads of this wave: h0 .. h0 + HW - 1
+    constexpr int NHG = H / HW;                      // head groups per query
+    using T = BwTiling<HW, DP>;
     using M = BlockMap<DP>;
     __shared__ __attribute__((aligned(16))) uint8_t buf0[M::BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t buf1[M::BYTES];
     __shared__ __attribute__((aligned(16))) float stage_g[32];
 
     const int lane = threadIdx.x, hf = lane >> 5, l32 = lane & 31;
-    const int b = blockIdx.x % B, t = blockIdx.x / B;
+    const int h0 = HW * (int)(blockIdx.x % NHG);
+    const int row = (int)(blockIdx.x / NHG);
+    const int b = row % B, t = row / B;
     const int D = L.D;
     int lo, hi;
     key_range(ks, ke, t, S, skv, ratio, lo, hi);
 
-    // Q fragments: a[r][st] = q[head 32r + lane%32][16 st + 8 hf .. +7]; heads >= H
-    // and index_dim entries >= D are zero.
+    // Q fragments: a[r][st] = q[head h0 + 32r + lane%32][16 st + 8 hf .. +7];
+    // heads past the wave's group and index_dim entries >= D are zero.
     bf16x8 a[T::NRT][T::NSTEP];
     const uint16_t* qrow = L.q + (long)t * L.q_t + (long)b * L.q_b;
 #pragma unroll
     for (int r = 0; r < T::NRT; ++r) {
-        const int h = 32 * r + l32;
+        const int h = h0 + 32 * r + l32;
         const uint16_t* base = qrow + (long)min(h, H - 1) * D;
 #pragma unroll
         for (int st = 0; st < T::NSTEP; ++st) {
             const int d0 = 16 * st + 8 * hf;
             u32x4 v = *reinterpret_cast<const u32x4*>(base + min(d0, D - 8));
-            if (!(h < H && d0 < D)) v = u32x4{0u, 0u, 0u, 0u};
+            if (!(32 * r + l32 < HW && d0 < D)) v = u32x4{0u, 0u, 0u, 0u};
             a[r][st] = as_bf16x8(v);
         }
     }
@@ -305,8 +358,8 @@ __global__ __launch_bounds__(64, rows_min_waves(H, DP)) void backward_rows_kerne
     for (int r = 0; r < T::NRT; ++r)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int h = 32 * r + c_row(i, hf);
-            if (H < 32 && h >= H) continue;
+            const int hl = 32 * r + c_row(i, hf), h = h0 + hl;
+            if (HW < 32 && hl >= HW) continue;
             const float wh = wrow[min(h, H - 1)];
 #pragma unroll
             for (int dt = 0; dt < T::NDT; ++dt) {
@@ -318,8 +371,8 @@ __global__ __launch_bounds__(64, rows_min_waves(H, DP)) void backward_rows_kerne
 #pragma unroll
     for (int r = 0; r < T::NRT; ++r) {
         const float v = xor32_add(dwacc[r]);
-        const int h = 32 * r + l32;
-        if (hf == 0 && h < H) dw[((long)t * B + b) * H + h] = v;
+        const int hl = 32 * r + l32;
+        if (hf == 0 && hl < HW) dw[((long)t * B + b) * H + h0 + hl] = v;
     }
 }
 
@@ -352,15 +405,16 @@ __global__ __launch_bounds__(256, 1) void dk_keys_kernel(InLayout L, const float
     static_assert((T::NRT * T::NSTEP) % 4 == 0 && (T::NHS * T::NDT) % 4 == 0, "blocks split over 4 waves");
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
-    const int b = blockIdx.y;
-    const int s_group = blockIdx.x * kKeysPerGroup;
+    int zc, b, kg;
+    if (!dk_item(blockIdx.x, B, S, skv, ratio, ks == nullptr, zc, b, kg)) return;   // uniform: before any barrier
+    const int s_group = kg * kKeysPerGroup;
     const int s_wave = s_group + 64 * wave;                          // this wave's first key
     const int D = L.D;
     const int dlim = (D >> 3) - 1;
 
     // Queries of this workgroup; with causal ranges no query before
     // ratio * (first key) - 1 sees any of its keys.
-    int t0 = blockIdx.z * kQueryChunk;
+    int t0 = zc * kQueryChunk;
     const int t1 = min(S, t0 + kQueryChunk);
     if (ks == nullptr) t0 = (int)max((long)t0, (long)ratio * s_group - 1);
     if (t0 >= t1) return;                                  // uniform: before any barrier
@@ -548,11 +602,11 @@ static hipError_t launch_backward_t(const BackwardArgs& p) {
                        p.B, p.S, p.Skv, p.ratio, p.ks, p.ke, p.topk, G);
     hipLaunchKernelGGL((qt_fragments_kernel<H, DP>), dim3(rows), dim3(kWave), 0, p.stream,
                        static_cast<const uint16_t*>(p.q), p.D, qtf);
-    hipLaunchKernelGGL((backward_rows_kernel<H, DP>), dim3(rows), dim3(kWave), 0, p.stream, L, p.w, p.indices,
+    hipLaunchKernelGGL((backward_rows_kernel<H, DP>), dim3(rows * (unsigned)(H / rows_heads(H))), dim3(kWave), 0,
+                       p.stream, L, p.w, p.indices,
                        p.grad, p.B, p.S, p.Skv, p.ratio, p.ks, p.ke, p.topk, p.dq, p.dw);
-    const dim3 grid((unsigned)((p.Skv + kKeysPerGroup - 1) / kKeysPerGroup), (unsigned)p.B,
-                    (unsigned)((p.S + kQueryChunk - 1) / kQueryChunk));
-    hipLaunchKernelGGL((dk_keys_kernel<H, DP>), grid, dim3(256), 0, p.stream, L, p.w, G, qtf, p.B, p.S, p.Skv,
+    const long grid = dk_grid(p.B, p.S, p.Skv, p.ratio, p.ks == nullptr);
+    hipLaunchKernelGGL((dk_keys_kernel<H, DP>), dim3((unsigned)grid), dim3(256), 0, p.stream, L, p.w, G, qtf, p.B, p.S, p.Skv,
                        p.ratio, p.ks, p.ke, p.dk);
     return hipGetLastError();
 }
