@@ -243,10 +243,12 @@ int lix_indexer_scores_at(const void* q, const void* k, const float* w, const in
  * bf16 rounding, as a bf16 autograd graph of the forward would: the upstream
  * factor is rounded (g for dq, w applied in fp32 afterwards; the summed g of a
  * (query, key) pair times w_h for dk) and multiplies the exact bf16 k or q;
- * the products accumulate in fp32.  dk is a sum over
- * queries computed key-major (one partial per 256 keys and 512 queries, added
- * with fp32 atomics), so its low bits may vary from run to run; dq and dw are
- * deterministic.
+ * the products accumulate in fp32.  The ReLU masks m_h come from one
+ * recompute of d per entry and serve dq, dw and dk alike.  dk is a sum over
+ * queries computed key-major (one partial per 256 keys and 128 queries, added
+ * with fp32 atomics; a key listed more than once in a row has its g summed
+ * with LDS atomics first), so its low bits may vary from run to run; dq and
+ * dw are deterministic.
  *
  *   q, k, w      as in lix_indexer_logits; heads H <= 64, 32 < D <= 128, Skv <= 32768
  *   indices      int32 [B, S, topk]  (any values)
@@ -255,7 +257,8 @@ int lix_indexer_scores_at(const void* q, const void* k, const float* w, const in
  *   dk           fp32  [Skv, B, D]     out (cleared by the call, 16-byte aligned)
  *   dw           fp32  [S, B, H]       out (every element written)
  *   workspace    device memory of at least lix_indexer_backward_workspace_bytes
- *                bytes, 256-byte aligned, owned by the caller; its contents on
+ *                (for the same topk) bytes, 256-byte aligned, owned by the
+ *                caller; its contents on
  *                entry do not matter and on return are unspecified.  A smaller
  *                workspace_bytes: LIX_ERR_SHAPE.
  * Other H, D or Skv: LIX_ERR_UNSUPPORTED.
@@ -268,12 +271,15 @@ int lix_indexer_backward(const void* q, const void* k, const float* w, const int
 
 /*
  * lix_indexer_backward_workspace_bytes - device workspace lix_indexer_backward
- * needs for these sizes: the dense upstream gradient [B, S, Skv] fp32 (written
- * over each query's range only) plus q re-laid for the dk product
- * (S*B*heads*index_dim*2 bytes, heads padded to 32 or 64, index_dim to 64 or
- * 128).  -1 when the sizes are outside what lix_indexer_backward accepts.
+ * needs for these sizes: q re-laid for the dk product (S*B*heads*index_dim*2
+ * bytes, heads padded to 32 or 64, index_dim to 64 or 128), the ReLU masks of
+ * every entry (B*S*topk*4 bytes per 32 heads), the entries bucketed by groups
+ * of 64 keys (B*S*topk*16 bytes) and the bucket bounds (B*S*(Skv/64 + 1)*4
+ * bytes), each part rounded up to 256 bytes: linear in topk and in Skv/64,
+ * with no [B, S, Skv] term.  -1 when the sizes are outside what
+ * lix_indexer_backward accepts.
  */
-long long lix_indexer_backward_workspace_bytes(int B, int S, int Skv, int H, int D);
+long long lix_indexer_backward_workspace_bytes(int B, int S, int Skv, int H, int D, int topk);
 
 /*
  * lix_indexer_backward_noalloc - lix_indexer_backward without a workspace

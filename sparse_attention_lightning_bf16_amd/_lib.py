@@ -33,7 +33,7 @@ SIGNATURES = {
     "lix_topk_bf16": (_I, [_P, _I, _I, _I, _I, _P, _P, _P]),
     "lix_indexer_backward": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P, _P, _LL,
                                   _P]),
-    "lix_indexer_backward_workspace_bytes": (_LL, [_I, _I, _I, _I, _I]),
+    "lix_indexer_backward_workspace_bytes": (_LL, [_I, _I, _I, _I, _I, _I]),
     "lix_indexer_backward_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P,
                                           _P]),
 }

@@ -210,9 +210,9 @@ int lix_indexer_scores_at(const void* q, const void* k, const float* w, const in
     return launch_status(lix::launch_sparse_scores(a));
 }
 
-long long lix_indexer_backward_workspace_bytes(int B, int S, int Skv, int H, int D) {
-    if (check_dims_backward(B, S, Skv, H, D, 1, nullptr, nullptr, 1) != LIX_OK) return -1;
-    return lix::backward_workspace_bytes(B, S, Skv, H, D);
+long long lix_indexer_backward_workspace_bytes(int B, int S, int Skv, int H, int D, int topk) {
+    if (check_dims_backward(B, S, Skv, H, D, 1, nullptr, nullptr, topk) != LIX_OK) return -1;
+    return lix::backward_workspace_bytes(B, S, Skv, H, D, topk);
 }
 
 int lix_indexer_backward(const void* q, const void* k, const float* w, const int32_t* indices,
@@ -222,7 +222,7 @@ int lix_indexer_backward(const void* q, const void* k, const float* w, const int
     if (!q || !k || !w || !indices || !grad_scores || !dq || !dk || !dw || !workspace) return LIX_ERR_NULL;
     int st = check_dims_backward(B, S, Skv, H, D, compress_ratio, ks, ke, topk);
     if (st != LIX_OK) return st;
-    if (workspace_bytes < lix::backward_workspace_bytes(B, S, Skv, H, D)) return LIX_ERR_SHAPE;
+    if (workspace_bytes < lix::backward_workspace_bytes(B, S, Skv, H, D, topk)) return LIX_ERR_SHAPE;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(w, 4) || !aligned(indices, 4) || !aligned(grad_scores, 4) ||
         !aligned(dq, 4) || !aligned(dk, 16) || !aligned(dw, 4) || !aligned(ks, 4) || !aligned(ke, 4) ||
         !aligned(workspace, 256))
@@ -241,7 +241,8 @@ int lix_indexer_backward_noalloc(const void* q, const void* k, const float* w, c
     if (!q || !k || !w || !indices || !grad_scores || !dq || !dk || !dw) return LIX_ERR_NULL;
     int st = check_dims_backward(B, S, Skv, H, D, compress_ratio, ks, ke, topk);
     if (st != LIX_OK) return st;
-    if (lix::backward_workspace_bytes(B, S, Skv, H, D) > (long)LIX_NOALLOC_SCRATCH_BYTES) return LIX_ERR_UNSUPPORTED;
+    if (lix::backward_workspace_bytes(B, S, Skv, H, D, topk) > (long)LIX_NOALLOC_SCRATCH_BYTES)
+        return LIX_ERR_UNSUPPORTED;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(w, 4) || !aligned(indices, 4) || !aligned(grad_scores, 4) ||
         !aligned(dq, 4) || !aligned(dk, 16) || !aligned(dw, 4) || !aligned(ks, 4) || !aligned(ke, 4))
         return LIX_ERR_UNSUPPORTED;

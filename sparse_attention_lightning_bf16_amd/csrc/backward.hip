@@ -14,26 +14,28 @@
 //
 // dq and dw are sums over a query's own entries; dk is a sum over the queries
 // that selected a key.  Each is computed where its sum is local, so no output
-// element is accumulated with per-entry atomics:
+// element is accumulated with per-entry atomics, and every workspace array is
+// sized by the entries (B*S*topk) or by groups of 64 keys, never by B*S*Skv:
 //
-//   1. grad_scatter_kernel: the dense upstream gradient G[b,t,s] (sum of g over
-//      the valid entries of (b,t) naming key s), written over each query's
-//      range [ks, ke) only (workspace).
-//   2. qt_fragments_kernel: q (bf16, exact) laid out as the B fragments of
+//   1. qt_fragments_kernel: q (bf16, exact) laid out as the B fragments of
 //      the dk product (workspace), so a workgroup can move them into LDS with
 //      direct loads.
-//   3. backward_rows_kernel (query-major, one wave per query, the gathered
-//      32-key blocks of the scores-at kernel): d^T = K Q^T recomputed per block
-//      (lanes are heads, accumulator rows keys); dw += g relu(d^T) per lane;
-//      dq += (m g) K, whose A operand comes straight from d^T's accumulators and
-//      whose B operand is the gathered block read key-major; dq stays in
-//      registers for the whole row and is scaled by w at the end.
-//   4. dk_keys_kernel (key-major): a workgroup owns 256 keys (64 per wave, their
-//      K fragments in registers) and streams the queries that can see them:
-//      per query, q in A-fragment order and its dk fragments are moved into LDS
-//      (three-stage rotation, one barrier per query), D = Q K^T is recomputed
-//      (lanes are keys, rows heads), and dk += bf16(m G w) Q accumulates in
-//      registers; the workgroup's partial is added to dk once at the end.
+//   2. backward_rows_kernel (query-major, one wave per query and group of 32
+//      heads, the gathered 32-key blocks of the scores-at kernel): d^T = K Q^T
+//      recomputed per block (lanes are heads, accumulator rows keys); dw += g
+//      relu(d^T) per lane; dq += (m g) K, whose A operand comes straight from
+//      d^T's accumulators and whose B operand is the gathered block read
+//      key-major; dq stays in registers for the whole row and is scaled by w at
+//      the end.  Each entry's ReLU mask (one bit per head) goes to the
+//      workspace.
+//   3. bucket_entries_kernel: each row's valid entries {key, g, masks} sorted
+//      into buckets of 64 keys (workspace).
+//   4. dk_entries_kernel (key-major): a workgroup owns 256 keys (64 per wave)
+//      and streams the queries that can see them; per query, each wave turns
+//      its bucket into the A operand bf16(G w_h m_h) of its 64 keys (G the
+//      summed g of a key) and dk += A Q accumulates in registers, with no
+//      second recompute of q . k; the workgroup's partial is added to dk once
+//      at the end.
 //
 // Every term of a gradient product carries one bfloat16 rounding, the one a
 // bfloat16 autograd graph of the forward makes: the upstream factor is
@@ -117,37 +119,82 @@ inline long dk_grid(int B, int S, int skv, int ratio, bool causal) {
 
 }  // namespace
 
-// ---------------------------------------------------------------- 1. G
+// ---------------------------------------------------------------- 3. entries by key group
 
-// One workgroup per (b, t): sum the valid entries' g per key in LDS (dynamic,
-// (hi - lo) floats), then write G[b,t,lo..hi).  Positions outside [lo, hi)
-// are not written; the dk kernel never reads them.
-__global__ __launch_bounds__(256) void grad_scatter_kernel(const int32_t* __restrict__ indices,
-                                                           const float* __restrict__ grad, int B, int S, int skv,
-                                                           int ratio, const int32_t* __restrict__ ks,
-                                                           const int32_t* __restrict__ ke, int topk,
-                                                           float* __restrict__ G) {
-    extern __shared__ float row[];
-    const int tid = threadIdx.x;
-    const int b = blockIdx.x % B, t = blockIdx.x / B;
+// One workgroup per (b, t) (blockIdx.x = b * S + t): the row's valid entries
+// (key in [ks, ke)) sorted into buckets of 64 keys (bucket g holds keys 64g ..
+// 64g + 63), each entry {key, g bits, ReLU mask of heads 0-31, of heads
+// 32-63} (16 bytes), at ent[row][off[row][g] .. off[row][g + 1]); off has
+// ngroups + 1 entries per row.  The order inside a bucket is not specified.
+__global__ __launch_bounds__(256) void bucket_entries_kernel(const int32_t* __restrict__ indices,
+                                                             const float* __restrict__ grad,
+                                                             const uint32_t* __restrict__ masks, int nhg, int S,
+                                                             int skv, int ratio, const int32_t* __restrict__ ks,
+                                                             const int32_t* __restrict__ ke, int topk, int ngroups,
+                                                             int32_t* __restrict__ off, u32x4* __restrict__ ent) {
+    extern __shared__ int cnt[];                          // ngroups + 1 counters
+    __shared__ int wsum[4];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const long row = blockIdx.x;
+    const int t = (int)(row % S);
     int lo, hi;
     key_range(ks, ke, t, S, skv, ratio, lo, hi);
-    const int n = hi - lo;
-    if (n <= 0) return;                                   // uniform: no barrier reached
-    for (int i = tid; i < n; i += 256) row[i] = 0.0f;
+    const int32_t* irow = indices + row * topk;
+    const float* grow = grad + row * topk;
+    const uint32_t* mrow = masks + row * topk * nhg;
+    for (int g = tid; g <= ngroups; g += 256) cnt[g] = 0;
     __syncthreads();
-    const int32_t* irow = indices + ((long)b * S + t) * topk;
-    const float* grow = grad + ((long)b * S + t) * topk;
     for (int j = tid; j < topk; j += 256) {
         const int s = irow[j];
-        if (s >= lo && s < hi) atomicAdd(&row[s - lo], grow[j]);
+        if (s >= lo && s < hi) atomicAdd(&cnt[s >> 6], 1);
     }
     __syncthreads();
-    float* out = G + ((long)b * S + t) * skv + lo;
-    for (int i = tid; i < n; i += 256) out[i] = row[i];
+    // Exclusive prefix over the buckets: thread tid owns buckets
+    // [PER * tid, PER * tid + PER) (ngroups <= 512 for seqlen_kv <= 32768).
+    constexpr int PER = 2;
+    int c[PER], local = 0;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int g = PER * tid + k;
+        c[k] = g < ngroups ? cnt[g] : 0;
+        local += c[k];
+    }
+    int incl = local;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int u = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += u;
+    }
+    if (lane == 63) wsum[wv] = incl;
+    __syncthreads();
+    int run = incl - local;
+    for (int w2 = 0; w2 < wv; ++w2) run += wsum[w2];
+    const int total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    int32_t* orow = off + row * (ngroups + 1);
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int g = PER * tid + k;
+        if (g < ngroups) {
+            orow[g] = run;
+            cnt[g] = run;                                 // insertion point of bucket g
+        }
+        run += c[k];
+    }
+    if (tid == 0) orow[ngroups] = total;
+    __syncthreads();
+    u32x4* erow = ent + row * topk;
+    for (int j = tid; j < topk; j += 256) {
+        const int s = irow[j];
+        if (s >= lo && s < hi) {
+            const int pos = atomicAdd(&cnt[s >> 6], 1);
+            const uint32_t m0 = mrow[(long)j * nhg];
+            const uint32_t m1 = nhg > 1 ? mrow[(long)j * nhg + 1] : 0u;
+            erow[pos] = u32x4{(uint32_t)s, __float_as_uint(grow[j]), m0, m1};
+        }
+    }
 }
 
-// ---------------------------------------------------------------- 2. dk B fragments of q
+// ---------------------------------------------------------------- 1. dk B fragments of q
 
 // Fragment (hs, dt) of query (t, b), lane l, holds q[head][32 dt + l%32] (the
 // bf16 input bits) for the 8 heads 32(hs/2) + 16(hs%2) + 8(jj/4) + 4(l/32) + jj%4,
@@ -184,7 +231,7 @@ __global__ __launch_bounds__(64) void qt_fragments_kernel(const uint16_t* __rest
         }
 }
 
-// ---------------------------------------------------------------- 3. dq, dw (query-major)
+// ---------------------------------------------------------------- 2. dq, dw (query-major)
 
 // One wave per (query, group of up to 32 heads): the wave's dq accumulators
 // (32 x DP fp32) and q fragments leave room for two waves per SIMD.  The
@@ -197,7 +244,8 @@ __global__ __launch_bounds__(64, 2) void backward_rows_kernel(InLayout L, const 
                                                              const float* __restrict__ grad, int B, int S, int skv,
                                                              int ratio, const int32_t* __restrict__ ks,
                                                              const int32_t* __restrict__ ke, int topk,
-                                                             float* __restrict__ dq, float* __restrict__ dw) {
+                                                             float* __restrict__ dq, float* __restrict__ dw,
+                                                             uint32_t* __restrict__ masks) {
     constexpr int HW = rows_heads(H);                // heads of this wave: h0 .. h0 + HW - 1
     constexpr int NHG = H / HW;                      // head groups per query
     using T = BwTiling<HW, DP>;
@@ -264,7 +312,8 @@ __global__ __launch_bounds__(64, 2) void backward_rows_kernel(InLayout L, const 
 #pragma unroll
     for (int r = 0; r < T::NRT; ++r) dwacc[r] = 0.0f;
 
-    auto compute = [&](const uint8_t* buf, float g_own, bool vis) {
+    uint32_t* mrow = masks + ((long)b * S + t) * topk * NHG + blockIdx.x % NHG;
+    auto compute = [&](int blk, const uint8_t* buf, float g_own, bool vis) {
         f32x16 acct[T::NRT];
 #pragma unroll
         for (int r = 0; r < T::NRT; ++r) acct[r] = f32x16{};
@@ -285,6 +334,21 @@ __global__ __launch_bounds__(64, 2) void backward_rows_kernel(InLayout L, const 
         for (int q4 = 0; q4 < 4; ++q4) {
             const float4 gg = *reinterpret_cast<const float4*>(stage_g + 8 * q4 + 4 * hf);
             gv[4 * q4 + 0] = gg.x; gv[4 * q4 + 1] = gg.y; gv[4 * q4 + 2] = gg.z; gv[4 * q4 + 3] = gg.w;
+        }
+        // ReLU masks of the block's entries for this wave's heads, for the dk
+        // kernel: bit l of entry (32 blk + k) = d of head h0 + l > 0, where
+        // accumulator slot i holds key c_row(i, hf) and lane l%32 head h0 + l%32.
+        // Lane k < 32 collects entry k's mask from the ballots.
+        {
+            uint32_t mk = 0u;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const unsigned long long bal = __ballot(acct[0][i] > 0.0f);
+                mk = (l32 == c_row(i, 0)) ? (uint32_t)bal : mk;
+                mk = (l32 == c_row(i, 1)) ? (uint32_t)(bal >> 32) : mk;
+            }
+            const int j = 32 * blk + l32;
+            if (hf == 0 && j < topk) mrow[(long)j * NHG] = mk;
         }
         // dw: lane = head 32r + lane%32, rows = keys c_row(i, hf).
 #pragma unroll
@@ -346,7 +410,7 @@ __global__ __launch_bounds__(64, 2) void backward_rows_kernel(InLayout L, const 
         const int idx_nn = load_idx(blk + 2);
         const bool act_n = (blk + 1 < nb) && __ballot(visible(idx_n, blk + 1)) != 0ull;
         if (act_n) gather_block<DP>(other, kb, L.k_s, dlim, visible(idx_n, blk + 1) ? idx_n : 0, lane);
-        if (act_c) compute(cur, g_c, visible(idx_c, blk));
+        if (act_c) compute(blk, cur, g_c, visible(idx_c, blk));
         idx_c = idx_n; act_c = act_n; idx_n = idx_nn; g_c = g_n;
     }
 
@@ -382,36 +446,44 @@ __global__ __launch_bounds__(64, 2) void backward_rows_kernel(InLayout L, const 
 // this wave are outstanding (expcnt and lgkmcnt left at their maxima).
 constexpr int wait_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
+// A workgroup owns 256 keys (64 per wave: wave w owns bucket 4 kg + w) and
+// streams the queries of one chunk that can see them.  Per query, through a
+// three-stage rotation of LDS buffers (one barrier per query), it moves in by
+// direct loads the query's dk B fragments of q, one copy of its head weights
+// per wave and each wave's bucket of entries (up to 64; more only with
+// repeated keys).  A wave builds a 64-slot table of its keys (summed g and
+// ReLU masks, from the rows kernel's recompute) and forms the dk A operand
+// bf16(G w_h) where m_h, else 0, in the order of the B fragments' heads: the
+// product needs no recompute of q . k.  dk stays in registers; the
+// workgroup's partial is added to dk once at the end.
 template <int H, int DP>
-__global__ __launch_bounds__(256, 1) void dk_keys_kernel(InLayout L, const float* __restrict__ w,
-                                                         const float* __restrict__ G,
-                                                         const uint8_t* __restrict__ qtf, int B, int S, int skv,
-                                                         int ratio, const int32_t* __restrict__ ks,
-                                                         const int32_t* __restrict__ ke, float* __restrict__ dk) {
+__global__ __launch_bounds__(256, 2) void dk_entries_kernel(const float* __restrict__ w,
+                                                            const int32_t* __restrict__ off,
+                                                            const u32x4* __restrict__ ent,
+                                                            const uint8_t* __restrict__ qtf, int B, int S, int skv,
+                                                            int ratio, const int32_t* __restrict__ ks,
+                                                            const int32_t* __restrict__ ke, int topk, int ngroups,
+                                                            int D, float* __restrict__ dk) {
     using T = BwTiling<H, DP>;
-    // Three stages, each: q in A-fragment order, q in the dk B-fragment order,
-    // G at the workgroup's 256 keys and one copy of the query's head weights
-    // per wave (64 floats; heads past H repeat w[H-1] and meet zero B rows).
-    constexpr int QS = 0, QT = T::QS_BYTES, GS = QT + T::QT_BYTES, WS = GS + 4 * kKeysPerGroup;
-    constexpr int STAGE = WS + 4 * 4 * 64;
-    // Three separate arrays, used in a fixed rotation, so the compiler can tell
-    // that loads into one never alias reads of another.
+    // Stage: q in dk B-fragment order, per wave one copy of the head weights
+    // (64 floats; heads past H repeat w[H-1] and meet zero B rows) and the
+    // wave's bucket (64 entries of 16 bytes).
+    constexpr int QT = 0, WS = T::QT_BYTES, ES = WS + 4 * 4 * 64;
+    constexpr int STAGE = ES + 4 * 64 * 16;
     __shared__ __attribute__((aligned(16))) uint8_t lds0[STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t lds1[STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t lds2[STAGE];
-    // Vector-memory operations one wave issues per stage: its share of the q
-    // and fragment blocks, one G load and one weight load.
-    constexpr int PER_WAVE = (T::NRT * T::NSTEP + T::NHS * T::NDT) / 4 + 2;
-    static_assert((T::NRT * T::NSTEP) % 4 == 0 && (T::NHS * T::NDT) % 4 == 0, "blocks split over 4 waves");
+    __shared__ int offs[kQueryChunk][5];                    // bucket bounds of the chunk's queries
+    __shared__ float tab_g[4][64];                          // per wave: summed g of its keys
+    __shared__ uint2 tab_m[4][64];                          // per wave: ReLU masks of its keys
+    constexpr int PER_WAVE = T::NHS * T::NDT / 4 + 2;       // vector-memory operations per stage and wave
+    static_assert((T::NHS * T::NDT) % 4 == 0, "fragment blocks split over 4 waves");
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
     int zc, b, kg;
     if (!dk_item(blockIdx.x, B, S, skv, ratio, ks == nullptr, zc, b, kg)) return;   // uniform: before any barrier
     const int s_group = kg * kKeysPerGroup;
     const int s_wave = s_group + 64 * wave;                          // this wave's first key
-    const int D = L.D;
-    const int dlim = (D >> 3) - 1;
-
     // Queries of this workgroup; with causal ranges no query before
     // ratio * (first key) - 1 sees any of its keys.
     int t0 = zc * kQueryChunk;
@@ -419,56 +491,30 @@ __global__ __launch_bounds__(256, 1) void dk_keys_kernel(InLayout L, const float
     if (ks == nullptr) t0 = (int)max((long)t0, (long)ratio * s_group - 1);
     if (t0 >= t1) return;                                  // uniform: before any barrier
 
-    // K fragments of the wave's 64 keys (B operand of D = Q K^T): kf[kc][st] =
-    // k[s_wave + 32kc + lane%32][16 st + 8 hf .. +7]; keys >= skv and index_dim
-    // entries >= D are zero.
-    bf16x8 kf[2][T::NSTEP];
-    const uint16_t* kb = L.k + (long)b * L.k_b;
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-        const int s = s_wave + 32 * kc + l32;
-        const uint16_t* base = kb + (long)min(s, skv - 1) * L.k_s;
-#pragma unroll
-        for (int st = 0; st < T::NSTEP; ++st) {
-            const int d0 = 16 * st + 8 * hf;
-            u32x4 v = *reinterpret_cast<const u32x4*>(base + min(d0, D - 8));
-            if (!(s < skv && d0 < D)) v = u32x4{0u, 0u, 0u, 0u};
-            kf[kc][st] = as_bf16x8(v);
-        }
+    // Bucket bounds of buckets 4 kg .. 4 kg + 4 for every query of the chunk.
+    for (int i = tid; i < (t1 - t0) * 5; i += 256) {
+        const int q = i / 5, k = i % 5;
+        const long row = (long)b * S + t0 + q;
+        offs[q][k] = off[row * (ngroups + 1) + min(4 * kg + k, ngroups)];
     }
+    __syncthreads();
 
-    // Stage query t (all by direct global->LDS loads): q in A-fragment order
-    // (block (r, st), lane l = head 32r + l%32, chunk 2st + l/32; padded heads
-    // repeat head H-1 and padded chunks the last real one: they meet zero
-    // fragments or zero K entries), the query's dk fragments, G at this
-    // wave's keys (clamped into the query's written range; masked where it is
-    // read) and the query's head weights (lane l: head min(l, H-1)) into the
-    // wave's own copy.
     auto stage = [&](int t, uint8_t* st_base) {
-        const uint16_t* qrow = L.q + (long)t * L.q_t + (long)b * L.q_b;
-#pragma unroll
-        for (int blk = wave; blk < T::NRT * T::NSTEP; blk += 4) {
-            const int r = blk / T::NSTEP, st = blk % T::NSTEP;
-            const int h = min(32 * r + l32, H - 1), d8 = min(2 * st + hf, dlim);
-            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(qrow + (long)h * D + 8 * d8),
-                                             (lds_ptr_t)(st_base + QS + blk * 1024), 16, 0, 0);
-        }
         const uint8_t* src = qtf + ((long)t * B + b) * T::QT_BYTES + 16 * lane;
 #pragma unroll
         for (int blk = wave; blk < T::NHS * T::NDT; blk += 4)
             __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + blk * 1024),
                                              (lds_ptr_t)(st_base + QT + blk * 1024), 16, 0, 0);
-        // One 64-lane dword load per wave: lane l carries key s_wave + l.
-        int lo, hi;
-        key_range(ks, ke, t, S, skv, ratio, lo, hi);
-        const float* grow = G + ((long)b * S + t) * skv;
-        const int sg = s_wave + lane;
-        const int sc = hi > lo ? min(max(sg, lo), hi - 1) : 0;           // a written position
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(grow + sc),
-                                         (lds_ptr_t)(st_base + GS + 4 * 64 * wave), 4, 0, 0);
         const float* wrow = w + ((long)t * B + b) * H;
         __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(wrow + min(lane, H - 1)),
                                          (lds_ptr_t)(st_base + WS + 4 * 64 * wave), 4, 0, 0);
+        // The wave's bucket: lane i carries entry beg + i (clamped into the
+        // row's topk entries; lanes past the bucket are ignored where the
+        // entries are read).
+        const int beg = offs[t - t0][wave], n = offs[t - t0][wave + 1] - beg;
+        const long e = ((long)b * S + t) * topk + min(beg + min(lane, max(n - 1, 0)), topk - 1);
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(ent + e),
+                                         (lds_ptr_t)(st_base + ES + 1024 * wave), 16, 0, 0);
     };
 
     f32x16 dkacc[2][T::NDT];
@@ -478,62 +524,62 @@ __global__ __launch_bounds__(256, 1) void dk_keys_kernel(InLayout L, const float
         for (int dt = 0; dt < T::NDT; ++dt) dkacc[kc][dt] = f32x16{};
 
     auto compute = [&](int t, const uint8_t* st_base) {
-        int lo, hi;
-        key_range(ks, ke, t, S, skv, ratio, lo, hi);
-        float g[2];
+        const int beg = offs[t - t0][wave], n = offs[t - t0][wave + 1] - beg;
+        if (n == 0) return;                                          // no entry of this wave's keys
+        // Table of the wave's 64 keys.  Every LDS operation of one wave runs
+        // in program order: clear, then add / store, then read back.
+        tab_g[wave][lane] = 0.0f;
+        tab_m[wave][lane] = uint2{0u, 0u};
+        auto put = [&](const u32x4& e) {
+            const int sl = (int)e.x - s_wave;                        // 0..63: the bucket's keys
+            atomicAdd(&tab_g[wave][sl], __uint_as_float(e.y));       // repeated keys: their g summed
+            tab_m[wave][sl] = uint2{e.z, e.w};                       // repeated keys: the same mask
+        };
+        if (lane < n) put(*reinterpret_cast<const u32x4*>(st_base + ES + 1024 * wave + 16 * lane));
+        for (int i0 = 64; i0 < n; i0 += 64) {                        // more than 64 entries: repeats
+            const int i = i0 + lane;
+            if (i < n) put(ent[((long)b * S + t) * topk + beg + i]);
+        }
+        float G[2];
+        uint2 mk[2];
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
-            const int s = s_wave + 32 * kc + l32;
-            const float v = reinterpret_cast<const float*>(st_base + GS)[64 * wave + 32 * kc + l32];
-            g[kc] = (s >= lo && s < hi) ? v : 0.0f;
+            G[kc] = tab_g[wave][32 * kc + l32];
+            mk[kc] = tab_m[wave][32 * kc + l32];
         }
-        if (__ballot(g[0] != 0.0f || g[1] != 0.0f) == 0ull) return;     // no selected key in this wave
-        // D = Q K^T: lanes are keys (32kc + lane%32), rows heads 32r + c_row(i, hf).
-        f32x16 accd[T::NRT][2];
-#pragma unroll
-        for (int r = 0; r < T::NRT; ++r) { accd[r][0] = f32x16{}; accd[r][1] = f32x16{}; }
-#pragma unroll
-        for (int st = 0; st < T::NSTEP; ++st)
-#pragma unroll
-            for (int r = 0; r < T::NRT; ++r) {
-                const bf16x8 qa =
-                    as_bf16x8(*reinterpret_cast<const u32x4*>(st_base + QS + (r * T::NSTEP + st) * 1024 + 16 * lane));
-#pragma unroll
-                for (int kc = 0; kc < 2; ++kc) accd[r][kc] = mfma_32x32x16(qa, kf[kc][st], accd[r][kc]);
-            }
-        // dk += bf16(m G w) Q: A = the key's G times the head's weight, rounded
-        // to bf16, where d > 0, in the order of D's accumulator rows
-        // (contraction over heads: row i of tile r is head 32r + c_row(i, hf));
-        // B the query's exact q fragments, each read once for both key halves.
+        // dk += A Q: A row = key 32 kc + lane%32, k = the 8 heads of this
+        // lane's B-fragment rows (fragment hs = 2r + s: heads 32r + 16s +
+        // 8(jj/4) + 4hf + jj%4); A = bf16(G w_h) where the head's mask bit is
+        // set, else 0; B the query's exact q fragments.
         const float* wl = reinterpret_cast<const float*>(st_base + WS + 4 * 64 * wave);
 #pragma unroll
         for (int r = 0; r < T::NRT; ++r)
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                // heads of accumulator rows 8s .. 8s+7: two runs of four
+            for (int sst = 0; sst < 2; ++sst) {
                 float wv[8];
 #pragma unroll
                 for (int g4 = 0; g4 < 2; ++g4) {
-                    const float4 v4 = *reinterpret_cast<const float4*>(wl + 32 * r + 8 * (2 * s + g4) + 4 * hf);
+                    const float4 v4 = *reinterpret_cast<const float4*>(wl + 32 * r + 8 * (2 * sst + g4) + 4 * hf);
                     wv[4 * g4 + 0] = v4.x; wv[4 * g4 + 1] = v4.y; wv[4 * g4 + 2] = v4.z; wv[4 * g4 + 3] = v4.w;
                 }
                 bf16x8 af[2];
 #pragma unroll
                 for (int kc = 0; kc < 2; ++kc) {
+                    const uint32_t bits = r == 0 ? mk[kc].x : mk[kc].y;   // heads 32r .. 32r + 31
                     u32x4 av;
 #pragma unroll
                     for (int p = 0; p < 4; ++p) {
-                        const int i0 = 8 * s + 2 * p;
-                        const float e0 = accd[r][kc][i0] > 0.0f ? g[kc] * wv[2 * p] : 0.0f;
-                        const float e1 = accd[r][kc][i0 + 1] > 0.0f ? g[kc] * wv[2 * p + 1] : 0.0f;
+                        const int hl0 = 16 * sst + 8 * (p >> 1) + 4 * hf + 2 * (p & 1);   // head - 32r of jj = 2p
+                        const float e0 = ((bits >> hl0) & 1u) ? G[kc] * wv[2 * p] : 0.0f;
+                        const float e1 = ((bits >> (hl0 + 1)) & 1u) ? G[kc] * wv[2 * p + 1] : 0.0f;
                         av[p] = pack_bf16(e0, e1);
                     }
                     af[kc] = as_bf16x8(av);
                 }
 #pragma unroll
                 for (int dt = 0; dt < T::NDT; ++dt) {
-                    const bf16x8 qf = as_bf16x8(
-                        *reinterpret_cast<const u32x4*>(st_base + QT + ((2 * r + s) * T::NDT + dt) * 1024 + 16 * lane));
+                    const bf16x8 qf = as_bf16x8(*reinterpret_cast<const u32x4*>(
+                        st_base + QT + ((2 * r + sst) * T::NDT + dt) * 1024 + 16 * lane));
 #pragma unroll
                     for (int kc = 0; kc < 2; ++kc) dkacc[kc][dt] = mfma_32x32x16(af[kc], qf, dkacc[kc][dt]);
                 }
@@ -591,23 +637,24 @@ template <int H, int DP>
 static hipError_t launch_backward_t(const BackwardArgs& p) {
     InLayout L{static_cast<const uint16_t*>(p.q), (long)p.B * H * p.D, (long)H * p.D,
                static_cast<const uint16_t*>(p.k), (long)p.B * p.D, (long)p.D, p.D};
-    float* G = reinterpret_cast<float*>(p.workspace);
-    uint8_t* qtf = reinterpret_cast<uint8_t*>(p.workspace) + backward_g_bytes(p.B, p.S, p.Skv);
+    const BackwardLayout ly = backward_layout(p.B, p.S, p.Skv, H, p.D, p.topk);
+    uint8_t* ws = static_cast<uint8_t*>(p.workspace);
+    uint8_t* qtf = ws + ly.qt;
+    uint32_t* masks = reinterpret_cast<uint32_t*>(ws + ly.masks);
+    int32_t* off = reinterpret_cast<int32_t*>(ws + ly.off);
+    u32x4* ent = reinterpret_cast<u32x4*>(ws + ly.ent);
     const unsigned rows = (unsigned)((long)p.B * p.S);
-    const size_t row_bytes = (size_t)p.Skv * 4;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(grad_scatter_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)row_bytes);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(grad_scatter_kernel, dim3(rows), dim3(256), row_bytes, p.stream, p.indices, p.grad,
-                       p.B, p.S, p.Skv, p.ratio, p.ks, p.ke, p.topk, G);
+    const int nhg = H / rows_heads(H);
+    const int ngroups = (p.Skv + 63) / 64;
     hipLaunchKernelGGL((qt_fragments_kernel<H, DP>), dim3(rows), dim3(kWave), 0, p.stream,
                        static_cast<const uint16_t*>(p.q), p.D, qtf);
-    hipLaunchKernelGGL((backward_rows_kernel<H, DP>), dim3(rows * (unsigned)(H / rows_heads(H))), dim3(kWave), 0,
-                       p.stream, L, p.w, p.indices,
-                       p.grad, p.B, p.S, p.Skv, p.ratio, p.ks, p.ke, p.topk, p.dq, p.dw);
+    hipLaunchKernelGGL((backward_rows_kernel<H, DP>), dim3(rows * (unsigned)nhg), dim3(kWave), 0, p.stream, L, p.w,
+                       p.indices, p.grad, p.B, p.S, p.Skv, p.ratio, p.ks, p.ke, p.topk, p.dq, p.dw, masks);
+    hipLaunchKernelGGL(bucket_entries_kernel, dim3(rows), dim3(256), (size_t)(ngroups + 1) * 4, p.stream, p.indices,
+                       p.grad, masks, nhg, p.S, p.Skv, p.ratio, p.ks, p.ke, p.topk, ngroups, off, ent);
     const long grid = dk_grid(p.B, p.S, p.Skv, p.ratio, p.ks == nullptr);
-    hipLaunchKernelGGL((dk_keys_kernel<H, DP>), dim3((unsigned)grid), dim3(256), 0, p.stream, L, p.w, G, qtf, p.B, p.S, p.Skv,
-                       p.ratio, p.ks, p.ke, p.dk);
+    hipLaunchKernelGGL((dk_entries_kernel<H, DP>), dim3((unsigned)grid), dim3(256), 0, p.stream, p.w, off, ent, qtf,
+                       p.B, p.S, p.Skv, p.ratio, p.ks, p.ke, p.topk, ngroups, p.D, p.dk);
     return hipGetLastError();
 }
 

@@ -120,13 +120,19 @@ struct BackwardArgs {
     float* dq;                // [S,B,H,D]
     float* dk;                // [Skv,B,D]
     float* dw;                // [S,B,H]
-    void* workspace;          // backward_workspace_bytes(B, S, Skv, H, D) bytes
+    void* workspace;          // backward_workspace_bytes(B, S, Skv, H, D, topk) bytes
     hipStream_t stream;
 };
-// Workspace of the backward: G [B,S,Skv] fp32 (rounded up to 256 bytes), then
-// q re-laid for the dk product (backward_qt_bytes per (t, b)).
-long backward_g_bytes(int B, int S, int Skv);
-long backward_workspace_bytes(int B, int S, int Skv, int H, int D);
+// Workspace of the backward, byte offsets of its parts (each 256-byte
+// aligned): q re-laid as the dk B fragments ([S,B] blocks of BwTiling's
+// QT_BYTES); the rows kernel's ReLU masks ([B,S,topk] x ceil(H/32) uint32);
+// bucket bounds ([B,S] x (ceil(Skv/64) + 1) int32); the entries bucketed by
+// 64-key group ([B,S,topk] x 16 bytes).  O(B S (topk + Skv/64) + S B H D).
+struct BackwardLayout {
+    long qt, masks, off, ent, total;
+};
+BackwardLayout backward_layout(int B, int S, int Skv, int H, int D, int topk);
+long backward_workspace_bytes(int B, int S, int Skv, int H, int D, int topk);
 hipError_t launch_indexer_backward(const BackwardArgs& p);
 // Device address and size of the current device's static backward workspace
 // (lix_indexer_backward_noalloc); taken with hipGetSymbolAddress once per device.

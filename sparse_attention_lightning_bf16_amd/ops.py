@@ -223,7 +223,7 @@ def indexer_backward(q, k, weights, compress_ratio, topk_indices, grad_scores, c
         raise ValueError("topk_indices and grad_scores must be on the device of q")
     tk = topk_indices.shape[2]
     lib = _lib.load()
-    ws_bytes = lib.lix_indexer_backward_workspace_bytes(B, S, Skv, H, D)
+    ws_bytes = lib.lix_indexer_backward_workspace_bytes(B, S, Skv, H, D, tk)
     if ws_bytes < 0:
         raise _lib.LixError(-3, "lix_indexer_backward_workspace_bytes")
     dq = torch.empty(S, B, H, D, dtype=torch.float32, device=q.device)

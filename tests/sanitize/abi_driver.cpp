@@ -130,10 +130,10 @@ int main() {
     EXPECT(lix_topk_scores(fp, ip, 1, 4, 8, 2, fp, nullptr), DEV);
     EXPECT(lix_indexer_scores_at(p, p, fp, ip, 1, 8, 4, 64, 128, 4, nullptr, nullptr, 0, fp, nullptr), SHP);
     EXPECT(lix_indexer_scores_at(p, p, fp, ip, 1, 8, 4, 64, 128, 4, nullptr, nullptr, 2, fp, nullptr), DEV);
-    const long long ws = lix_indexer_backward_workspace_bytes(1, 8, 4, 64, 128);
+    const long long ws = lix_indexer_backward_workspace_bytes(1, 8, 4, 64, 128, 2);
     if (ws <= 0) ++g_failures;
-    if (lix_indexer_backward_workspace_bytes(1, 8, 40000, 64, 128) != -1) ++g_failures;
-    if (lix_indexer_backward_workspace_bytes(INT_MAX, INT_MAX, INT_MAX, 64, 128) != -1) ++g_failures;
+    if (lix_indexer_backward_workspace_bytes(1, 8, 40000, 64, 128, 2) != -1) ++g_failures;
+    if (lix_indexer_backward_workspace_bytes(INT_MAX, INT_MAX, INT_MAX, 64, 128, 2) != -1) ++g_failures;
     EXPECT(lix_indexer_backward(p, p, fp, ip, fp, 1, 8, 4, 64, 128, 4, nullptr, nullptr, 2, fp, fp, fp, p, 1000,
                                 nullptr), SHP);
     EXPECT(lix_indexer_backward(p, p, fp, ip, fp, 1, 8, 4, 128, 128, 4, nullptr, nullptr, 2, fp, fp, fp, p, ws,
@@ -184,7 +184,7 @@ int main() {
                 break;
             case 4: {
                 const int B = pick_int(), S = pick_int(), Skv = pick_int(), H = pick_int(), D = pick_int();
-                (void)lix_indexer_backward_workspace_bytes(B, S, Skv, H, D);
+                (void)lix_indexer_backward_workspace_bytes(B, S, Skv, H, D, pick_int());
                 st = lix_indexer_backward(pick_ptr(), pick_ptr(), (float*)pick_ptr(), (int32_t*)pick_ptr(),
                                           (float*)pick_ptr(), B, S, Skv, H, D, pick_int(), nullptr, nullptr,
                                           pick_int(), (float*)pick_ptr(), (float*)pick_ptr(), (float*)pick_ptr(),

@@ -412,6 +412,21 @@ def test_backward_invalid_entries_and_zero_gradient():
     assert torch.isfinite(a[1]).all()
 
 
+def test_backward_keys_repeated_past_one_bucket():
+    # Rows naming a few keys many times: more than 64 entries in one 64-key
+    # bucket (the dk kernel's second pass over a bucket), repeated keys summed.
+    B, S, Skv, H, D, tk = 2, 60, 300, 64, 128, 200
+    inp, nb, _, grad = backward_case(B, S, Skv, H, D, tk, seed=345)
+    g = torch.Generator().manual_seed(346)
+    idx = torch.randint(0, 10, (B, S, tk), generator=g, dtype=torch.int32)
+    idx[:, :, ::7] = torch.randint(0, Skv, (B, S, (tk + 6) // 7), generator=g, dtype=torch.int32)
+    q, k, w = dev(inp["q"]), dev(inp["k"]), dev(inp["w"])
+    dq, dk, dw = lx.indexer_backward(q, k, w, 1, dev(idx), dev(grad))
+    ks, ke = oracle.causal_ranges(S, Skv, 1)
+    check_backward_against_oracle({"dq": dq.cpu().numpy(), "dk": dk.cpu().numpy(), "dw": dw.cpu().numpy()}, nb,
+                                  idx.numpy(), grad.numpy(), ks, ke, "repeated keys")
+
+
 def test_backward_4k_topk_selection():
     # The 4K workload end to end: fused top-k, then the backward of its scores.
     cfg = synth.WORKLOADS["4k"]
@@ -429,26 +444,30 @@ def test_backward_4k_topk_selection():
     check_backward_against_oracle(got, nb, ix.cpu().numpy(), grad.numpy(), ks, ke, "backward 4k")
 
 
-def test_backward_32k_sampled_rows_and_homogeneity():
-    # Full size, in the launch configuration the bench times.  dq and dw of a
-    # query depend on that query alone: sampled queries against the oracle.
-    # dk sums over every query: checked through Euler's identity for the
-    # positively homogeneous score (degree 1 in q, in k and in w):
-    # <dq, q> = <dk, k> = <dw, w> = sum over valid entries of g * score.
-    cfg = synth.WORKLOADS["32k"]
+@pytest.mark.parametrize("workload", ["32k", "131k"])
+def test_backward_workload_sampled_rows_and_homogeneity(workload):
+    # Full size, in the launch configuration the bench times (32K) and the
+    # longest workload (131K: the workspace grows with topk and Skv/64, not
+    # with S * Skv).  dq and dw of a query depend on that query alone: sampled
+    # queries against the oracle.  dk sums over every query: checked through
+    # Euler's identity for the positively homogeneous score (degree 1 in q, in
+    # k and in w): <dq, q> = <dk, k> = <dw, w> = sum over valid entries of
+    # g * score.
+    cfg = synth.WORKLOADS[workload]
     S, Skv, tk = cfg["seqlen"], cfg["seqlen_kv"], cfg["topk"]
-    inp, nb = v4_case(1, S, Skv, 64, 128, cfg["seed"])
+    extra = {"heavy_fraction": cfg["heavy_fraction"]} if "heavy_fraction" in cfg else {}
+    inp, nb = v4_case(1, S, Skv, 64, 128, cfg["seed"], **extra)
     q, k, w = dev(inp["q"]), dev(inp["k"]), dev(inp["w"])
-    log("32k: fused top-k, then the backward")
+    log(f"{workload}: fused top-k, then the backward")
     sc, ix = lx.topk(q, k, w, 4, tk)
     grad = dev(synth.upstream_gradient(1, S, tk, 346))
     dq, dk, dw = lx.indexer_backward(q, k, w, 4, ix, grad)
     torch.cuda.synchronize()
-    rows = np.unique(np.concatenate([np.arange(0, S, 1024), [3, 4, 7, 8191, 8192, 8195, S - 1]]))
+    rows = np.unique(np.concatenate([np.arange(0, S, S // 32), [3, 4, 7, 8191, 8192, 8195, S - 1]]))
     ks, ke = ranges(S, Skv, 4)
-    log(f"32k: oracle backward on {len(rows)} sampled queries")
+    log(f"{workload}: oracle backward on {len(rows)} sampled queries")
     check_backward_against_oracle({"dq": dq.cpu().numpy(), "dw": dw.cpu().numpy()}, nb, ix.cpu().numpy(),
-                                  grad.cpu().numpy(), ks, ke, "backward 32k", rows=rows)
+                                  grad.cpu().numpy(), ks, ke, f"backward {workload}", rows=rows)
     valid = torch.isfinite(sc)
     gs = torch.where(valid, grad, torch.zeros_like(grad))
     total = (gs.double() * torch.where(valid, sc, torch.zeros_like(sc)).double()).sum().item()
@@ -898,7 +917,7 @@ def test_every_output_leaves_memory_around_it_untouched():
     assert lib.lix_indexer_scores_at(q.data_ptr(), k.data_ptr(), w.data_ptr(), idx_given.data_ptr(), B, S, Skv, H,
                                      D, c, None, None, tk, so.data_ptr(), st) == 0
     assert _intact(sbuf, n, F), "scores_at"
-    ws_bytes = lib.lix_indexer_backward_workspace_bytes(B, S, Skv, H, D)
+    ws_bytes = lib.lix_indexer_backward_workspace_bytes(B, S, Skv, H, D, tk)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
     bufs = {name: _guarded(m, torch.float32, F) for name, m in
             (("dq", S * B * H * D), ("dk", Skv * B * D), ("dw", S * B * H))}
