@@ -15,6 +15,8 @@
 // for an index outside [0, Skv).
 #include <type_traits>
 
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 #include "row_select.h"
@@ -535,10 +537,12 @@ __global__ __launch_bounds__(kRowThreads, MINB) void topk_rows_reg_kernel(
     }
 }
 
-// One workgroup of NW waves per row of materialized scores (select_row_binned).
+// One workgroup of NW waves per row of materialized scores (select_row_binned):
+// rows t_end - 1, t_end - 2, ... (longest causal rows first), gridDim.x / B of
+// them.
 template <int NCH, bool BF16, int NW>
 __global__ __launch_bounds__(64 * NW) void topk_rows_bin_kernel(const void* __restrict__ logits_v, int B, int S,
-                                                                    int skv, int ratio,
+                                                                    int t_end, int skv, int ratio,
                                                                     const int32_t* __restrict__ ks,
                                                                     const int32_t* __restrict__ ke, int topk,
                                                                     void* __restrict__ scores_v,
@@ -546,7 +550,7 @@ __global__ __launch_bounds__(64 * NW) void topk_rows_bin_kernel(const void* __re
     using In = RowIn<BF16>;
     __shared__ BinShared sh;
     const int b = blockIdx.x % B;
-    const int t = S - 1 - (int)(blockIdx.x / B);              // longest causal rows first
+    const int t = t_end - 1 - (int)(blockIdx.x / B);
     int lo = 0, hi = skv;
     if constexpr (!BF16) key_range(ks, ke, t, S, skv, ratio, lo, hi);
     const In* row = static_cast<const In*>(logits_v) + ((long)b * S + t) * skv + lo;
@@ -578,31 +582,42 @@ hipError_t launch_topk_rows(const TopkArgs& p) {
     // Measured on MI355X: one register-resident wave per row wins for rows of
     // up to 2048 keys; rows up to 8192 keys go to the binned workgroup kernel
     // (the row in the registers of four waves), up to 32768 keys to the same
-    // kernel with sixteen waves (one workgroup per CU), longer ones to the
-    // radix kernel that re-reads the row.  The two-wave register variant
+    // kernel with eight or sixteen waves, longer ones to the radix kernel that
+    // re-reads the row.  The two-wave register variant
     // (WPR = 2) measured slower at 8192 keys and is not used.
     if (p.Skv <= 2048) {
         launch_reg<8, 1, 4>(p);
     } else {
         dim3 grid((unsigned)((long)p.B * p.S));
-        if (p.Skv <= 8192)
+        auto rows = [&](int t_lo, int t_hi) { return dim3((unsigned)((long)p.B * (t_hi - t_lo))); };
+        if (p.Skv <= 8192) {
             hipLaunchKernelGGL((topk_rows_bin_kernel<8, false, 4>), grid, dim3(256), 0, p.stream,
-                               static_cast<const void*>(p.logits), p.B, p.S, p.Skv, p.ratio, p.ks, p.ke, p.topk,
+                               static_cast<const void*>(p.logits), p.B, p.S, p.S, p.Skv, p.ratio, p.ks, p.ke, p.topk,
                                static_cast<void*>(p.scores), p.indices);
-        else if (p.Skv <= 32768)
-            hipLaunchKernelGGL((topk_rows_bin_kernel<8, false, 16>), grid, dim3(1024), 0, p.stream,
-                               static_cast<const void*>(p.logits), p.B, p.S, p.Skv, p.ratio, p.ks, p.ke, p.topk,
-                               static_cast<void*>(p.scores), p.indices);
-        else
+        } else if (p.Skv <= 32768) {
+            // Causal rows of at most 16384 keys (t < 16384 ratio) fit the
+            // registers of eight waves, which leaves room for two workgroups
+            // per CU; longer rows take sixteen.
+            const int t_split = p.ks == nullptr ? (int)std::min<long>(p.S, 16384L * p.ratio) : 0;
+            if (t_split < p.S)
+                hipLaunchKernelGGL((topk_rows_bin_kernel<8, false, 16>), rows(t_split, p.S), dim3(1024), 0, p.stream,
+                                   static_cast<const void*>(p.logits), p.B, p.S, p.S, p.Skv, p.ratio, p.ks, p.ke,
+                                   p.topk, static_cast<void*>(p.scores), p.indices);
+            if (t_split > 0)
+                hipLaunchKernelGGL((topk_rows_bin_kernel<8, false, 8>), rows(0, t_split), dim3(512), 0, p.stream,
+                                   static_cast<const void*>(p.logits), p.B, p.S, t_split, p.Skv, p.ratio, p.ks, p.ke,
+                                   p.topk, static_cast<void*>(p.scores), p.indices);
+        } else {
             hipLaunchKernelGGL(topk_rows_kernel<0>, grid, dim3(kTopkThreads), 0, p.stream, p.logits, p.B, p.S,
                                p.Skv, p.ratio, p.ks, p.ke, p.topk, p.scores, p.indices);
+        }
     }
     return hipGetLastError();
 }
 
 hipError_t launch_topk_bf16(const TopkBf16Args& p) {
     dim3 grid((unsigned)((long)p.B * p.L));
-    hipLaunchKernelGGL((topk_rows_bin_kernel<8, true, 4>), grid, dim3(256), 0, p.stream, p.scores, p.B, p.L,
+    hipLaunchKernelGGL((topk_rows_bin_kernel<8, true, 4>), grid, dim3(256), 0, p.stream, p.scores, p.B, p.L, p.L,
                        p.G, 1, nullptr, nullptr, p.topk, p.out_scores, p.indices);
     return hipGetLastError();
 }

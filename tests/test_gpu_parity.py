@@ -197,6 +197,26 @@ def test_topk_long_rows_from_logits(Skv):
     assert np.array_equal(sc.cpu().numpy()[0].astype(np.float64), want_s)
 
 
+def test_topk_causal_long_rows_across_the_kernel_split():
+    # Causal rows of 8193..32768 keys: those of at most 16384 keys go to the
+    # eight-wave kernel, longer ones to the sixteen-wave kernel.  Both against
+    # the fused selection, bit for bit, and sampled rows against the oracle.
+    B, S, Skv, H, D, c, tk = 1, 16600, 20000, 64, 128, 1, 1000
+    inp, nb = v4_case(B, S, Skv, H, D, seed=620)
+    q, k, w = dev(inp["q"]), dev(inp["k"]), dev(inp["w"])
+    logits = lx.indexer_logits(q, k, w, c)
+    sc_m, ix_m = lx.topk_from_logits(logits, c, tk)
+    sc_f, ix_f = lx.topk(q, k, w, c, tk)
+    assert torch.equal(ix_m, ix_f) and torch.equal(sc_m, sc_f)
+    ks, ke = oracle.causal_ranges(S, Skv, c)
+    rows = np.array([0, 999, 1000, 8191, 8192, 16382, 16383, 16384, 16385, S - 1])
+    lg = logits[0][torch.from_numpy(rows).to(DEV)].cpu().numpy().astype(np.float64)
+    for i, t in enumerate(rows):
+        want_s, want_i = oracle.topk_select(lg[i:i + 1], ks[t:t + 1], ke[t:t + 1], tk)
+        assert np.array_equal(ix_m[0, t].cpu().numpy(), want_i[0]), t
+        assert np.array_equal(sc_m[0, t].cpu().numpy().astype(np.float64), want_s[0]), t
+
+
 @pytest.mark.parametrize("H,D,topk", [(64, 128, 2048), (128, 128, 256), (32, 64, 100), (16, 32, 33),
                                       (8, 128, 64)])
 def test_fused_equals_materialized(H, D, topk):
