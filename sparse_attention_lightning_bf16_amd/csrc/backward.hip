@@ -141,7 +141,7 @@ __global__ __launch_bounds__(256) void bucket_entries_kernel(const int32_t* __re
     key_range(ks, ke, t, S, skv, ratio, lo, hi);
     const int32_t* irow = indices + row * topk;
     const float* grow = grad + row * topk;
-    const uint32_t* mrow = masks + row * topk * nhg;
+    const uint32_t* mrow = masks + row * topk * nhg;         // [head group][topk]
     for (int g = tid; g <= ngroups; g += 256) cnt[g] = 0;
     __syncthreads();
     for (int j = tid; j < topk; j += 256) {
@@ -187,8 +187,8 @@ __global__ __launch_bounds__(256) void bucket_entries_kernel(const int32_t* __re
         const int s = irow[j];
         if (s >= lo && s < hi) {
             const int pos = atomicAdd(&cnt[s >> 6], 1);
-            const uint32_t m0 = mrow[(long)j * nhg];
-            const uint32_t m1 = nhg > 1 ? mrow[(long)j * nhg + 1] : 0u;
+            const uint32_t m0 = mrow[j];
+            const uint32_t m1 = nhg > 1 ? mrow[topk + j] : 0u;
             erow[pos] = u32x4{(uint32_t)s, __float_as_uint(grow[j]), m0, m1};
         }
     }
@@ -255,8 +255,14 @@ __global__ __launch_bounds__(64, 2) void backward_rows_kernel(InLayout L, const 
     __shared__ __attribute__((aligned(16))) float stage_g[32];
 
     const int lane = threadIdx.x, hf = lane >> 5, l32 = lane & 31;
-    const int h0 = HW * (int)(blockIdx.x % NHG);
-    const int row = (int)(blockIdx.x / NHG);
+    // The head groups of one query get flat ids 8 apart (groups of 8 rows):
+    // they go to the same XCD at about the same time and share the query's
+    // indices, gradients and key rows through its L2.
+    const int hq = (int)((blockIdx.x / kXcds) % NHG);
+    const long row_l = (long)(blockIdx.x / (kXcds * NHG)) * kXcds + blockIdx.x % kXcds;
+    if (row_l >= (long)B * S) return;                         // padding of the last group of 8 rows
+    const int h0 = HW * hq;
+    const int row = (int)row_l;
     const int b = row % B, t = row / B;
     const int D = L.D;
     int lo, hi;
@@ -312,7 +318,7 @@ __global__ __launch_bounds__(64, 2) void backward_rows_kernel(InLayout L, const 
 #pragma unroll
     for (int r = 0; r < T::NRT; ++r) dwacc[r] = 0.0f;
 
-    uint32_t* mrow = masks + ((long)b * S + t) * topk * NHG + blockIdx.x % NHG;
+    uint32_t* mrow = masks + (((long)b * S + t) * NHG + hq) * topk;     // [B,S,head group,topk]
     auto compute = [&](int blk, const uint8_t* buf, float g_own, bool vis) {
         f32x16 acct[T::NRT];
 #pragma unroll
@@ -348,7 +354,7 @@ __global__ __launch_bounds__(64, 2) void backward_rows_kernel(InLayout L, const 
                 mk = (l32 == c_row(i, 1)) ? (uint32_t)(bal >> 32) : mk;
             }
             const int j = 32 * blk + l32;
-            if (hf == 0 && j < topk) mrow[(long)j * NHG] = mk;
+            if (hf == 0 && j < topk) mrow[j] = mk;
         }
         // dw: lane = head 32r + lane%32, rows = keys c_row(i, hf).
 #pragma unroll
@@ -648,7 +654,8 @@ static hipError_t launch_backward_t(const BackwardArgs& p) {
     const int ngroups = (p.Skv + 63) / 64;
     hipLaunchKernelGGL((qt_fragments_kernel<H, DP>), dim3(rows), dim3(kWave), 0, p.stream,
                        static_cast<const uint16_t*>(p.q), p.D, qtf);
-    hipLaunchKernelGGL((backward_rows_kernel<H, DP>), dim3(rows * (unsigned)nhg), dim3(kWave), 0, p.stream, L, p.w,
+    const unsigned rows8 = (rows + kXcds - 1) / kXcds * kXcds;
+    hipLaunchKernelGGL((backward_rows_kernel<H, DP>), dim3(rows8 * (unsigned)nhg), dim3(kWave), 0, p.stream, L, p.w,
                        p.indices, p.grad, p.B, p.S, p.Skv, p.ratio, p.ks, p.ke, p.topk, p.dq, p.dw, masks);
     hipLaunchKernelGGL(bucket_entries_kernel, dim3(rows), dim3(256), (size_t)(ngroups + 1) * 4, p.stream, p.indices,
                        p.grad, masks, nhg, p.S, p.Skv, p.ratio, p.ks, p.ke, p.topk, ngroups, off, ent);

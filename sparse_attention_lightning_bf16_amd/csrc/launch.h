@@ -125,7 +125,7 @@ struct BackwardArgs {
 };
 // Workspace of the backward, byte offsets of its parts (each 256-byte
 // aligned): q re-laid as the dk B fragments ([S,B] blocks of BwTiling's
-// QT_BYTES); the rows kernel's ReLU masks ([B,S,topk] x ceil(H/32) uint32);
+// QT_BYTES); the rows kernel's ReLU masks ([B,S] x ceil(H/32) x topk uint32);
 // bucket bounds ([B,S] x (ceil(Skv/64) + 1) int32); the entries bucketed by
 // 64-key group ([B,S,topk] x 16 bytes).  O(B S (topk + Skv/64) + S B H D).
 struct BackwardLayout {
