@@ -29,8 +29,9 @@ Prints one JSON line.  `value` is causally valid TFLOP/s (2*H*D per visible
 pair) over the whole step; queries/s are reported beside it.
 
 --part NAME launches only one kernel's call in a loop (for profiler runs) and
-prints its median duration: logits, topk, fused, gather, scores_at,
-backward, v41, topk_bf16, copy.
+prints its median duration: logits, topk, fused, streaming, gather,
+scores_at, backward, v41, topk_bf16, copy; --workload 131k runs it on the
+131K workload instead of the 32K one.
 """
 
 import argparse
@@ -203,21 +204,38 @@ def extra_workloads(dev, steps, warmup, flush):
 
 # ---------------------------------------------------------------- recorded traffic
 
-def source_digest():
-    """sha256 over the library's kernel and ABI sources (csrc/*)."""
+CSRC = os.path.join(ROOT, "sparse_attention_lightning_bf16_amd", "csrc")
+# Translation unit of each kernel whose traffic the summary records.
+KERNEL_UNITS = {"v4_logits_kernel": "score.hip", "v41_scores_kernel": "score.hip", "v4_fused_topk_kernel": "fused.hip",
+                "topk_rows_bin_kernel": "topk.hip", "gather_kernel": "topk.hip", "sparse_scores_kernel": "sparse.hip",
+                "qt_fragments_kernel": "backward.hip", "backward_rows_kernel": "backward.hip",
+                "bucket_entries_kernel": "backward.hip", "dk_entries_kernel": "backward.hip"}
+
+
+def source_digest(unit):
+    """sha256 over a translation unit of the library and every csrc header it includes, directly or not:
+    the sources a kernel of that unit is built from."""
     import hashlib
-    root = os.path.join(ROOT, "sparse_attention_lightning_bf16_amd", "csrc")
+    import re
+    seen, todo = set(), [unit]
+    while todo:
+        name = todo.pop()
+        if name in seen or not os.path.exists(os.path.join(CSRC, name)):
+            continue
+        seen.add(name)
+        text = open(os.path.join(CSRC, name), "rb").read()
+        todo += [m.decode() for m in re.findall(rb'#include "([^"]+)"', text)]
     h = hashlib.sha256()
-    for name in sorted(os.listdir(root)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(root, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in sorted(seen):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
 def recorded_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE/WRITE_SIZE summary, or None when
-    that summary was taken on other kernel sources than the ones built here."""
+    """HBM bytes per launch of `kernel` (name with template arguments) from the committed
+    FETCH_SIZE/WRITE_SIZE summary, or None when the counters were taken on other sources of that
+    kernel's translation unit than the ones built here."""
     path = os.path.join(ROOT, TRAFFIC_SUMMARY)
     try:
         lines = open(path).read().splitlines()
@@ -226,10 +244,9 @@ def recorded_traffic(kernel):
     for line in lines:
         if line.startswith("traffic-record: "):
             rec = json.loads(line[len("traffic-record: "):])
-            if rec.get("source_sha256") != source_digest():
-                return None
             k = rec.get("kernels", {}).get(kernel)
-            if k is None:
+            unit = KERNEL_UNITS.get(kernel.split("<")[0])
+            if k is None or unit is None or k.get("source_sha256") != source_digest(unit):
                 return None
             return {"read_bytes": k["read_bytes"], "written_bytes": k["written_bytes"],
                     "total_bytes": k["read_bytes"] + k["written_bytes"],
@@ -288,7 +305,7 @@ def cpu_baseline(inp32, every32):
         "queries_per_s": head["queries_per_s"],
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"{head['rows']} query rows (every {every32}th of {cfg['seqlen']}) of the 32K workload: "
+        "sample": (f"{head['rows']} query rows (one in {every32} of {cfg['seqlen']}) of the 32K workload: "
                    f"float64 logits of each visible key, then top-{cfg['topk']}; {head['seconds']:.1f} s"),
         "other_workloads": others,
         "host_cpu": platform.processor() or platform.machine(),
@@ -354,9 +371,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the achievable peaks, the 4K cold/warm and the 131K fused parts")
-    ap.add_argument("--cpu-sample-every", type=int, default=6)
+    ap.add_argument("--cpu-sample-every", type=int, default=3)
     ap.add_argument("--part", choices=("all",) + PARTS, default="all",
                     help="time one kernel's call only (for profiler runs); the JSON line then covers that part")
+    ap.add_argument("--workload", choices=("32k", "131k"), default="32k",
+                    help="workload of a --part run (the full run always measures the 32K step)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -371,10 +390,11 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    cfg = synth.WORKLOADS["32k"]
+    wl = args.workload if args.part != "all" else "32k"
+    cfg = synth.WORKLOADS[wl]
     B, S, Skv, H, D = cfg["batch"], cfg["seqlen"], cfg["seqlen_kv"], cfg["heads"], cfg["index_dim"]
     c, tk = cfg["compress_ratio"], cfg["topk"]
-    log("generating the 32K workload")
+    log(f"generating the {wl} workload")
     inp = synth.v4_inputs(**cfg)
     q, k, w = (inp[x].to(dev) for x in "qkw")
     torch.cuda.synchronize()
