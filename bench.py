@@ -483,8 +483,8 @@ def main():
     bw_ms = median_ms(lambda: lx.indexer_backward(q, k, w, c, ix_f, g_up), max(5, args.steps // 2), 2)
     parts.update({
         "backward_ms": bw_ms,
-        # algorithmic work: four GEMM passes over the selected entries (d twice, dq, dk)
-        "backward_gemm_tflops": 4 * 2.0 * H * D * at_pairs / bw_ms / 1e9,
+        # algorithmic work: three GEMM passes over the selected entries (the recompute of d, dq, dk)
+        "backward_gemm_tflops": 3 * 2.0 * H * D * at_pairs / bw_ms / 1e9,
     })
     del g_up
 
