@@ -68,6 +68,8 @@ __device__ __forceinline__ uint32_t mask_pair(uint32_t v, float a_lo, float a_hi
 }
 
 typedef __attribute__((address_space(1))) float gfloat;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 // Work items of the dk kernel, (query chunk z, batch b, key group kg), in the
 // order the workgroups take them.  Workgroups go to the eight XCDs in turn
@@ -284,15 +286,24 @@ __global__ __launch_bounds__(64, 2) void backward_rows_kernel(InLayout L, const 
             a[r][st] = as_bf16x8(v);
         }
     }
-    // Key-major reads of a gathered block: element (key 16s + 8(jj/4) + 4hf + jj%4,
-    // index_dim 32dt + lane%32) lies at kbase[dt%2][(jj%4) ^ (jj/4)]
-    // + 1024(4(dt/2) + 2s + jj/4) + 128(jj%4) (the BlockMap placement, 8-chunk segments).
-    int kbase[2][4];
+    // Key-major B fragments of the dq product by transposing LDS reads
+    // (ds_read_b64_tr_b16): within each group of 16 lanes, output lane 4b + e
+    // receives, as its element a, element e of the 4 values source lane 4a + b
+    // reads.  Fragment slot jj of lane l must hold (key 16s + 8(jj/4) + 4hf +
+    // jj%4, index_dim 32dt + l%32): read rd = jj/4 gives slots 4rd .. 4rd + 3 if
+    // source lane (group g, a, b) reads index_dim 32dt + 16(g%2) + 4b .. +3 of key
+    // 16s + 8rd + 4(g/2) + a.  In the BlockMap placement (8-chunk segments) that
+    // is byte tbase[dt%2][rd] + 1024(4(dt/2) + 2s + rd).
+    int tbase[2][2];
+    {
+        const int tg = lane >> 4, ta = (lane & 15) >> 2, tb = lane & 3;
+        const int tm = 4 * (tg >> 1) + ta;                      // row within the 8-row load
+        const int tx = (2 * (tg & 1) + (tb >> 1)) ^ tm;          // chunk within the segment, before swizzle
 #pragma unroll
-    for (int p2 = 0; p2 < 2; ++p2)
+        for (int p2 = 0; p2 < 2; ++p2)
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
-            kbase[p2][x] = 512 * hf + 64 * (p2 ^ hf) + 16 * ((l32 >> 3) ^ x) + 2 * (lane & 7);
+            for (int rd = 0; rd < 2; ++rd) tbase[p2][rd] = 16 * (8 * tm + (tx ^ (4 * p2) ^ rd)) + 8 * (tb & 1);
+    }
     int fofs[M::KR];
 #pragma unroll
     for (int kq = 0; kq < M::KR; ++kq) fofs[kq] = M::frag_off(kq, lane);
@@ -370,20 +381,12 @@ __global__ __launch_bounds__(64, 2) void backward_rows_kernel(InLayout L, const 
             bf16x8 kt[T::NDT];
 #pragma unroll
             for (int dt = 0; dt < T::NDT; ++dt) {
-                uint32_t pk[4];
+                i16x4 part[2];
 #pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    uint32_t half[2];
-#pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        const int jj = 2 * p + u;
-                        const int off = kbase[dt & 1][(jj & 3) ^ (jj >> 2)] + 1024 * (4 * (dt >> 1) + 2 * s + (jj >> 2)) +
-                                        128 * (jj & 3);
-                        half[u] = *reinterpret_cast<const uint16_t*>(buf + off);
-                    }
-                    pk[p] = half[0] | (half[1] << 16);
-                }
-                kt[dt] = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
+                for (int rd = 0; rd < 2; ++rd)
+                    part[rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(
+                        const_cast<uint8_t*>(buf) + tbase[dt & 1][rd] + 1024 * (4 * (dt >> 1) + 2 * s + rd)));
+                kt[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
             }
 #pragma unroll
             for (int r = 0; r < T::NRT; ++r) {
@@ -652,6 +655,7 @@ static hipError_t launch_backward_t(const BackwardArgs& p) {
     const unsigned rows = (unsigned)((long)p.B * p.S);
     const int nhg = H / rows_heads(H);
     const int ngroups = (p.Skv + 63) / 64;
+    if (ngroups > 512) return hipErrorInvalidValue;          // the bucket kernel's prefix covers 512 buckets
     hipLaunchKernelGGL((qt_fragments_kernel<H, DP>), dim3(rows), dim3(kWave), 0, p.stream,
                        static_cast<const uint16_t*>(p.q), p.D, qtf);
     const unsigned rows8 = (rows + kXcds - 1) / kXcds * kXcds;
