@@ -271,13 +271,12 @@ int lix_indexer_backward(const void* q, const void* k, const float* w, const int
 
 /*
  * lix_indexer_backward_workspace_bytes - device workspace lix_indexer_backward
- * needs for these sizes: q re-laid for the dk product (S*B*heads*index_dim*2
- * bytes, heads padded to 32 or 64, index_dim to 64 or 128), the ReLU masks of
- * every entry (B*S*topk*4 bytes per 32 heads), the entries bucketed by groups
- * of 64 keys (B*S*topk*16 bytes) and the bucket bounds (B*S*(Skv/64 + 1)*4
- * bytes), each part rounded up to 256 bytes: linear in topk and in Skv/64,
- * with no [B, S, Skv] term.  -1 when the sizes are outside what
- * lix_indexer_backward accepts.
+ * needs for these sizes: the ReLU masks of every entry (B*S*topk*4 bytes per
+ * 32 heads), the bucket bounds (B*S*(Skv/64 + 1)*4 bytes) and the entries
+ * bucketed by groups of 64 keys (B*S*topk*16 bytes), each part rounded up to
+ * 256 bytes: linear in topk and in Skv/64, with no [B, S, Skv] term and no
+ * copy of q, k or w.  -1 when the sizes are outside what lix_indexer_backward
+ * accepts.
  */
 long long lix_indexer_backward_workspace_bytes(int B, int S, int Skv, int H, int D, int topk);
 

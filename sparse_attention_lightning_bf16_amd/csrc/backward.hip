@@ -17,10 +17,7 @@
 // element is accumulated with per-entry atomics, and every workspace array is
 // sized by the entries (B*S*topk) or by groups of 64 keys, never by B*S*Skv:
 //
-//   1. qt_fragments_kernel: q (bf16, exact) laid out as the B fragments of
-//      the dk product (workspace), so a workgroup can move them into LDS with
-//      direct loads.
-//   2. backward_rows_kernel (query-major, one wave per query and group of 32
+//   1. backward_rows_kernel (query-major, one wave per query and group of 32
 //      heads, the gathered 32-key blocks of the scores-at kernel): d^T = K Q^T
 //      recomputed per block (lanes are heads, accumulator rows keys); dw += g
 //      relu(d^T) per lane; dq += (m g) K, whose A operand comes straight from
@@ -28,14 +25,14 @@
 //      key-major; dq stays in registers for the whole row and is scaled by w at
 //      the end.  Each entry's ReLU mask (one bit per head) goes to the
 //      workspace.
-//   3. bucket_entries_kernel: each row's valid entries {key, g, masks} sorted
+//   2. bucket_entries_kernel: each row's valid entries {key, g, masks} sorted
 //      into buckets of 64 keys (workspace).
-//   4. dk_entries_kernel (key-major): a workgroup owns 256 keys (64 per wave)
+//   3. dk_entries_kernel (key-major): a workgroup owns 256 keys (64 per wave)
 //      and streams the queries that can see them; per query, each wave turns
 //      its bucket into the A operand bf16(G w_h m_h) of its 64 keys (G the
 //      summed g of a key) and dk += A Q accumulates in registers, with no
-//      second recompute of q . k; the workgroup's partial is added to dk once
-//      at the end.
+//      second recompute of q . k; q is read in its own layout.  The
+//      workgroup's partial is added to dk once at the end.
 //
 // Every term of a gradient product carries one bfloat16 rounding, the one a
 // bfloat16 autograd graph of the forward makes: the upstream factor is
@@ -57,14 +54,28 @@ constexpr int kBwWaitVmcnt0 = 0x0F70;     // s_waitcnt vmcnt(0), expcnt/lgkmcnt 
 constexpr int kKeysPerGroup = 256;        // keys per dk workgroup (64 per wave)
 constexpr int kQueryChunk = 128;          // queries per dk workgroup
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats rounded to bf16 (to nearest even) in one packed conversion.
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-    return (uint32_t)bf16_bits(lo) | ((uint32_t)bf16_bits(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
-// Keep the low and/or high bf16 of v where the matching accumulator is > 0.
-__device__ __forceinline__ uint32_t mask_pair(uint32_t v, float a_lo, float a_hi) {
-    const uint32_t m = (a_lo > 0.0f ? 0x0000FFFFu : 0u) | (a_hi > 0.0f ? 0xFFFF0000u : 0u);
-    return v & m;
+// Lane LANE of v takes the wave-uniform value s (v_writelane_b32).
+template <int LANE>
+__device__ __forceinline__ void write_lane(uint32_t& v, uint32_t s) {
+    asm("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(s), "i"(LANE));
+}
+
+// v_writelane_b32 can read an SGPR that a VALU instruction (a compare for a
+// ballot) wrote just before it with its old value: wait states between the
+// ballots and the lane writes that read them.  Every value passes through
+// the statement, so each ballot is complete before it and each lane write
+// after it.
+__device__ __forceinline__ void settle_sgprs(unsigned long long (&v)[8]) {
+    asm volatile("s_nop 4" : "+s"(v[0]), "+s"(v[1]), "+s"(v[2]), "+s"(v[3]), "+s"(v[4]), "+s"(v[5]), "+s"(v[6]),
+                 "+s"(v[7]));
 }
 
 typedef __attribute__((address_space(1))) float gfloat;
@@ -121,13 +132,27 @@ inline long dk_grid(int B, int S, int skv, int ratio, bool causal) {
 
 }  // namespace
 
-// ---------------------------------------------------------------- 3. entries by key group
+// ---------------------------------------------------------------- entries by key group
+
+// A head group's ReLU mask (bit l = head l) in pair order: bit i holds head
+// 2i and bit 16 + i head 2i + 1 (the even heads in the low half, the odd in
+// the high), so one 16-bit-lane shift pair turns a head pair into the mask of
+// a packed bf16 pair.
+__device__ __forceinline__ uint32_t pair_order(uint32_t x) {
+    uint32_t t;
+    t = (x ^ (x >> 1)) & 0x22222222u; x ^= t ^ (t << 1);
+    t = (x ^ (x >> 2)) & 0x0C0C0C0Cu; x ^= t ^ (t << 2);
+    t = (x ^ (x >> 4)) & 0x00F000F0u; x ^= t ^ (t << 4);
+    t = (x ^ (x >> 8)) & 0x0000FF00u; x ^= t ^ (t << 8);
+    return x;
+}
 
 // One workgroup per (b, t) (blockIdx.x = b * S + t): the row's valid entries
 // (key in [ks, ke)) sorted into buckets of 64 keys (bucket g holds keys 64g ..
 // 64g + 63), each entry {key, g bits, ReLU mask of heads 0-31, of heads
-// 32-63} (16 bytes), at ent[row][off[row][g] .. off[row][g + 1]); off has
-// ngroups + 1 entries per row.  The order inside a bucket is not specified.
+// 32-63} (16 bytes, masks in pair order), at ent[row][off[row][g] .. off[row][g
+// + 1]); off has ngroups + 1 entries per row.  The order inside a bucket is
+// not specified.
 __global__ __launch_bounds__(256) void bucket_entries_kernel(const int32_t* __restrict__ indices,
                                                              const float* __restrict__ grad,
                                                              const uint32_t* __restrict__ masks, int nhg, int S,
@@ -189,51 +214,14 @@ __global__ __launch_bounds__(256) void bucket_entries_kernel(const int32_t* __re
         const int s = irow[j];
         if (s >= lo && s < hi) {
             const int pos = atomicAdd(&cnt[s >> 6], 1);
-            const uint32_t m0 = mrow[j];
-            const uint32_t m1 = nhg > 1 ? mrow[topk + j] : 0u;
+            const uint32_t m0 = pair_order(mrow[j]);
+            const uint32_t m1 = nhg > 1 ? pair_order(mrow[topk + j]) : 0u;
             erow[pos] = u32x4{(uint32_t)s, __float_as_uint(grow[j]), m0, m1};
         }
     }
 }
 
-// ---------------------------------------------------------------- 1. dk B fragments of q
-
-// Fragment (hs, dt) of query (t, b), lane l, holds q[head][32 dt + l%32] (the
-// bf16 input bits) for the 8 heads 32(hs/2) + 16(hs%2) + 8(jj/4) + 4(l/32) + jj%4,
-// jj = 0..7: the order in which the dk A operand walks a D accumulator's rows.
-// Padded heads and index_dim entries >= D are zero.  One wave per (t, b);
-// 1 KiB per fragment.
-template <int H, int DP>
-__global__ __launch_bounds__(64) void qt_fragments_kernel(const uint16_t* __restrict__ q, int D,
-                                                          uint8_t* __restrict__ qt) {
-    using T = BwTiling<H, DP>;
-    const int lane = threadIdx.x, hf = lane >> 5, l32 = lane & 31;
-    const long tb = blockIdx.x;                           // t * B + b
-    const uint16_t* qrow = q + tb * H * D;
-    uint8_t* dst = qt + tb * T::QT_BYTES + 16 * lane;
-#pragma unroll
-    for (int hs = 0; hs < T::NHS; ++hs)
-#pragma unroll
-        for (int dt = 0; dt < T::NDT; ++dt) {
-            const int d = 32 * dt + l32;
-            uint32_t pk[4];
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                uint32_t half[2];
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const int jj = 2 * p + u;
-                    const int h = 32 * (hs >> 1) + 16 * (hs & 1) + 8 * (jj >> 2) + 4 * hf + (jj & 3);
-                    const uint16_t v = qrow[(long)min(h, H - 1) * D + min(d, D - 1)];
-                    half[u] = (h < H && d < D) ? (uint32_t)v : 0u;
-                }
-                pk[p] = half[0] | (half[1] << 16);
-            }
-            *reinterpret_cast<u32x4*>(dst + (hs * T::NDT + dt) * 1024) = u32x4{pk[0], pk[1], pk[2], pk[3]};
-        }
-}
-
-// ---------------------------------------------------------------- 2. dq, dw (query-major)
+// ---------------------------------------------------------------- dq, dw (query-major)
 
 // One wave per (query, group of up to 32 heads): the wave's dq accumulators
 // (32 x DP fp32) and q fragments leave room for two waves per SIMD.  The
@@ -355,15 +343,21 @@ __global__ __launch_bounds__(64, 2) void backward_rows_kernel(InLayout L, const 
         // ReLU masks of the block's entries for this wave's heads, for the dk
         // kernel: bit l of entry (32 blk + k) = d of head h0 + l > 0, where
         // accumulator slot i holds key c_row(i, hf) and lane l%32 head h0 + l%32.
-        // Lane k < 32 collects entry k's mask from the ballots.
+        // Slot i's ballot holds the masks of keys c_row(i, 0) (low half) and
+        // c_row(i, 1) (high half); lane k < 32 takes entry k's.
         {
             uint32_t mk = 0u;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const unsigned long long bal = __ballot(acct[0][i] > 0.0f);
-                mk = (l32 == c_row(i, 0)) ? (uint32_t)bal : mk;
-                mk = (l32 == c_row(i, 1)) ? (uint32_t)(bal >> 32) : mk;
-            }
+            static_for<0, 2>([&](auto hc) {
+                constexpr int i0 = 8 * decltype(hc)::value;
+                unsigned long long bal[8];
+                static_for<0, 8>([&](auto ic) { bal[ic] = __ballot(acct[0][i0 + ic] > 0.0f); });
+                settle_sgprs(bal);
+                static_for<0, 8>([&](auto ic) {
+                    constexpr int i = i0 + decltype(ic)::value;
+                    write_lane<c_row(i, 0)>(mk, (uint32_t)bal[ic]);
+                    write_lane<c_row(i, 1)>(mk, (uint32_t)(bal[ic] >> 32));
+                });
+            });
             const int j = 32 * blk + l32;
             if (hf == 0 && j < topk) mrow[j] = mk;
         }
@@ -373,9 +367,6 @@ __global__ __launch_bounds__(64, 2) void backward_rows_kernel(InLayout L, const 
 #pragma unroll
             for (int i = 0; i < 16; ++i) dwacc[r] = fmaf(gv[i], relu(acct[r][i]), dwacc[r]);
         // dq += (m * g) K over the block's 32 keys (two k-steps of 16).
-        uint32_t gpk[8];
-#pragma unroll
-        for (int p = 0; p < 8; ++p) gpk[p] = pack_bf16(gv[2 * p], gv[2 * p + 1]);
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             bf16x8 kt[T::NDT];
@@ -392,8 +383,10 @@ __global__ __launch_bounds__(64, 2) void backward_rows_kernel(InLayout L, const 
             for (int r = 0; r < T::NRT; ++r) {
                 u32x4 av;
 #pragma unroll
-                for (int p = 0; p < 4; ++p)
-                    av[p] = mask_pair(gpk[4 * s + p], acct[r][8 * s + 2 * p], acct[r][8 * s + 2 * p + 1]);
+                for (int p = 0; p < 4; ++p) {
+                    const int i0 = 8 * s + 2 * p;
+                    av[p] = pack_bf16(acct[r][i0] > 0.0f ? gv[i0] : 0.0f, acct[r][i0 + 1] > 0.0f ? gv[i0 + 1] : 0.0f);
+                }
                 const bf16x8 af = as_bf16x8(av);
 #pragma unroll
                 for (int dt = 0; dt < T::NDT; ++dt) dqacc[r][dt] = mfma_32x32x16(af, kt[dt], dqacc[r][dt]);
@@ -449,44 +442,59 @@ __global__ __launch_bounds__(64, 2) void backward_rows_kernel(InLayout L, const 
     }
 }
 
-// ---------------------------------------------------------------- 4. dk (key-major)
+// ---------------------------------------------------------------- dk (key-major)
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // this wave are outstanding (expcnt and lgkmcnt left at their maxima).
 constexpr int wait_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// Mask of a packed bf16 pair from a pair-order mask word shifted so that the
+// pair's two bits sit at bits 15 and 31: each 16-bit half becomes all ones
+// where its bit is set (an arithmetic shift of each half by 15).
+__device__ __forceinline__ uint32_t half_masks(uint32_t x) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(s16x2, x) >> (short)15);
+}
+
 // A workgroup owns 256 keys (64 per wave: wave w owns bucket 4 kg + w) and
 // streams the queries of one chunk that can see them.  Per query, through a
 // three-stage rotation of LDS buffers (one barrier per query), it moves in by
-// direct loads the query's dk B fragments of q, one copy of its head weights
-// per wave and each wave's bucket of entries (up to 64; more only with
-// repeated keys).  A wave builds a 64-slot table of its keys (summed g and
-// ReLU masks, from the rows kernel's recompute) and forms the dk A operand
-// bf16(G w_h) where m_h, else 0, in the order of the B fragments' heads: the
-// product needs no recompute of q . k.  dk stays in registers; the
-// workgroup's partial is added to dk once at the end.
+// direct loads the query's q rows (16-byte chunks, the chunk index XOR-ed
+// with the head's low three bits), one copy of its head weights per wave and
+// each wave's bucket of entries (up to 64; more only with repeated keys).  A
+// wave builds a 64-slot table of its keys (summed g and ReLU masks, from the
+// rows kernel's recompute) and forms the dk A operand bf16(G w_h) where m_h,
+// else 0, for the heads of the B fragments, which transposing LDS reads take
+// from the q rows: the product needs no recompute of q . k.  dk stays in
+// registers; the workgroup's partial is added to dk once at the end.
 template <int H, int DP>
-__global__ __launch_bounds__(256, 2) void dk_entries_kernel(const float* __restrict__ w,
+__global__ __launch_bounds__(256, 2) void dk_entries_kernel(const uint16_t* __restrict__ q,
+                                                            const float* __restrict__ w,
                                                             const int32_t* __restrict__ off,
-                                                            const u32x4* __restrict__ ent,
-                                                            const uint8_t* __restrict__ qtf, int B, int S, int skv,
+                                                            const u32x4* __restrict__ ent, int B, int S, int skv,
                                                             int ratio, const int32_t* __restrict__ ks,
                                                             const int32_t* __restrict__ ke, int topk, int ngroups,
                                                             int D, float* __restrict__ dk) {
     using T = BwTiling<H, DP>;
-    // Stage: q in dk B-fragment order, per wave one copy of the head weights
-    // (64 floats; heads past H repeat w[H-1] and meet zero B rows) and the
-    // wave's bucket (64 entries of 16 bytes).
-    constexpr int QT = 0, WS = T::QT_BYTES, ES = WS + 4 * 4 * 64;
+    // Stage: q rows of heads 0 .. 32 NRT - 1 (rows past H repeat head H - 1,
+    // chunks past index_dim repeat its last chunk: they meet zero A entries or
+    // feed dk columns that are not stored), per wave one copy of the head
+    // weights (64 floats; heads past H repeat w[H-1]) and the wave's bucket
+    // (64 entries of 16 bytes).
+    constexpr int CPK = DP / 8;                              // 16-byte chunks per head row
+    constexpr int QBYTES = 32 * T::NRT * DP * 2;
+    constexpr int QBLK = QBYTES / 1024;                      // 1 KiB direct loads (one per wave instruction)
+    constexpr int QT = 0, WS = QBYTES, ES = WS + 4 * 4 * 64;
     constexpr int STAGE = ES + 4 * 64 * 16;
     __shared__ __attribute__((aligned(16))) uint8_t lds0[STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t lds1[STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t lds2[STAGE];
     __shared__ int offs[kQueryChunk][5];                    // bucket bounds of the chunk's queries
     __shared__ float tab_g[4][64];                          // per wave: summed g of its keys
-    __shared__ uint2 tab_m[4][64];                          // per wave: ReLU masks of its keys
-    constexpr int PER_WAVE = T::NHS * T::NDT / 4 + 2;       // vector-memory operations per stage and wave
-    static_assert((T::NHS * T::NDT) % 4 == 0, "fragment blocks split over 4 waves");
+    __shared__ uint2 tab_m[4][64];                          // per wave: ReLU masks of its keys (pair order)
+    constexpr int PER_WAVE = QBLK / 4 + 2;                  // vector-memory operations per stage and wave
+    static_assert(QBLK % 4 == 0, "q blocks split over 4 waves");
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
     int zc, b, kg;
@@ -502,18 +510,28 @@ __global__ __launch_bounds__(256, 2) void dk_entries_kernel(const float* __restr
 
     // Bucket bounds of buckets 4 kg .. 4 kg + 4 for every query of the chunk.
     for (int i = tid; i < (t1 - t0) * 5; i += 256) {
-        const int q = i / 5, k = i % 5;
-        const long row = (long)b * S + t0 + q;
-        offs[q][k] = off[row * (ngroups + 1) + min(4 * kg + k, ngroups)];
+        const int qq = i / 5, k = i % 5;
+        const long row = (long)b * S + t0 + qq;
+        offs[qq][k] = off[row * (ngroups + 1) + min(4 * kg + k, ngroups)];
     }
     __syncthreads();
 
-    auto stage = [&](int t, uint8_t* st_base) {
-        const uint8_t* src = qtf + ((long)t * B + b) * T::QT_BYTES + 16 * lane;
+    // The q chunks this lane moves: LDS position P = 64 blk + lane holds
+    // head P / CPK, chunk (P % CPK) ^ (head % 8) (element offsets in a query's
+    // [H, D] rows, clamped as above).
+    int qofs[QBLK / 4];
 #pragma unroll
-        for (int blk = wave; blk < T::NHS * T::NDT; blk += 4)
-            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + blk * 1024),
-                                             (lds_ptr_t)(st_base + QT + blk * 1024), 16, 0, 0);
+    for (int u = 0; u < QBLK / 4; ++u) {
+        const int pos = 64 * (wave + 4 * u) + lane, head = pos / CPK;
+        const int c = (pos % CPK) ^ (head & 7);
+        qofs[u] = min(head, H - 1) * D + 8 * min(c, D / 8 - 1);
+    }
+    auto stage = [&](int t, uint8_t* st_base) {
+        const uint16_t* qrow = q + ((long)t * B + b) * H * D;
+#pragma unroll
+        for (int u = 0; u < QBLK / 4; ++u)
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(qrow + qofs[u]),
+                                             (lds_ptr_t)(st_base + QT + (wave + 4 * u) * 1024), 16, 0, 0);
         const float* wrow = w + ((long)t * B + b) * H;
         __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(wrow + min(lane, H - 1)),
                                          (lds_ptr_t)(st_base + WS + 4 * 64 * wave), 4, 0, 0);
@@ -525,6 +543,23 @@ __global__ __launch_bounds__(256, 2) void dk_entries_kernel(const float* __restr
         __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(ent + e),
                                          (lds_ptr_t)(st_base + ES + 1024 * wave), 16, 0, 0);
     };
+
+    // B fragments by transposing LDS reads (ds_read_b64_tr_b16): within each
+    // group of 16 lanes, output lane 4b + e receives, as its element a,
+    // element e of the 4 values source lane 4a + b reads.  Fragment (hs, dt)
+    // slot jj of lane l must hold q[head 16 hs + 8(jj/4) + 4(l/32) + jj%4]
+    // [index_dim 32 dt + l%32]: read rd = jj/4 gives slots 4rd .. 4rd + 3 if
+    // source lane (group g, a, b) reads index_dim 32 dt + 16(g%2) + 4b .. +3
+    // of head 16 hs + 8 rd + 4(g/2) + a, which the swizzled placement puts at
+    // byte tq[dt] + 16 CPK (16 hs + 8 rd).
+    int tq[T::NDT];
+    {
+        const int sg = lane >> 4, sa = (lane & 15) >> 2, sb = lane & 3;
+        const int hm = 4 * (sg >> 1) + sa;                        // head within the 8-head read
+        const int xl = (2 * (sg & 1) + (sb >> 1)) ^ hm;
+#pragma unroll
+        for (int dt = 0; dt < T::NDT; ++dt) tq[dt] = 16 * (hm * CPK + ((4 * dt) ^ xl)) + 8 * (sb & 1);
+    }
 
     f32x16 dkacc[2][T::NDT];
 #pragma unroll
@@ -550,47 +585,55 @@ __global__ __launch_bounds__(256, 2) void dk_entries_kernel(const float* __restr
             if (i < n) put(ent[((long)b * S + t) * topk + beg + i]);
         }
         float G[2];
-        uint2 mk[2];
+        uint32_t mw[2][T::NRT];
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
             G[kc] = tab_g[wave][32 * kc + l32];
-            mk[kc] = tab_m[wave][32 * kc + l32];
+            const uint2 m = tab_m[wave][32 * kc + l32];
+            // Pair i of heads 32r + 2i, + 2i + 1 at bits i and 16 + i; this
+            // lane's pairs start at 2 hf.
+            mw[kc][0] = m.x >> (2 * hf);
+            if constexpr (T::NRT > 1) mw[kc][1] = m.y >> (2 * hf);
         }
-        // dk += A Q: A row = key 32 kc + lane%32, k = the 8 heads of this
-        // lane's B-fragment rows (fragment hs = 2r + s: heads 32r + 16s +
-        // 8(jj/4) + 4hf + jj%4); A = bf16(G w_h) where the head's mask bit is
-        // set, else 0; B the query's exact q fragments.
+        // dk += A Q: A row = key 32 kc + lane%32, k = the 8 heads 32r + 16s +
+        // 8(jj/4) + 4hf + jj%4 of fragment hs = 2r + s; A = bf16(G w_h) where
+        // the head's mask bit is set, else 0; B the query's exact q.
         const float* wl = reinterpret_cast<const float*>(st_base + WS + 4 * 64 * wave);
 #pragma unroll
         for (int r = 0; r < T::NRT; ++r)
 #pragma unroll
             for (int sst = 0; sst < 2; ++sst) {
+                const int hs = 2 * r + sst;
+                bf16x8 qf[T::NDT];
+#pragma unroll
+                for (int dt = 0; dt < T::NDT; ++dt) {
+                    i16x4 part[2];
+#pragma unroll
+                    for (int rd = 0; rd < 2; ++rd)
+                        part[rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(
+                            const_cast<uint8_t*>(st_base) + QT + 16 * CPK * (16 * hs + 8 * rd) + tq[dt]));
+                    qf[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+                }
                 float wv[8];
 #pragma unroll
                 for (int g4 = 0; g4 < 2; ++g4) {
                     const float4 v4 = *reinterpret_cast<const float4*>(wl + 32 * r + 8 * (2 * sst + g4) + 4 * hf);
                     wv[4 * g4 + 0] = v4.x; wv[4 * g4 + 1] = v4.y; wv[4 * g4 + 2] = v4.z; wv[4 * g4 + 3] = v4.w;
                 }
-                bf16x8 af[2];
 #pragma unroll
                 for (int kc = 0; kc < 2; ++kc) {
-                    const uint32_t bits = r == 0 ? mk[kc].x : mk[kc].y;   // heads 32r .. 32r + 31
                     u32x4 av;
 #pragma unroll
                     for (int p = 0; p < 4; ++p) {
-                        const int hl0 = 16 * sst + 8 * (p >> 1) + 4 * hf + 2 * (p & 1);   // head - 32r of jj = 2p
-                        const float e0 = ((bits >> hl0) & 1u) ? G[kc] * wv[2 * p] : 0.0f;
-                        const float e1 = ((bits >> (hl0 + 1)) & 1u) ? G[kc] * wv[2 * p + 1] : 0.0f;
-                        av[p] = pack_bf16(e0, e1);
+                        // heads 32r + 16 sst + 8(p/2) + 4hf + 2(p%2) and + 1: pair
+                        // 8 sst + 4(p/2) + 2hf + p%2, at bits ip and 16 + ip of mw.
+                        const int ip = 8 * sst + 4 * (p >> 1) + (p & 1);
+                        av[p] = pack_bf16(G[kc] * wv[2 * p], G[kc] * wv[2 * p + 1]) &
+                                half_masks(mw[kc][r] << (15 - ip));
                     }
-                    af[kc] = as_bf16x8(av);
-                }
+                    const bf16x8 af = as_bf16x8(av);
 #pragma unroll
-                for (int dt = 0; dt < T::NDT; ++dt) {
-                    const bf16x8 qf = as_bf16x8(*reinterpret_cast<const u32x4*>(
-                        st_base + QT + ((2 * r + sst) * T::NDT + dt) * 1024 + 16 * lane));
-#pragma unroll
-                    for (int kc = 0; kc < 2; ++kc) dkacc[kc][dt] = mfma_32x32x16(af[kc], qf, dkacc[kc][dt]);
+                    for (int dt = 0; dt < T::NDT; ++dt) dkacc[kc][dt] = mfma_32x32x16(af, qf[dt], dkacc[kc][dt]);
                 }
             }
     };
@@ -648,7 +691,6 @@ static hipError_t launch_backward_t(const BackwardArgs& p) {
                static_cast<const uint16_t*>(p.k), (long)p.B * p.D, (long)p.D, p.D};
     const BackwardLayout ly = backward_layout(p.B, p.S, p.Skv, H, p.D, p.topk);
     uint8_t* ws = static_cast<uint8_t*>(p.workspace);
-    uint8_t* qtf = ws + ly.qt;
     uint32_t* masks = reinterpret_cast<uint32_t*>(ws + ly.masks);
     int32_t* off = reinterpret_cast<int32_t*>(ws + ly.off);
     u32x4* ent = reinterpret_cast<u32x4*>(ws + ly.ent);
@@ -656,16 +698,15 @@ static hipError_t launch_backward_t(const BackwardArgs& p) {
     const int nhg = H / rows_heads(H);
     const int ngroups = (p.Skv + 63) / 64;
     if (ngroups > 512) return hipErrorInvalidValue;          // the bucket kernel's prefix covers 512 buckets
-    hipLaunchKernelGGL((qt_fragments_kernel<H, DP>), dim3(rows), dim3(kWave), 0, p.stream,
-                       static_cast<const uint16_t*>(p.q), p.D, qtf);
     const unsigned rows8 = (rows + kXcds - 1) / kXcds * kXcds;
     hipLaunchKernelGGL((backward_rows_kernel<H, DP>), dim3(rows8 * (unsigned)nhg), dim3(kWave), 0, p.stream, L, p.w,
                        p.indices, p.grad, p.B, p.S, p.Skv, p.ratio, p.ks, p.ke, p.topk, p.dq, p.dw, masks);
     hipLaunchKernelGGL(bucket_entries_kernel, dim3(rows), dim3(256), (size_t)(ngroups + 1) * 4, p.stream, p.indices,
                        p.grad, masks, nhg, p.S, p.Skv, p.ratio, p.ks, p.ke, p.topk, ngroups, off, ent);
     const long grid = dk_grid(p.B, p.S, p.Skv, p.ratio, p.ks == nullptr);
-    hipLaunchKernelGGL((dk_entries_kernel<H, DP>), dim3((unsigned)grid), dim3(256), 0, p.stream, p.w, off, ent, qtf,
-                       p.B, p.S, p.Skv, p.ratio, p.ks, p.ke, p.topk, ngroups, p.D, p.dk);
+    hipLaunchKernelGGL((dk_entries_kernel<H, DP>), dim3((unsigned)grid), dim3(256), 0, p.stream,
+                       static_cast<const uint16_t*>(p.q), p.w, off, ent, p.B, p.S, p.Skv, p.ratio, p.ks, p.ke,
+                       p.topk, ngroups, p.D, p.dk);
     return hipGetLastError();
 }
 

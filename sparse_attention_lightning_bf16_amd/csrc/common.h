@@ -4,9 +4,22 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "tiling.h"
 
 namespace lix {
+
+// f(integral_constant<int, I>) for I = 0 .. N-1, unrolled at compile time
+// whatever the loop body's size (the register arrays it indexes must never be
+// indexed at run time, and I can be a template or asm immediate argument).
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));

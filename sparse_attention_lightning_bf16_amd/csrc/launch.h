@@ -124,12 +124,11 @@ struct BackwardArgs {
     hipStream_t stream;
 };
 // Workspace of the backward, byte offsets of its parts (each 256-byte
-// aligned): q re-laid as the dk B fragments ([S,B] blocks of BwTiling's
-// QT_BYTES); the rows kernel's ReLU masks ([B,S] x ceil(H/32) x topk uint32);
+// aligned): the rows kernel's ReLU masks ([B,S] x ceil(H/32) x topk uint32);
 // bucket bounds ([B,S] x (ceil(Skv/64) + 1) int32); the entries bucketed by
-// 64-key group ([B,S,topk] x 16 bytes).  O(B S (topk + Skv/64) + S B H D).
+// 64-key group ([B,S,topk] x 16 bytes).  O(B S (topk + Skv/64)).
 struct BackwardLayout {
-    long qt, masks, off, ent, total;
+    long masks, off, ent, total;
 };
 BackwardLayout backward_layout(int B, int S, int Skv, int H, int D, int topk);
 long backward_workspace_bytes(int B, int S, int Skv, int H, int D, int topk);

@@ -54,11 +54,11 @@ long streaming_slot_bytes(int H, int D, int Skv) {
 
 BackwardLayout backward_layout(int B, int S, int Skv, int H, int D, int topk) {
     auto up = [](long x) { return (x + 255) & ~255L; };
-    const int nrt = H > 32 ? 2 : 1, ndt = padded_dim(D) / 32, nhg = H > 32 ? H / 32 : 1;
+    (void)D;   // q is read in place
+    const int nhg = H > 32 ? H / 32 : 1;
     const long rows = (long)B * S;
     BackwardLayout ly{};
-    ly.qt = 0;
-    ly.masks = up(rows * (2 * nrt) * ndt * 1024);
+    ly.masks = 0;
     ly.off = ly.masks + up(rows * topk * nhg * 4);
     ly.ent = ly.off + up(rows * ((Skv + 63) / 64 + 1) * 4);
     ly.total = ly.ent + up(rows * topk * 16);

@@ -157,17 +157,6 @@ __device__ __forceinline__ int mbcnt(unsigned long long mask, int acc) {
 // hold NaN slots) or for every chunk when ALL_PARTIAL.  The bounds pass
 // through an empty asm statement so each pass recomputes its scalar chunk
 // conditions instead of keeping them live across the kernel.
-// f(integral_constant<int, I>) for I = 0 .. N-1, unrolled at compile time
-// whatever the loop body's size (the register arrays it indexes must never be
-// indexed at run time).
-template <int I, int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-    if constexpr (I < N) {
-        f(std::integral_constant<int, I>{});
-        static_for<I + 1, N>(f);
-    }
-}
-
 template <int NCH, bool ALL_PARTIAL, class F>
 __device__ __forceinline__ void visit_chunks(int jmax, int jpart, F&& f) {
     asm volatile("" : "+s"(jmax), "+s"(jpart));

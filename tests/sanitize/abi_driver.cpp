@@ -134,7 +134,7 @@ int main() {
     if (ws <= 0) ++g_failures;
     if (lix_indexer_backward_workspace_bytes(1, 8, 40000, 64, 128, 2) != -1) ++g_failures;
     if (lix_indexer_backward_workspace_bytes(INT_MAX, INT_MAX, INT_MAX, 64, 128, 2) != -1) ++g_failures;
-    EXPECT(lix_indexer_backward(p, p, fp, ip, fp, 1, 8, 4, 64, 128, 4, nullptr, nullptr, 2, fp, fp, fp, p, 1000,
+    EXPECT(lix_indexer_backward(p, p, fp, ip, fp, 1, 8, 4, 64, 128, 4, nullptr, nullptr, 2, fp, fp, fp, p, ws - 1,
                                 nullptr), SHP);
     EXPECT(lix_indexer_backward(p, p, fp, ip, fp, 1, 8, 4, 128, 128, 4, nullptr, nullptr, 2, fp, fp, fp, p, ws,
                                 nullptr), UNS);

@@ -213,7 +213,7 @@ def backward_call(q=P, k=P, w=P, idx=P, g=P, B=1, S=8, Skv=4, H=64, D=128, c=4, 
     (dict(q=P + 4), UNSUP), (dict(g=P + 2), UNSUP), (dict(dk=P + 4), UNSUP), (dict(dq=P + 2), UNSUP),
     (dict(dw=P + 1), UNSUP), (dict(B=1 << 16, S=1 << 16, topk=1 << 16), UNSUP),
     (dict(B=262144, S=2, D=64), UNSUP),            # key row stride B * index_dim = 2^24
-    (dict(ws=None), NULL), (dict(ws_bytes=1000), SHAPE), (dict(ws=P + 16), UNSUP), (dict(Skv=32769), UNSUP),
+    (dict(ws=None), NULL), (dict(ws_bytes=767), SHAPE), (dict(ws=P + 16), UNSUP), (dict(Skv=32769), UNSUP),
 ])
 def test_backward_validation(kw, code):
     assert backward_call(**kw) == code
@@ -224,17 +224,17 @@ def test_backward_workspace_bytes():
     up = lambda x: (x + 255) // 256 * 256
 
     def parts(B, S, Skv, H, D, tk):
-        # q as dk B fragments, ReLU masks per entry and 32 heads, bucket bounds
-        # per 64 keys, 16-byte bucketed entries: no [B,S,Skv] term
-        hp, dp, nhg = (64 if H > 32 else 32), (64 if D <= 64 else 128), max(1, H // 32)
-        return (up(S * B * hp * dp * 2) + up(B * S * tk * nhg * 4) + up(B * S * ((Skv + 63) // 64 + 1) * 4)
-                + up(B * S * tk * 16))
+        # ReLU masks per entry and 32 heads, bucket bounds per 64 keys, 16-byte
+        # bucketed entries: no [B,S,Skv] term and no copy of q
+        nhg = max(1, H // 32)
+        return up(B * S * tk * nhg * 4) + up(B * S * ((Skv + 63) // 64 + 1) * 4) + up(B * S * tk * 16)
     for args in ((1, 8, 4, 64, 128, 2), (2, 100, 30, 16, 48, 7), (1, 32768, 8192, 64, 128, 2048),
                  (1, 131072, 32768, 64, 128, 2048)):
         assert lib.lix_indexer_backward_workspace_bytes(*args) == parts(*args), args
-    assert lib.lix_indexer_backward_workspace_bytes(1, 8, 4, 64, 128, 2) == 131072 + 3 * 256
-    # 32K: 2.0 GiB, 131K: 8.2 GiB (a dense [B,S,Skv] fp32 gradient alone would be 1 GiB / 16 GiB)
-    assert lib.lix_indexer_backward_workspace_bytes(1, 131072, 32768, 64, 128, 2048) < 9 << 30
+    assert lib.lix_indexer_backward_workspace_bytes(1, 8, 4, 64, 128, 2) == 3 * 256
+    # 32K: 1.5 GiB, 131K: 6.3 GiB (a dense [B,S,Skv] fp32 gradient alone would be 1 GiB / 16 GiB)
+    assert lib.lix_indexer_backward_workspace_bytes(1, 32768, 8192, 64, 128, 2048) < 1.6 * (1 << 30)
+    assert lib.lix_indexer_backward_workspace_bytes(1, 131072, 32768, 64, 128, 2048) < 6.5 * (1 << 30)
     assert lib.lix_indexer_backward_workspace_bytes(1, 8, 4, 128, 128, 2) == -1
     assert lib.lix_indexer_backward_workspace_bytes(1, 8, 40000, 64, 128, 2) == -1
     assert lib.lix_indexer_backward_workspace_bytes(1, 8, 4, 64, 128, 0) == -1
@@ -274,9 +274,9 @@ def backward_noalloc_call(q=P, k=P, w=P, idx=P, g=P, B=1, S=8, Skv=4, H=64, D=12
     (dict(q=None), NULL), (dict(idx=None), NULL), (dict(g=None), NULL), (dict(dk=None), NULL),
     (dict(B=0), SHAPE), (dict(topk=0), SHAPE), (dict(ke=P), SHAPE),
     (dict(H=128), UNSUP), (dict(D=32), UNSUP), (dict(dk=P + 4), UNSUP), (dict(Skv=32769), UNSUP),
-    # workspace above the static array: q as dk fragments alone is 512 MiB here
-    (dict(B=1, S=32768, Skv=8192), UNSUP),
-    (dict(B=1, S=1024, Skv=1024), DEVICE),       # about 16 MiB: fits, stops at the device check
+    # workspace above the static array: the entries alone are 256 MiB here
+    (dict(B=1, S=32768, Skv=8192, topk=512), UNSUP),
+    (dict(B=1, S=1024, Skv=1024), DEVICE),       # fits, stops at the device check
 ])
 def test_backward_noalloc_validation(kw, code):
     assert backward_noalloc_call(**kw) == code
@@ -285,7 +285,7 @@ def test_backward_noalloc_validation(kw, code):
 def test_backward_noalloc_limit_matches_the_workspace_size():
     lib = lx.load()
     cap = _lib.LIX_NOALLOC_SCRATCH_BYTES
-    assert lib.lix_indexer_backward_workspace_bytes(1, 2048, 2048, 64, 128, 2) <= cap
-    assert backward_noalloc_call(B=1, S=2048, Skv=2048) == DEVICE
-    assert lib.lix_indexer_backward_workspace_bytes(1, 4096, 4096, 64, 128, 2) > cap
-    assert backward_noalloc_call(B=1, S=4096, Skv=4096) == UNSUP
+    assert lib.lix_indexer_backward_workspace_bytes(1, 4096, 4096, 64, 128, 512) <= cap
+    assert backward_noalloc_call(B=1, S=4096, Skv=4096, topk=512) == DEVICE
+    assert lib.lix_indexer_backward_workspace_bytes(1, 4096, 4096, 64, 128, 1024) > cap
+    assert backward_noalloc_call(B=1, S=4096, Skv=4096, topk=1024) == UNSUP
