@@ -281,16 +281,19 @@ __global__ __launch_bounds__(64, 2) void backward_rows_kernel(InLayout L, const 
     // jj%4, index_dim 32dt + l%32): read rd = jj/4 gives slots 4rd .. 4rd + 3 if
     // source lane (group g, a, b) reads index_dim 32dt + 16(g%2) + 4b .. +3 of key
     // 16s + 8rd + 4(g/2) + a.  In the BlockMap placement (8-chunk segments) that
-    // is byte tbase[dt%2][rd] + 1024(4(dt/2) + 2s + rd).
+    // is byte tbase[dt%2][rd] + 1024(4(dt/2) + 2s + rd): load 4(dt/2) + 2s + rd
+    // (parity rd), row m = 4(g/2) + a, chunk 4(dt%2) + 2(g%2) + b/2 of the segment.
+    static_assert(M::SEG == 8, "transposing reads assume 8-chunk row segments");
     int tbase[2][2];
     {
         const int tg = lane >> 4, ta = (lane & 15) >> 2, tb = lane & 3;
         const int tm = 4 * (tg >> 1) + ta;                      // row within the 8-row load
-        const int tx = (2 * (tg & 1) + (tb >> 1)) ^ tm;          // chunk within the segment, before swizzle
+        const int x0 = 2 * (tg & 1) + (tb >> 1);                 // chunk within the 32 index_dim values
 #pragma unroll
         for (int p2 = 0; p2 < 2; ++p2)
 #pragma unroll
-            for (int rd = 0; rd < 2; ++rd) tbase[p2][rd] = 16 * (8 * tm + (tx ^ (4 * p2) ^ rd)) + 8 * (tb & 1);
+            for (int rd = 0; rd < 2; ++rd)
+                tbase[p2][rd] = 16 * (8 * tm + ((4 * p2 + x0) ^ M::swz(rd, tm))) + 8 * (tb & 1);
     }
     int fofs[M::KR];
 #pragma unroll
@@ -457,11 +460,23 @@ __device__ __forceinline__ uint32_t half_masks(uint32_t x) {
     return __builtin_bit_cast(uint32_t, __builtin_bit_cast(s16x2, x) >> (short)15);
 }
 
+// Chunk swizzle of the dk kernel's staged q rows: chunk c (16 bytes) of head
+// h sits at position c ^ q_swizzle(h) of the head's row.  The transposing
+// reads of one fragment take 8 heads x 32 index_dim values; with rows of 256
+// (or 128) bytes the unswizzled chunks of heads 4a .. 4a + 3 share their LDS
+// banks, and this XOR (a search over XOR masks of the head's low bits) puts
+// every 32 lanes of a read on 64 distinct banks and every 16 on 32.
+template <int CPK>
+__device__ __forceinline__ int q_swizzle(int h) {
+    if constexpr (CPK == 16) return ((h & 1) ? 4 : 0) ^ ((h & 2) ? 10 : 0);
+    else return ((h & 1) ? 2 : 0) ^ ((h & 2) ? 4 : 0);
+}
+
 // A workgroup owns 256 keys (64 per wave: wave w owns bucket 4 kg + w) and
 // streams the queries of one chunk that can see them.  Per query, through a
 // three-stage rotation of LDS buffers (one barrier per query), it moves in by
-// direct loads the query's q rows (16-byte chunks, the chunk index XOR-ed
-// with the head's low three bits), one copy of its head weights per wave and
+// direct loads the query's q rows (16-byte chunks in q_swizzle order), one
+// copy of its head weights per wave and
 // each wave's bucket of entries (up to 64; more only with repeated keys).  A
 // wave builds a 64-slot table of its keys (summed g and ReLU masks, from the
 // rows kernel's recompute) and forms the dk A operand bf16(G w_h) where m_h,
@@ -517,13 +532,14 @@ __global__ __launch_bounds__(256, 2) void dk_entries_kernel(const uint16_t* __re
     __syncthreads();
 
     // The q chunks this lane moves: LDS position P = 64 blk + lane holds
-    // head P / CPK, chunk (P % CPK) ^ (head % 8) (element offsets in a query's
-    // [H, D] rows, clamped as above).
+    // head P / CPK, chunk (P % CPK) ^ q_swizzle(head) (element offsets in a
+    // query's [H, D] rows, clamped as above).
+    static_assert(CPK == 8 || CPK == 16, "q rows of 128 or 256 bytes");
     int qofs[QBLK / 4];
 #pragma unroll
     for (int u = 0; u < QBLK / 4; ++u) {
         const int pos = 64 * (wave + 4 * u) + lane, head = pos / CPK;
-        const int c = (pos % CPK) ^ (head & 7);
+        const int c = (pos % CPK) ^ q_swizzle<CPK>(head);
         qofs[u] = min(head, H - 1) * D + 8 * min(c, D / 8 - 1);
     }
     auto stage = [&](int t, uint8_t* st_base) {
@@ -551,14 +567,15 @@ __global__ __launch_bounds__(256, 2) void dk_entries_kernel(const uint16_t* __re
     // [index_dim 32 dt + l%32]: read rd = jj/4 gives slots 4rd .. 4rd + 3 if
     // source lane (group g, a, b) reads index_dim 32 dt + 16(g%2) + 4b .. +3
     // of head 16 hs + 8 rd + 4(g/2) + a, which the swizzled placement puts at
-    // byte tq[dt] + 16 CPK (16 hs + 8 rd).
+    // byte tq[dt] + 16 CPK (16 hs + 8 rd) (the swizzle depends on a alone).
     int tq[T::NDT];
     {
         const int sg = lane >> 4, sa = (lane & 15) >> 2, sb = lane & 3;
         const int hm = 4 * (sg >> 1) + sa;                        // head within the 8-head read
-        const int xl = (2 * (sg & 1) + (sb >> 1)) ^ hm;
+        const int x0 = 2 * (sg & 1) + (sb >> 1);                  // chunk within the 32 index_dim values
 #pragma unroll
-        for (int dt = 0; dt < T::NDT; ++dt) tq[dt] = 16 * (hm * CPK + ((4 * dt) ^ xl)) + 8 * (sb & 1);
+        for (int dt = 0; dt < T::NDT; ++dt)
+            tq[dt] = 16 * (hm * CPK + ((4 * dt + x0) ^ q_swizzle<CPK>(sa))) + 8 * (sb & 1);
     }
 
     f32x16 dkacc[2][T::NDT];

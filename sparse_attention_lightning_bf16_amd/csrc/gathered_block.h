@@ -12,7 +12,10 @@ namespace lix {
 // row p % 32, chunks SEG*(p/32) .. +SEG-1, and within the segment the chunk
 // (L % SEG) ^ swz(ld, L/SEG): consecutive lanes read one contiguous piece of
 // a key row.  The swizzle makes the 16 (and each 8) consecutive lanes of a
-// B-fragment read hit distinct 16-byte bank groups.
+// B-fragment read hit distinct 16-byte bank groups, and (8-chunk segments)
+// each 32 (and 16) lanes of the backward's transposing reads of 8 keys x 32
+// index_dim values distinct banks (an XOR of the row's three bits and the
+// load's parity, found by a search over such masks).
 template <int DP>
 struct BlockMap {
     static constexpr int CPK = DP / 8;                  // 16-byte chunks per key row
@@ -23,8 +26,11 @@ struct BlockMap {
     static constexpr int BYTES = NLOAD * kWave * 16;   // one block in LDS
     static constexpr int KR = SEG == 8 ? 4 : NSTEP;     // distinct per-lane read offsets
     static_assert(SEG == 4 || SEG == 8, "row segments of 4 or 8 chunks");
+    __device__ static constexpr int seg_swz(int m) {
+        return ((m & 1) ? 2 : 0) ^ ((m & 2) ? 4 : 0) ^ ((m & 4) ? 1 : 0);
+    }
     __device__ static constexpr int swz(int ld, int m) {
-        return SEG == 8 ? (m ^ (ld & 1)) : (((m >> 1) ^ (m >> 3)) & (SEG - 1));
+        return SEG == 8 ? (seg_swz(m) ^ ((ld & 1) ? 2 : 0)) : (((m >> 1) ^ (m >> 3)) & (SEG - 1));
     }
     // Byte offset of this lane's B fragment for k-step st: key row lane % 32,
     // chunk 2 st + lane / 32.  Equals frag_off(st % KR) + 4096 (st / KR).
