@@ -42,8 +42,10 @@ struct BlockMap {
 };
 
 // Gather one block into buf: lane r < 32 holds the key row s of entry r (a
-// valid row of kb); lanes >= 32 hold a copy of lane r - 32's.  Index_dim
-// chunks past the last real one (dlim) are clamped to it.
+// valid row of kb, so s >= 0); lanes >= 32 hold a copy of lane r - 32's.
+// Index_dim chunks past the last real one (dlim) are clamped to it.  Row
+// offsets are unsigned 32 x 32 -> 64-bit products (the row stride k_s is
+// below 2^24).
 template <int DP>
 __device__ __forceinline__ void gather_block(uint8_t* buf, const uint16_t* kb, long k_s, int dlim, int s, int lane) {
     using M = BlockMap<DP>;
@@ -57,7 +59,7 @@ __device__ __forceinline__ void gather_block(uint8_t* buf, const uint16_t* kb, l
     for (int ld = 0; ld < M::NLOAD; ++ld) {
         const int p = M::RPI * ld + m;
         const int d8 = min(M::SEG * (p >> 5) + (cp ^ M::swz(ld, m)), dlim);
-        const uint16_t* src = kb + (long)rows[ld % NR] * k_s + 8 * d8;
+        const uint16_t* src = kb + (uint64_t)(uint32_t)rows[ld % NR] * (uint32_t)k_s + 8 * d8;
         __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), (lds_ptr_t)(buf + ld * kWave * 16), 16,
                                          0, 0);
     }
