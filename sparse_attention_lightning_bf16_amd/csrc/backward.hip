@@ -584,11 +584,21 @@ __global__ __launch_bounds__(256, 2) void dk_entries_kernel(const uint16_t* __re
 #pragma unroll
         for (int dt = 0; dt < T::NDT; ++dt) dkacc[kc][dt] = f32x16{};
 
-    auto compute = [&](int t, const uint8_t* st_base) {
+    // The wave's table for one query: its 64 keys' summed g and ReLU masks,
+    // built in LDS from its bucket and read back into registers (G, mw); n is
+    // the bucket's size.  It is built one query ahead, after the products of
+    // the current query are issued, so its LDS round trips overlap them.
+    struct Tab {
+        float G[2];
+        uint32_t mw[2][T::NRT];
+        int n;
+    };
+    auto prep = [&](int t, const uint8_t* st_base, Tab& tb) {
         const int beg = offs[t - t0][wave], n = offs[t - t0][wave + 1] - beg;
+        tb.n = n;
         if (n == 0) return;                                          // no entry of this wave's keys
-        // Table of the wave's 64 keys.  Every LDS operation of one wave runs
-        // in program order: clear, then add / store, then read back.
+        // Every LDS operation of one wave runs in program order: clear, then
+        // add / store, then read back.
         tab_g[wave][lane] = 0.0f;
         tab_m[wave][lane] = uint2{0u, 0u};
         auto put = [&](const u32x4& e) {
@@ -601,20 +611,22 @@ __global__ __launch_bounds__(256, 2) void dk_entries_kernel(const uint16_t* __re
             const int i = i0 + lane;
             if (i < n) put(ent[((long)b * S + t) * topk + beg + i]);
         }
-        float G[2];
-        uint32_t mw[2][T::NRT];
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
-            G[kc] = tab_g[wave][32 * kc + l32];
+            tb.G[kc] = tab_g[wave][32 * kc + l32];
             const uint2 m = tab_m[wave][32 * kc + l32];
             // Pair i of heads 32r + 2i, + 2i + 1 at bits i and 16 + i; this
             // lane's pairs start at 2 hf.
-            mw[kc][0] = m.x >> (2 * hf);
-            if constexpr (T::NRT > 1) mw[kc][1] = m.y >> (2 * hf);
+            tb.mw[kc][0] = m.x >> (2 * hf);
+            if constexpr (T::NRT > 1) tb.mw[kc][1] = m.y >> (2 * hf);
         }
-        // dk += A Q: A row = key 32 kc + lane%32, k = the 8 heads 32r + 16s +
-        // 8(jj/4) + 4hf + jj%4 of fragment hs = 2r + s; A = bf16(G w_h) where
-        // the head's mask bit is set, else 0; B the query's exact q.
+    };
+
+    // dk += A Q for one query: A row = key 32 kc + lane%32, k = the 8 heads
+    // 32r + 16s + 8(jj/4) + 4hf + jj%4 of fragment hs = 2r + s; A = bf16(G w_h)
+    // where the head's mask bit is set, else 0; B the query's exact q.
+    auto products = [&](const uint8_t* st_base, const Tab& tb) {
+        if (tb.n == 0) return;
         const float* wl = reinterpret_cast<const float*>(st_base + WS + 4 * 64 * wave);
 #pragma unroll
         for (int r = 0; r < T::NRT; ++r)
@@ -645,8 +657,8 @@ __global__ __launch_bounds__(256, 2) void dk_entries_kernel(const uint16_t* __re
                         // heads 32r + 16 sst + 8(p/2) + 4hf + 2(p%2) and + 1: pair
                         // 8 sst + 4(p/2) + 2hf + p%2, at bits ip and 16 + ip of mw.
                         const int ip = 8 * sst + 4 * (p >> 1) + (p & 1);
-                        av[p] = pack_bf16(G[kc] * wv[2 * p], G[kc] * wv[2 * p + 1]) &
-                                half_masks(mw[kc][r] << (15 - ip));
+                        av[p] = pack_bf16(tb.G[kc] * wv[2 * p], tb.G[kc] * wv[2 * p + 1]) &
+                                half_masks(tb.mw[kc][r] << (15 - ip));
                     }
                     const bf16x8 af = as_bf16x8(av);
 #pragma unroll
@@ -662,20 +674,32 @@ __global__ __launch_bounds__(256, 2) void dk_entries_kernel(const uint16_t* __re
         __builtin_amdgcn_s_barrier();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
     };
-    auto iter = [&](int t, const uint8_t* cur, uint8_t* ahead2) {
-        if (t + 2 < t1) stage(t + 2, ahead2);
-        compute(t, cur);
-        wait_and_barrier(t + 2 < t1);
+    // Per query t: stage t + 2, the products of t, the table of t + 1 (from
+    // the wave's own bucket loads of stage t + 1, complete once at most the
+    // stage t + 2 loads are outstanding), then one barrier.
+    Tab tb;
+    auto iter = [&](int t, const uint8_t* cur, const uint8_t* next, uint8_t* ahead2) {
+        const bool more = t + 2 < t1;
+        if (more) stage(t + 2, ahead2);
+        products(cur, tb);
+        if (t + 1 < t1) {
+            if (more) __builtin_amdgcn_s_waitcnt(wait_vmcnt(PER_WAVE));
+            else __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            prep(t + 1, next, tb);
+        }
+        wait_and_barrier(more);
     };
     stage(t0, lds0);
     if (t0 + 1 < t1) stage(t0 + 1, lds1);
     wait_and_barrier(t0 + 1 < t1);
+    prep(t0, lds0, tb);
     for (int t = t0; t < t1; t += 3) {
-        iter(t, lds0, lds2);
+        iter(t, lds0, lds1, lds2);
         if (t + 1 >= t1) break;
-        iter(t + 1, lds1, lds0);
+        iter(t + 1, lds1, lds2, lds0);
         if (t + 2 >= t1) break;
-        iter(t + 2, lds2, lds1);
+        iter(t + 2, lds2, lds0, lds1);
     }
 
     // dk rows of the wave's keys: key s_wave + 32kc + c_row(i, hf), index_dim
