@@ -208,8 +208,8 @@ CSRC = os.path.join(ROOT, "sparse_attention_lightning_bf16_amd", "csrc")
 # Translation unit of each kernel whose traffic the summary records.
 KERNEL_UNITS = {"v4_logits_kernel": "score.hip", "v41_scores_kernel": "score.hip", "v4_fused_topk_kernel": "fused.hip",
                 "topk_rows_bin_kernel": "topk.hip", "gather_kernel": "topk.hip", "sparse_scores_kernel": "sparse.hip",
-                "qt_fragments_kernel": "backward.hip", "backward_rows_kernel": "backward.hip",
-                "bucket_entries_kernel": "backward.hip", "dk_entries_kernel": "backward.hip"}
+                "backward_rows_kernel": "backward.hip", "bucket_entries_kernel": "backward.hip",
+                "dk_entries_kernel": "backward.hip"}
 
 
 def source_digest(unit):
