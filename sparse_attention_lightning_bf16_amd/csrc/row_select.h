@@ -17,6 +17,9 @@
 namespace lix {
 
 constexpr int kBins = 2048;
+// Word 3 of a raw buffer resource on gfx9 (32-bit data format; the range
+// check against num_records is on).
+constexpr int kBufWord3 = 0x00020000;
 
 // Inclusive prefix sum over the 64 lanes with DPP moves (no LDS): shifts by
 // 1, 2, 4, 8 inside each row of 16 lanes, then the totals of rows 0 and 2
@@ -282,19 +285,29 @@ __device__ __forceinline__ void select_row_binned(const RowIn<BF16>* __restrict_
             }
         });
     } else {
-        // Every slot is loaded, at an address clamped into the row (n > topk
-        // >= 1 here), with no branch between the loads, so all of them are in
-        // flight before the first is used (loads under per-chunk branches are
-        // waited for chunk by chunk); slots past the row then become NaN.
+        // Every slot is loaded with no branch between the loads, so all of
+        // them are in flight before the first is used (loads under per-chunk
+        // branches are waited for chunk by chunk): raw buffer loads over the
+        // row's n scores (n > topk >= 1 here), whose range check returns 0
+        // for a slot past the row, at one per-lane offset per chunk and the
+        // slot's 64-key step as the instruction's offset.  Then the slots past
+        // the row become NaN, in the chunks that reach past it (a uniform test
+        // per chunk).
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<In*>(row), (short)0, n * (int)sizeof(float), kBufWord3);
         static_for<0, NCH>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
+            const int vo = 4 * key_of(j, 0);
 #pragma unroll
-            for (int m = 0; m < 4; ++m) x[j][m] = row[min(key_of(j, m), n - 1)];
+            for (int m = 0; m < 4; ++m)
+                x[j][m] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, vo + 256 * m, 0, 0));
         });
         static_for<0, NCH>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
+            if ((NW * j + wv + 1) * 256 > n) {
 #pragma unroll
-            for (int m = 0; m < 4; ++m) x[j][m] = pick(key_of(j, m) < n, x[j][m], qnan);
+                for (int m = 0; m < 4; ++m) x[j][m] = pick(key_of(j, m) < n, x[j][m], qnan);
+            }
         });
     }
 
