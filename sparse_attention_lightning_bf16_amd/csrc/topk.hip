@@ -559,14 +559,35 @@ __global__ __launch_bounds__(64 * NW) void topk_rows_bin_kernel(const void* __re
     select_row_binned<NCH, BF16, NW>(row, hi - lo, lo, topk, so, io, sh, threadIdx.x);
 }
 
+// Scores at given indices: one workgroup per row (rows blockIdx.x,
+// blockIdx.x + gridDim.x, ...); each thread takes eight of the row's entries
+// 256 apart, their index loads and then their gathers all in flight at once.
+constexpr int kGatherUnroll = 8;
 __global__ __launch_bounds__(256) void gather_kernel(const float* __restrict__ logits,
-                                                     const int32_t* __restrict__ idx, long total, int skv,
+                                                     const int32_t* __restrict__ idx, long rows, int skv,
                                                      int topk, float* __restrict__ out) {
-    const long i = (long)blockIdx.x * 256 + threadIdx.x;
-    if (i >= total) return;
-    const long row = i / topk;
-    const int v = idx[i];
-    out[i] = (v >= 0 && v < skv) ? logits[row * skv + v] : neg_inf();
+    const int tid = threadIdx.x;
+    for (long row = blockIdx.x; row < rows; row += gridDim.x) {
+        const float* lrow = logits + row * skv;
+        const int32_t* irow = idx + row * topk;
+        float* orow = out + row * topk;
+        for (int j0 = 0; j0 < topk; j0 += 256 * kGatherUnroll) {
+            int v[kGatherUnroll];
+#pragma unroll
+            for (int u = 0; u < kGatherUnroll; ++u) {
+                const int j = j0 + 256 * u + tid;
+                v[u] = irow[min(j, topk - 1)];
+            }
+            float r[kGatherUnroll];
+#pragma unroll
+            for (int u = 0; u < kGatherUnroll; ++u) r[u] = lrow[min(max(v[u], 0), skv - 1)];
+#pragma unroll
+            for (int u = 0; u < kGatherUnroll; ++u) {
+                const int j = j0 + 256 * u + tid;
+                if (j < topk) orow[j] = (v[u] >= 0 && v[u] < skv) ? r[u] : neg_inf();
+            }
+        }
+    }
 }
 
 template <int VEC, int WPR, int MINB>
@@ -623,9 +644,9 @@ hipError_t launch_topk_bf16(const TopkBf16Args& p) {
 }
 
 hipError_t launch_gather(const GatherArgs& p) {
-    const long total = (long)p.B * p.S * p.topk;
-    dim3 grid((unsigned)((total + 255) / 256));
-    hipLaunchKernelGGL(gather_kernel, grid, dim3(256), 0, p.stream, p.logits, p.indices, total, p.Skv, p.topk,
+    const long rows = (long)p.B * p.S;
+    dim3 grid((unsigned)(rows < (1L << 20) ? rows : (1L << 20)));
+    hipLaunchKernelGGL(gather_kernel, grid, dim3(256), 0, p.stream, p.logits, p.indices, rows, p.Skv, p.topk,
                        p.scores);
     return hipGetLastError();
 }
