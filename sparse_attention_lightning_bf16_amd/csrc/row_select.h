@@ -269,12 +269,15 @@ __device__ __forceinline__ void select_row_binned(const RowIn<BF16>* __restrict_
 #pragma unroll
             for (int m = 0; m < 4; ++m) x[decltype(jc)::value][m] = qnan;   // chunks past the row
         });
-        visit_chunks<NCH, false>(jmax, jpart, [&](int j, auto partial) {
+        // (Raw buffer loads over the row's n scores: a slot past the row reads
+        // 0 and is made NaN below.)
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(row)), (short)0, n * 2, kBufWord3);
+        visit_chunks<NCH, false>(jmax, jpart, [&](int j, auto) {
+            const int vo = 2 * key_of(j, 0);
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int e = key_of(j, m);
-                x[j][m] = __uint_as_float((uint32_t)row[decltype(partial)::value ? min(e, n - 1) : e]);
-            }
+            for (int m = 0; m < 4; ++m)
+                x[j][m] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, vo + 128 * m, 0, 0));
         });
         visit_chunks<NCH, true>(jmax, jpart, [&](int j, auto) {
             const bool partial = j == jpart;
