@@ -475,14 +475,14 @@ __device__ __forceinline__ int q_swizzle(int h) {
 // A workgroup owns 256 keys (64 per wave: wave w owns bucket 4 kg + w) and
 // streams the queries of one chunk that can see them.  Per query, through a
 // three-stage rotation of LDS buffers (one barrier per query), it moves in by
-// direct loads the query's q rows (16-byte chunks in q_swizzle order), one
-// copy of its head weights per wave and
-// each wave's bucket of entries (up to 64; more only with repeated keys).  A
-// wave builds a 64-slot table of its keys (summed g and ReLU masks, from the
-// rows kernel's recompute) and forms the dk A operand bf16(G w_h) where m_h,
-// else 0, for the heads of the B fragments, which transposing LDS reads take
-// from the q rows: the product needs no recompute of q . k.  dk stays in
-// registers; the workgroup's partial is added to dk once at the end.
+// direct loads the query's q rows (16-byte chunks in q_swizzle order) and
+// each wave's bucket of entries (up to 64; more only with repeated keys), and
+// writes the query's head weights in a replicated layout.  A wave builds a
+// 64-slot table of its keys (summed g and ReLU masks, from the rows kernel's
+// recompute) and forms the dk A operand bf16(G w_h) where m_h, else 0, for the
+// heads of the B fragments, which transposing LDS reads take from the q rows
+// (as they take the weights): the product needs no recompute of q . k.  dk
+// stays in registers; the workgroup's partial is added to dk once at the end.
 template <int H, int DP>
 __global__ __launch_bounds__(256, 2) void dk_entries_kernel(const uint16_t* __restrict__ q,
                                                             const float* __restrict__ w,
@@ -494,9 +494,10 @@ __global__ __launch_bounds__(256, 2) void dk_entries_kernel(const uint16_t* __re
     using T = BwTiling<H, DP>;
     // Stage: q rows of heads 0 .. 32 NRT - 1 (rows past H repeat head H - 1,
     // chunks past index_dim repeat its last chunk: they meet zero A entries or
-    // feed dk columns that are not stored), per wave one copy of the head
-    // weights (64 floats; heads past H repeat w[H-1]) and the wave's bucket
-    // (64 entries of 16 bytes).
+    // feed dk columns that are not stored), the head weights in the layout the
+    // transposing reads below take them from (weight h at 16 h: its low 16
+    // bits four times, then its high 16 bits four times; heads past H repeat
+    // w[H-1]) and each wave's bucket (64 entries of 16 bytes).
     constexpr int CPK = DP / 8;                              // 16-byte chunks per head row
     constexpr int QBYTES = 32 * T::NRT * DP * 2;
     constexpr int QBLK = QBYTES / 1024;                      // 1 KiB direct loads (one per wave instruction)
@@ -508,7 +509,6 @@ __global__ __launch_bounds__(256, 2) void dk_entries_kernel(const uint16_t* __re
     __shared__ int offs[kQueryChunk][5];                    // bucket bounds of the chunk's queries
     __shared__ float tab_g[4][64];                          // per wave: summed g of its keys
     __shared__ uint2 tab_m[4][64];                          // per wave: ReLU masks of its keys (pair order)
-    constexpr int PER_WAVE = QBLK / 4 + 2;                  // vector-memory operations per stage and wave
     static_assert(QBLK % 4 == 0, "q blocks split over 4 waves");
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
@@ -548,9 +548,6 @@ __global__ __launch_bounds__(256, 2) void dk_entries_kernel(const uint16_t* __re
         for (int u = 0; u < QBLK / 4; ++u)
             __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(qrow + qofs[u]),
                                              (lds_ptr_t)(st_base + QT + (wave + 4 * u) * 1024), 16, 0, 0);
-        const float* wrow = w + ((long)t * B + b) * H;
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(wrow + min(lane, H - 1)),
-                                         (lds_ptr_t)(st_base + WS + 4 * 64 * wave), 4, 0, 0);
         // The wave's bucket: lane i carries entry beg + i (clamped into the
         // row's topk entries; lanes past the bucket are ignored where the
         // entries are read).
@@ -586,8 +583,7 @@ __global__ __launch_bounds__(256, 2) void dk_entries_kernel(const uint16_t* __re
 
     // The wave's table for one query: its 64 keys' summed g and ReLU masks,
     // built in LDS from its bucket and read back into registers (G, mw); n is
-    // the bucket's size.  It is built one query ahead, after the products of
-    // the current query are issued, so its LDS round trips overlap them.
+    // the bucket's size.  It is built one query ahead of the products.
     struct Tab {
         float G[2];
         uint32_t mw[2][T::NRT];
@@ -625,9 +621,23 @@ __global__ __launch_bounds__(256, 2) void dk_entries_kernel(const uint16_t* __re
     // dk += A Q for one query: A row = key 32 kc + lane%32, k = the 8 heads
     // 32r + 16s + 8(jj/4) + 4hf + jj%4 of fragment hs = 2r + s; A = bf16(G w_h)
     // where the head's mask bit is set, else 0; B the query's exact q.
+    // The weights of a stage: thread i loads weight i / 4 (one stage ahead)
+    // and writes LDS dword i of the replicated layout, its half (i / 2) % 2
+    // twice.
+    auto load_w = [&](int t) { return __float_as_uint(w[((long)t * B + b) * H + min(tid >> 2, H - 1)]); };
+    auto put_w = [&](uint32_t bits, uint8_t* st_base) {
+        const uint32_t h = ((tid >> 1) & 1) ? (bits >> 16) : (bits & 0xFFFFu);
+        *reinterpret_cast<uint32_t*>(st_base + WS + 4 * tid) = h | (h << 16);
+    };
+    // Weights by transposing reads: source lane 4a + b of a 16-lane group
+    // reads the 8 bytes at WS + 16 h + 8 a, which hold one half of weight h
+    // (a even: low, odd: high; h + 1 for a >= 2) four times, so every output
+    // lane receives weights h and h + 1 whole.  (Neither these reads nor the q
+    // reads are ordinary LDS loads for the compiler's wait-count pass, so the
+    // direct loads of the next stage in flight do not hold them up.)
+    const int wofs = WS + 8 * ((lane & 15) >> 2);
     auto products = [&](const uint8_t* st_base, const Tab& tb) {
         if (tb.n == 0) return;
-        const float* wl = reinterpret_cast<const float*>(st_base + WS + 4 * 64 * wave);
 #pragma unroll
         for (int r = 0; r < T::NRT; ++r)
 #pragma unroll
@@ -645,9 +655,14 @@ __global__ __launch_bounds__(256, 2) void dk_entries_kernel(const uint16_t* __re
                 }
                 float wv[8];
 #pragma unroll
-                for (int g4 = 0; g4 < 2; ++g4) {
-                    const float4 v4 = *reinterpret_cast<const float4*>(wl + 32 * r + 8 * (2 * sst + g4) + 4 * hf);
-                    wv[4 * g4 + 0] = v4.x; wv[4 * g4 + 1] = v4.y; wv[4 * g4 + 2] = v4.z; wv[4 * g4 + 3] = v4.w;
+                for (int k2 = 0; k2 < 4; ++k2) {
+                    // weights 32r + 8(2 sst + k2/2) + 4hf + 2(k2%2), + 1
+                    const int h = 32 * r + 8 * (2 * sst + (k2 >> 1)) + 4 * hf + 2 * (k2 & 1);
+                    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4*)(const_cast<uint8_t*>(st_base) + wofs + 16 * h));
+                    const f32x2 f = __builtin_bit_cast(f32x2, v);
+                    wv[2 * k2] = f[0];
+                    wv[2 * k2 + 1] = f[1];
                 }
 #pragma unroll
                 for (int kc = 0; kc < 2; ++kc) {
@@ -667,33 +682,44 @@ __global__ __launch_bounds__(256, 2) void dk_entries_kernel(const uint16_t* __re
             }
     };
 
-    auto wait_and_barrier = [&](bool more) {
-        if (!more) __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
-        else __builtin_amdgcn_s_waitcnt(wait_vmcnt(PER_WAVE));
+    auto drain_and_barrier = [&]() {
+        __builtin_amdgcn_s_waitcnt(0x0070);                    // vmcnt(0) lgkmcnt(0)
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_barrier();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
     };
-    // Per query t: stage t + 2, the products of t, the table of t + 1 (from
-    // the wave's own bucket loads of stage t + 1, complete once at most the
-    // stage t + 2 loads are outstanding), then one barrier.
+    // Per query t: the weights and the table of t + 1 (the bucket from stage
+    // t + 1, complete), then the weight and direct loads of stage t + 2, then
+    // the products of t (transposing reads and registers only), then a wait
+    // for every load in flight and a barrier: no ordinary LDS access runs
+    // while direct loads are outstanding, and the loads of stage t + 2 land
+    // during the products.
     Tab tb;
-    auto iter = [&](int t, const uint8_t* cur, const uint8_t* next, uint8_t* ahead2) {
-        const bool more = t + 2 < t1;
-        if (more) stage(t + 2, ahead2);
-        products(cur, tb);
+    uint32_t wn = 0;                                           // weight bits of the next stage
+    auto iter = [&](int t, const uint8_t* cur, uint8_t* next, uint8_t* ahead2) {
+        Tab tn;
+        tn.n = 0;
         if (t + 1 < t1) {
-            if (more) __builtin_amdgcn_s_waitcnt(wait_vmcnt(PER_WAVE));
-            else __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            prep(t + 1, next, tb);
+            put_w(wn, next);
+            prep(t + 1, next, tn);
         }
-        wait_and_barrier(more);
+        if (t + 2 < t1) {
+            wn = load_w(t + 2);
+            stage(t + 2, ahead2);
+        }
+        products(cur, tb);
+        tb = tn;
+        drain_and_barrier();
     };
     stage(t0, lds0);
     if (t0 + 1 < t1) stage(t0 + 1, lds1);
-    wait_and_barrier(t0 + 1 < t1);
+    const uint32_t w0 = load_w(t0);
+    if (t0 + 1 < t1) wn = load_w(t0 + 1);
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    put_w(w0, lds0);
     prep(t0, lds0, tb);
+    drain_and_barrier();
     for (int t = t0; t < t1; t += 3) {
         iter(t, lds0, lds1, lds2);
         if (t + 1 >= t1) break;
