@@ -17,8 +17,9 @@
 // element is accumulated with per-entry atomics, and every workspace array is
 // sized by the entries (B*S*topk) or by groups of 64 keys, never by B*S*Skv:
 //
-//   1. backward_rows_kernel (query-major, one wave per query and group of 32
-//      heads, the gathered 32-key blocks of the scores-at kernel): d^T = K Q^T
+//   1. backward_rows_kernel (query-major, one workgroup per query with one
+//      wave per group of 32 heads, over the gathered 32-key blocks of the
+//      scores-at kernel, which the waves share): d^T = K Q^T
 //      recomputed per block (lanes are heads, accumulator rows keys); dw += g
 //      relu(d^T) per lane; dq += (m g) K, whose A operand comes straight from
 //      d^T's accumulators and whose B operand is the gathered block read
@@ -50,7 +51,9 @@ namespace lix {
 
 namespace {
 
-constexpr int kBwWaitVmcnt0 = 0x0F70;     // s_waitcnt vmcnt(0), expcnt/lgkmcnt untouched
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left at their maxima).
+constexpr int wait_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 constexpr int kKeysPerGroup = 256;        // keys per dk workgroup (64 per wave)
 constexpr int kQueryChunk = 128;          // queries per dk workgroup
 
@@ -223,13 +226,104 @@ __global__ __launch_bounds__(256) void bucket_entries_kernel(const int32_t* __re
 
 // ---------------------------------------------------------------- dq, dw (query-major)
 
-// One wave per (query, group of up to 32 heads): the wave's dq accumulators
-// (32 x DP fp32) and q fragments leave room for two waves per SIMD.  The
-// waves of one query gather the same key blocks (from L2: k is small).
+// One workgroup per query, one wave per group of up to 32 heads: a wave's dq
+// accumulators (32 x DP fp32) and q fragments leave room for two waves per
+// SIMD, and the waves of a query share each gathered key block (each moves a
+// part of it).
 constexpr int rows_heads(int H) { return H > 32 ? 32 : H; }
+constexpr int rows_waves(int H) { return H > 32 ? H / 32 : 1; }
+
+// The loads ld = part * LPW .. part * LPW + LPW - 1 of gather_block (LPW =
+// NLOAD / NPART): one wave's share of a block that NPART waves gather
+// together.  The row of each load's lane comes from the lane that holds that
+// entry (s >= 0 on every lane).
+template <int DP, int NPART>
+__device__ __forceinline__ void gather_share(uint8_t* buf, const uint16_t* kb, long k_s, int dlim, int s, int lane,
+                                             int part) {
+    using M = BlockMap<DP>;
+    static_assert(M::NLOAD % NPART == 0, "block loads split evenly over the waves");
+    constexpr int LPW = M::NLOAD / NPART;
+    const int m = lane / M::SEG, cp = lane % M::SEG;
+#pragma unroll
+    for (int u = 0; u < LPW; ++u) {
+        const int ld = part * LPW + u;
+        const int p = M::RPI * ld + m;
+        const int row = __shfl(s, p & 31);
+        const int d8 = min(M::SEG * (p >> 5) + (cp ^ M::swz(ld, m)), dlim);
+        const uint16_t* src = kb + (uint64_t)(uint32_t)row * (uint32_t)k_s + 8 * d8;
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), (lds_ptr_t)(buf + ld * kWave * 16), 16,
+                                         0, 0);
+    }
+}
+
+// LDS reads issued from inline assembly, each statement waiting for its own
+// reads: the compiler's wait-count pass treats every ordinary LDS access as
+// possibly touching a buffer that direct loads are still filling and waits
+// for all of them; these reads (of buffers whose loads are known complete)
+// are not held up that way.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+__device__ __forceinline__ void lds_read4_b128(u32x4& v0, u32x4& v1, u32x4& v2, u32x4& v3, uint32_t a0,
+                                               uint32_t a1, uint32_t a2, uint32_t a3) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3)
+        : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+        : "memory");
+}
+__device__ __forceinline__ void lds_read3_b32(uint32_t& v0, uint32_t& v1, uint32_t& v2, uint32_t a0, uint32_t a1,
+                                              uint32_t a2) {
+    asm volatile(
+        "ds_read_b32 %0, %3\n\t"
+        "ds_read_b32 %1, %4\n\t"
+        "ds_read_b32 %2, %5\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v0), "=&v"(v1), "=&v"(v2)
+        : "v"(a0), "v"(a1), "v"(a2)
+        : "memory");
+}
+// Transposing reads (ds_read_b64_tr_b16) of N 8-byte pieces, N = 4 or 8.
+template <int N>
+__device__ __forceinline__ void lds_read_tr(i16x4 (&v)[N], const uint32_t (&a)[N]) {
+    static_assert(N == 4 || N == 8, "four or eight transposing reads");
+    if constexpr (N == 4) {
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %4\n\t"
+            "ds_read_b64_tr_b16 %1, %5\n\t"
+            "ds_read_b64_tr_b16 %2, %6\n\t"
+            "ds_read_b64_tr_b16 %3, %7\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+            : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+            : "memory");
+    } else {
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %8\n\t"
+            "ds_read_b64_tr_b16 %1, %9\n\t"
+            "ds_read_b64_tr_b16 %2, %10\n\t"
+            "ds_read_b64_tr_b16 %3, %11\n\t"
+            "ds_read_b64_tr_b16 %4, %12\n\t"
+            "ds_read_b64_tr_b16 %5, %13\n\t"
+            "ds_read_b64_tr_b16 %6, %14\n\t"
+            "ds_read_b64_tr_b16 %7, %15\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]),
+              "=&v"(v[7])
+            : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+            : "memory");
+    }
+}
+__device__ __forceinline__ void lds_write_b32(uint32_t a, float v) {
+    asm volatile("ds_write_b32 %0, %1" : : "v"(a), "v"(v) : "memory");
+}
 
 template <int H, int DP>
-__global__ __launch_bounds__(64, 2) void backward_rows_kernel(InLayout L, const float* __restrict__ w,
+__global__ __launch_bounds__(kWave * rows_waves(H), 2) void backward_rows_kernel(InLayout L, const float* __restrict__ w,
                                                              const int32_t* __restrict__ indices,
                                                              const float* __restrict__ grad, int B, int S, int skv,
                                                              int ratio, const int32_t* __restrict__ ks,
@@ -237,22 +331,25 @@ __global__ __launch_bounds__(64, 2) void backward_rows_kernel(InLayout L, const 
                                                              float* __restrict__ dq, float* __restrict__ dw,
                                                              uint32_t* __restrict__ masks) {
     constexpr int HW = rows_heads(H);                // heads of this wave: h0 .. h0 + HW - 1
-    constexpr int NHG = H / HW;                      // head groups per query
+    constexpr int NHG = H / HW;                      // head groups per query: the workgroup's waves
+    static_assert(NHG == rows_waves(H), "one wave per head group");
     using T = BwTiling<HW, DP>;
     using M = BlockMap<DP>;
+    constexpr int LPW = M::NLOAD / NHG;              // gather loads per wave and block
+    // Per block x (slot x % 3): the gathered keys, shared by the head groups,
+    // and per wave the block's indices (lanes 0-31) and gradients (32-63).
     __shared__ __attribute__((aligned(16))) uint8_t buf0[M::BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t buf1[M::BYTES];
-    __shared__ __attribute__((aligned(16))) float stage_g[32];
+    __shared__ __attribute__((aligned(16))) uint8_t buf2[M::BYTES];
+    __shared__ __attribute__((aligned(16))) uint32_t ig0[NHG][64];
+    __shared__ __attribute__((aligned(16))) uint32_t ig1[NHG][64];
+    __shared__ __attribute__((aligned(16))) uint32_t ig2[NHG][64];
+    __shared__ __attribute__((aligned(16))) float stage_g[NHG][32];
 
-    const int lane = threadIdx.x, hf = lane >> 5, l32 = lane & 31;
-    // The head groups of one query get flat ids 8 apart (groups of 8 rows):
-    // they go to the same XCD at about the same time and share the query's
-    // indices, gradients and key rows through its L2.
-    const int hq = (int)((blockIdx.x / kXcds) % NHG);
-    const long row_l = (long)(blockIdx.x / (kXcds * NHG)) * kXcds + blockIdx.x % kXcds;
-    if (row_l >= (long)B * S) return;                         // padding of the last group of 8 rows
+    const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
+    const int hq = __builtin_amdgcn_readfirstlane(tid >> 6);     // head group of this wave
     const int h0 = HW * hq;
-    const int row = (int)row_l;
+    const int row = blockIdx.x;                                  // t * B + b
     const int b = row % B, t = row / B;
     const int D = L.D;
     int lo, hi;
@@ -307,8 +404,6 @@ __global__ __launch_bounds__(64, 2) void backward_rows_kernel(InLayout L, const 
 
     // This lane's entry of block blk is 32 blk + lane%32 (clamped loads; the
     // entry number is checked where it is used).
-    auto load_idx = [&](int blk) { return irow[min(32 * blk + l32, topk - 1)]; };
-    auto load_g = [&](int blk) { return grow[min(32 * blk + l32, topk - 1)]; };
     auto visible = [&](int idx, int blk) { return 32 * blk + l32 < topk && idx >= lo && idx < hi; };
 
     f32x16 dqacc[T::NRT][T::NDT];
@@ -326,22 +421,36 @@ __global__ __launch_bounds__(64, 2) void backward_rows_kernel(InLayout L, const 
 #pragma unroll
         for (int r = 0; r < T::NRT; ++r) acct[r] = f32x16{};
         __builtin_amdgcn_sched_barrier(0);
+        static_assert(T::NSTEP % 4 == 0, "key fragments read four at a time");
 #pragma unroll
-        for (int st = 0; st < T::NSTEP; ++st) {
-            const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(buf + fofs[st % M::KR] + 4096 * (st / M::KR)));
+        for (int s4 = 0; s4 < T::NSTEP; s4 += 4) {
+            u32x4 kv[4];
+            uint32_t ka[4];
 #pragma unroll
-            for (int r = 0; r < T::NRT; ++r) acct[r] = mfma_32x32x16(kf, a[r][st], acct[r]);
+            for (int u = 0; u < 4; ++u) {
+                const int st = s4 + u;
+                ka[u] = lds_addr(buf + fofs[st % M::KR] + 4096 * (st / M::KR));
+            }
+            lds_read4_b128(kv[0], kv[1], kv[2], kv[3], ka[0], ka[1], ka[2], ka[3]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int r = 0; r < T::NRT; ++r) acct[r] = mfma_32x32x16(as_bf16x8(kv[u]), a[r][s4 + u], acct[r]);
         }
         __builtin_amdgcn_sched_barrier(0);
         // g of the entries on this lane's accumulator rows (row i is entry
         // 32 blk + c_row(i, hf)), through LDS; invalid entries get 0.  One
         // wave: its LDS operations run in order, no barrier needed.
-        if (hf == 0) stage_g[l32] = vis ? g_own : 0.0f;
+        if (hf == 0) lds_write_b32(lds_addr(&stage_g[hq][l32]), vis ? g_own : 0.0f);
         float gv[16];
+        {
+            u32x4 gg[4];
+            lds_read4_b128(gg[0], gg[1], gg[2], gg[3], lds_addr(&stage_g[hq][4 * hf]), lds_addr(&stage_g[hq][8 + 4 * hf]),
+                           lds_addr(&stage_g[hq][16 + 4 * hf]), lds_addr(&stage_g[hq][24 + 4 * hf]));
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const float4 gg = *reinterpret_cast<const float4*>(stage_g + 8 * q4 + 4 * hf);
-            gv[4 * q4 + 0] = gg.x; gv[4 * q4 + 1] = gg.y; gv[4 * q4 + 2] = gg.z; gv[4 * q4 + 3] = gg.w;
+            for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) gv[4 * q4 + e] = __uint_as_float(gg[q4][e]);
         }
         // ReLU masks of the block's entries for this wave's heads, for the dk
         // kernel: bit l of entry (32 blk + k) = d of head h0 + l > 0, where
@@ -373,14 +482,19 @@ __global__ __launch_bounds__(64, 2) void backward_rows_kernel(InLayout L, const 
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             bf16x8 kt[T::NDT];
+            {
+                i16x4 part[2 * T::NDT];
+                uint32_t pa[2 * T::NDT];
 #pragma unroll
-            for (int dt = 0; dt < T::NDT; ++dt) {
-                i16x4 part[2];
+                for (int dt = 0; dt < T::NDT; ++dt)
 #pragma unroll
-                for (int rd = 0; rd < 2; ++rd)
-                    part[rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(
-                        const_cast<uint8_t*>(buf) + tbase[dt & 1][rd] + 1024 * (4 * (dt >> 1) + 2 * s + rd)));
-                kt[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+                    for (int rd = 0; rd < 2; ++rd)
+                        pa[2 * dt + rd] = lds_addr(buf + tbase[dt & 1][rd] + 1024 * (4 * (dt >> 1) + 2 * s + rd));
+                lds_read_tr<2 * T::NDT>(part, pa);
+#pragma unroll
+                for (int dt = 0; dt < T::NDT; ++dt)
+                    kt[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[2 * dt], part[2 * dt + 1], 0, 1, 2,
+                                                                                3, 4, 5, 6, 7));
             }
 #pragma unroll
             for (int r = 0; r < T::NRT; ++r) {
@@ -397,26 +511,69 @@ __global__ __launch_bounds__(64, 2) void backward_rows_kernel(InLayout L, const 
         }
     };
 
-    // Block order per step: wait for every outstanding vector-memory operation
-    // (this block's gather and g, issued one step earlier), load the next
-    // block's g and the indices two blocks ahead, gather the next block into
-    // the other buffer, compute this block.  The explicit wait orders the LDS
-    // reads after the gather (one wave, no barrier).
-    int idx_c = load_idx(0), idx_n = load_idx(1);
-    float g_c = load_g(0);
-    bool act_c = __ballot(visible(idx_c, 0)) != 0ull;
-    if (act_c) gather_block<DP>(buf0, kb, L.k_s, dlim, visible(idx_c, 0) ? idx_c : 0, lane);
-    for (int blk = 0; blk < nb; ++blk) {
-        const uint8_t* cur = (blk & 1) ? buf1 : buf0;
-        uint8_t* other = (blk & 1) ? buf0 : buf1;
-        __builtin_amdgcn_s_waitcnt(kBwWaitVmcnt0);
+    // Blocks go through three slots (block x in slot x % 3): each wave moves
+    // the block's indices and gradients into its own part of the slot three
+    // blocks ahead, and its share of the gathered keys two blocks ahead.
+    // Every step issues the same loads (invisible entries and the blocks past
+    // the row gather key row 0; the index loads are clamped into the row), in
+    // this order: the indices and gradients of block blk + 3, then the share of
+    // block blk + 2.  At step blk's start, then, waiting until at most LPW of
+    // this wave's vector-memory operations are outstanding completes its
+    // indices of block blk + 2 and its share of block blk (the share of block
+    // blk + 1 may stay in flight); a barrier covers the other waves' shares
+    // and puts every wave past its products on the buffer refilled next.
+    // Steps come in threes with fixed buffers, so the compiler sees which
+    // buffer each read and each direct load touches; no value read from
+    // global memory crosses a step in a register.
+    auto load_ig = [&](int blk, uint32_t (*ig)[64]) {
+        const int j = min(32 * blk + l32, topk - 1);
+        const void* src = hf ? reinterpret_cast<const void*>(grow + j) : reinterpret_cast<const void*>(irow + j);
+        __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(&ig[hq][0]), 4, 0, 0);
+    };
+    auto gather = [&](int blk, int idx, uint8_t* buf) {
+        gather_share<DP, NHG>(buf, kb, L.k_s, dlim, visible(idx, blk) ? idx : 0, lane, hq);
+    };
+    // (The wait and barrier that open a step end the one before it, and the
+    // prologue, so every path into a step has waited the same way.)
+    auto wait_and_barrier = [&]() {
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        const float g_n = load_g(blk + 1);
-        const int idx_nn = load_idx(blk + 2);
-        const bool act_n = (blk + 1 < nb) && __ballot(visible(idx_n, blk + 1)) != 0ull;
-        if (act_n) gather_block<DP>(other, kb, L.k_s, dlim, visible(idx_n, blk + 1) ? idx_n : 0, lane);
-        if (act_c) compute(blk, cur, g_c, visible(idx_c, blk));
-        idx_c = idx_n; act_c = act_n; idx_n = idx_nn; g_c = g_n;
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(LPW));
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    };
+    auto step = [&](int blk, uint32_t (*ig_c)[64], uint32_t (*ig_2)[64], const uint8_t* cur, uint8_t* ahead2) {
+        uint32_t i2u, icu, gcu;
+        lds_read3_b32(i2u, icu, gcu, lds_addr(&ig_2[hq][l32]), lds_addr(&ig_c[hq][l32]), lds_addr(&ig_c[hq][32 + l32]));
+        const int idx2 = (int)i2u, idx_c = (int)icu;
+        const float g_c = __uint_as_float(gcu);
+        // (The slot of block blk takes block blk + 3's indices after those reads.)
+        load_ig(blk + 3, ig_c);
+        gather(blk + 2, idx2, ahead2);
+        const bool vis = visible(idx_c, blk);
+        if (__ballot(vis) != 0ull) compute(blk, cur, g_c, vis);
+        wait_and_barrier();
+    };
+    load_ig(0, ig0);
+    load_ig(1, ig1);
+    load_ig(2, ig2);
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    {
+        uint32_t i0, i1, g0;
+        lds_read3_b32(i0, i1, g0, lds_addr(&ig0[hq][l32]), lds_addr(&ig1[hq][l32]), lds_addr(&ig0[hq][32 + l32]));
+        gather(0, (int)i0, buf0);
+        gather(1, (int)i1, buf1);
+        // (g0 is read again by step 0; reading it here keeps every output of
+        // the statement used.)
+        asm volatile("" : : "v"(g0));
+    }
+    wait_and_barrier();
+    for (int blk = 0; blk < nb; blk += 3) {
+        step(blk, ig0, ig2, buf0, buf2);
+        if (blk + 1 >= nb) break;
+        step(blk + 1, ig1, ig0, buf1, buf0);
+        if (blk + 2 >= nb) break;
+        step(blk + 2, ig2, ig1, buf2, buf1);
     }
 
     // dq = w * accumulated (m g) K: rows are heads 32r + c_row(i, hf), columns
@@ -446,10 +603,6 @@ __global__ __launch_bounds__(64, 2) void backward_rows_kernel(InLayout L, const 
 }
 
 // ---------------------------------------------------------------- dk (key-major)
-
-// s_waitcnt immediate that waits until at most n vector-memory operations of
-// this wave are outstanding (expcnt and lgkmcnt left at their maxima).
-constexpr int wait_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 
@@ -765,8 +918,7 @@ static hipError_t launch_backward_t(const BackwardArgs& p) {
     const int nhg = H / rows_heads(H);
     const int ngroups = (p.Skv + 63) / 64;
     if (ngroups > 512) return hipErrorInvalidValue;          // the bucket kernel's prefix covers 512 buckets
-    const unsigned rows8 = (rows + kXcds - 1) / kXcds * kXcds;
-    hipLaunchKernelGGL((backward_rows_kernel<H, DP>), dim3(rows8 * (unsigned)nhg), dim3(kWave), 0, p.stream, L, p.w,
+    hipLaunchKernelGGL((backward_rows_kernel<H, DP>), dim3(rows), dim3(kWave * rows_waves(H)), 0, p.stream, L, p.w,
                        p.indices, p.grad, p.B, p.S, p.Skv, p.ratio, p.ks, p.ke, p.topk, p.dq, p.dw, masks);
     hipLaunchKernelGGL(bucket_entries_kernel, dim3(rows), dim3(256), (size_t)(ngroups + 1) * 4, p.stream, p.indices,
                        p.grad, masks, nhg, p.S, p.Skv, p.ratio, p.ks, p.ke, p.topk, ngroups, off, ent);
