@@ -6,10 +6,12 @@
 A step is one forward of the V4 lightning indexer on the 32K workload
 (batch 1, seqlen 32768, seqlen_kv 8192, 64 heads, index_dim 128,
 compress_ratio 4, topk 2048): causally masked scoring of every valid
-(query, key) pair plus the per-query top-k.  Two routes compute it and both
-are timed on the same inputs: lix_topk's fused path (no logits in HBM) and
-the materialized path (lix_indexer_logits, then lix_topk over the logits);
-the step is the faster one, named in config.path.  Each timing is the median
+(query, key) pair plus the per-query top-k.  Four routes compute it and all
+are timed on the same inputs: lix_topk's fused path (no logits in HBM),
+lix_topk_streaming, the materialized path (lix_indexer_logits, then lix_topk
+over the logits) and the same over the visible logits only
+(lix_indexer_logits_visible, which leaves the hidden positions unwritten);
+the step is the fastest, named in config.path.  Each timing is the median
 of K launches bracketed by HIP events on the stream the library launches on,
 after W untimed warm-ups; inputs are resident in HBM before timing starts.
 
@@ -29,7 +31,7 @@ Prints one JSON line.  `value` is causally valid TFLOP/s (2*H*D per visible
 pair) over the whole step; queries/s are reported beside it.
 
 --part NAME launches only one kernel's call in a loop (for profiler runs) and
-prints its median duration: logits, topk, fused, streaming, gather,
+prints its median duration: logits, logits_visible, topk, fused, streaming, gather,
 scores_at, backward, v41, topk_bf16, copy; --workload 131k runs it on the
 131K workload instead of the 32K one.
 """
@@ -53,7 +55,7 @@ METRIC = "indexer TFLOP/s (causal-valid) + queries/s incl. top-k, 32K ctx, 1 MI3
 PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, published
 TRAFFIC_SUMMARY = "profiles/hbm_traffic_32k_workload.md"
-PARTS = ("logits", "topk", "fused", "streaming", "gather", "scores_at", "backward", "v41", "topk_bf16", "copy")
+PARTS = ("logits", "logits_visible", "topk", "fused", "streaming", "gather", "scores_at", "backward", "v41", "topk_bf16", "copy")
 
 
 def log(msg):
@@ -147,7 +149,8 @@ def measured_peaks(dev, steps, warmup):
 # ---------------------------------------------------------------- other workloads
 
 def extra_workloads(dev, steps, warmup, flush):
-    """4K materialized, fused and streaming steps warm and cold; the 131K fused and materialized steps."""
+    """4K materialized, fused and streaming steps warm and cold; the 131K fused and materialized steps
+    (full and visible-only logits)."""
     out = {}
     cfg = synth.WORKLOADS["4k"]
     inp = synth.v4_inputs(**cfg)
@@ -199,6 +202,16 @@ def extra_workloads(dev, steps, warmup, flush):
     out["131k_materialized_topk_ms"] = tk_ms
     out["131k_materialized_tflops"] = 2.0 * cfg["heads"] * cfg["index_dim"] * pairs / ms_m / 1e9
     out["131k_fused_equals_materialized"] = bool(torch.equal(ix_m, ix_f) and torch.equal(sc_m, sc_f))
+    del sc_m, ix_m
+
+    def step131k_visible():                    # the same buffer: hidden positions are never read
+        lx.indexer_logits(q, k, w, c, out=logits, visible_only=True)
+        return lx.topk_from_logits(logits, c, tk)
+    out["131k_visible_logits_ms"] = median_ms(lambda: lx.indexer_logits(q, k, w, c, out=logits, visible_only=True),
+                                              n, 2)
+    out["131k_visible_step_ms"] = median_ms(step131k_visible, n, 2)
+    sc_v, ix_v = step131k_visible()
+    out["131k_visible_equals_fused"] = bool(torch.equal(ix_v, ix_f) and torch.equal(sc_v, sc_f))
     return out
 
 
@@ -343,6 +356,8 @@ def profile_part(args, dev, q, k, w, cfg):
         lx.indexer_logits(q, k, w, c, out=logits)
         if part == "logits":
             fn = lambda: lx.indexer_logits(q, k, w, c, out=logits)
+        elif part == "logits_visible":
+            fn = lambda: lx.indexer_logits(q, k, w, c, out=logits, visible_only=True)
         elif part == "topk":
             fn = lambda: lx.topk_from_logits(logits, c, tk)
         else:
@@ -430,6 +445,18 @@ def main():
     topk_ms = median_ms(lambda: lx.topk_from_logits(logits, c, tk), args.steps, args.warmup)
     sc_m, ix_m = lx.topk_from_logits(logits, c, tk)
     same = bool(torch.equal(ix_m, ix_f) and torch.equal(sc_m, sc_f))
+    log("timing the materialized path over the visible logits only")
+    logits_v = torch.full_like(logits, float("nan"))             # hidden positions stay NaN: never read
+
+    def visible_step():
+        lx.indexer_logits(q, k, w, c, out=logits_v, visible_only=True)
+        return lx.topk_from_logits(logits_v, c, tk)
+    step_v_ms, step_v_mean = time_calls(visible_step, args.steps, args.warmup)
+    score_v_ms = median_ms(lambda: lx.indexer_logits(q, k, w, c, out=logits_v, visible_only=True), args.steps,
+                           args.warmup)
+    sc_v, ix_v = visible_step()
+    visible_same = bool(torch.equal(ix_v, ix_f) and torch.equal(sc_v, sc_f))
+    del logits_v, sc_v, ix_v
     log("timing both routes cold")
     step_m_cold = median_ms(materialized_step, args.steps, args.warmup, between=flush)
     fused_cold = median_ms(lambda: lx.topk(q, k, w, c, tk), args.steps, args.warmup, between=flush)
@@ -464,6 +491,11 @@ def main():
         "materialized_scoring_tflops": flop / score_ms / 1e9,
         "materialized_scoring_mfma_frac": flop / score_ms / 1e9 / PEAK_BF16_TFLOPS,
         "materialized_logits_store_gbs": logits_bytes / score_ms / 1e6,
+        "visible_step_ms": step_v_ms,
+        "visible_step_mean_ms": step_v_mean,
+        "visible_logits_ms": score_v_ms,
+        "visible_scoring_tflops": flop / score_v_ms / 1e9,
+        "visible_equals_fused": visible_same,
         "topk_from_logits_gbs": topk_bytes / topk_ms / 1e6,
         "topk_from_logits_hbm_frac": topk_bytes / topk_ms / 1e6 / PEAK_HBM_GBS,
         "topk_bytes": topk_bytes,
@@ -523,14 +555,16 @@ def main():
     del flush_buf
 
     del ws_s
-    # The step is the fastest of the three routes to the same forward; all are reported.
+    # The step is the fastest of the four routes to the same forward; all are reported.
     routes = [
         (step_m_ms, "materialized: lix_indexer_logits then lix_topk over the logits",
-         {"name": "v4_logits_kernel<64, 128, false>", "ms": score_ms}),
+         {"name": "v4_logits_kernel<64, 128, false, true>", "ms": score_ms}),
+        (step_v_ms, "materialized over the visible logits: lix_indexer_logits_visible then lix_topk",
+         {"name": "v4_logits_kernel<64, 128, false, false>", "ms": score_v_ms}),
         (fused_ms, "fused: lix_topk scoring and selecting on chip",
          {"name": "v4_fused_topk_kernel", "ms": fused_ms}),
         (stream_ms, "streaming: lix_topk_streaming, each query block selected right after it is scored",
-         {"name": "v4_logits_kernel<64, 128, true>", "ms": stream_ms}),
+         {"name": "v4_logits_kernel<64, 128, true, false>", "ms": stream_ms}),
     ]
     step_ms, path, roof_kernel = min(routes, key=lambda r: r[0])
     value = flop / step_ms / 1e9

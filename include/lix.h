@@ -99,6 +99,21 @@ int lix_indexer_logits(const void* q, const void* k, const float* w,
                        float* logits, hipStream_t stream);
 
 /*
+ * lix_indexer_logits_visible - the same logits at the visible positions only.
+ *
+ * As lix_indexer_logits (same pages, arguments, validation and errors), for
+ * callers that read only the positions inside each query's range, such as
+ * lix_topk over the buffer: every position inside [ks, ke) receives the same
+ * bits lix_indexer_logits writes there; a position outside holds -inf or
+ * keeps its previous contents (the key blocks no query of a block of queries
+ * sees are not written).  The buffer is otherwise the caller's, as above.
+ */
+int lix_indexer_logits_visible(const void* q, const void* k, const float* w,
+                               int B, int S, int Skv, int H, int D, int compress_ratio,
+                               const int32_t* ks, const int32_t* ke,
+                               float* logits, hipStream_t stream);
+
+/*
  * lix_topk - per-query top-k of the indexer scores.
  *
  * Page "...deepseek_v4.kernels.tilelang_indexer", sections v4_lighting_indexer

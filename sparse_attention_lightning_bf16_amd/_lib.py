@@ -23,6 +23,7 @@ SIGNATURES = {
     "lix_status_string": (ctypes.c_char_p, [_I]),
     "lix_version": (_I, []),
     "lix_indexer_logits": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P]),
+    "lix_indexer_logits_visible": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P]),
     "lix_topk": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P]),
     "lix_topk_fused_supported": (_I, [_I, _I, _I, _I]),
     "lix_topk_streaming": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P, _LL, _P]),

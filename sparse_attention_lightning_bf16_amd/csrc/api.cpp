@@ -103,9 +103,11 @@ const char* lix_status_string(int status) {
 
 int lix_version(void) { return kVersion; }
 
-int lix_indexer_logits(const void* q, const void* k, const float* w, int B, int S, int Skv, int H, int D,
-                       int compress_ratio, const int32_t* ks, const int32_t* ke, float* logits,
-                       hipStream_t stream) {
+namespace {
+
+int indexer_logits(const void* q, const void* k, const float* w, int B, int S, int Skv, int H, int D,
+                   int compress_ratio, const int32_t* ks, const int32_t* ke, float* logits, hipStream_t stream,
+                   int fill) {
     if (!q || !k || !w || !logits) return LIX_ERR_NULL;
     int st = check_dims_v4(B, S, Skv, H, D, compress_ratio, ks, ke);
     if (st != LIX_OK) return st;
@@ -114,8 +116,22 @@ int lix_indexer_logits(const void* q, const void* k, const float* w, int B, int 
         return LIX_ERR_UNSUPPORTED;
     st = check_device({q, k, w, logits, ks, ke});
     if (st != LIX_OK) return st;
-    lix::LogitsArgs a{q, k, w, B, S, Skv, H, D, compress_ratio, ks, ke, logits, stream};
+    lix::LogitsArgs a{q, k, w, B, S, Skv, H, D, compress_ratio, ks, ke, logits, stream, fill};
     return launch_status(lix::launch_v4_logits(a));
+}
+
+}  // namespace
+
+int lix_indexer_logits(const void* q, const void* k, const float* w, int B, int S, int Skv, int H, int D,
+                       int compress_ratio, const int32_t* ks, const int32_t* ke, float* logits,
+                       hipStream_t stream) {
+    return indexer_logits(q, k, w, B, S, Skv, H, D, compress_ratio, ks, ke, logits, stream, 1);
+}
+
+int lix_indexer_logits_visible(const void* q, const void* k, const float* w, int B, int S, int Skv, int H, int D,
+                               int compress_ratio, const int32_t* ks, const int32_t* ke, float* logits,
+                               hipStream_t stream) {
+    return indexer_logits(q, k, w, B, S, Skv, H, D, compress_ratio, ks, ke, logits, stream, 0);
 }
 
 int lix_topk(const void* q, const void* k, const float* w, const float* logits, int B, int S, int Skv, int H,

@@ -18,6 +18,7 @@ struct LogitsArgs {
     const int32_t* ke;
     float* logits;
     hipStream_t stream;
+    int fill;                 // 1: -inf at every position outside the ranges; 0: those not all written
 };
 
 struct TopkArgs {

@@ -36,7 +36,8 @@ __device__ __forceinline__ void load_weights_f32(float (&wr)[T::NRT][16], const 
 
 // SELECT = false (lix_indexer_logits): out is the [B,S,Skv] logits; each
 // workgroup handles one query block; positions outside the staged span are
-// filled with -inf.
+// filled with -inf when FILL (lix_indexer_logits_visible leaves them as
+// they are).
 // SELECT = true (lix_topk_streaming): out is the workspace, one slot of
 // QB rows of skv floats per workgroup; the grid is persistent (workgroup w
 // handles blocks sched_block(w, gridDim.x, i)), a block's scores go to the
@@ -49,7 +50,7 @@ constexpr int logits_wg_waves(int H, int DP, bool select) { return select ? 4 : 
 template <int H, int DP, bool SELECT>
 using LogitsTiling = Tiling<H, DP, default_kt(H, DP), logits_wg_waves(H, DP, SELECT)>;
 
-template <int H, int DP, bool SELECT>
+template <int H, int DP, bool SELECT, bool FILL = !SELECT>
 __global__ __launch_bounds__(kWave * logits_wg_waves(H, DP, SELECT), stage_min_waves(H, DP)) void v4_logits_kernel(InLayout L, const float* __restrict__ w, int B, int S,
                                                         int skv, int ratio, const int32_t* __restrict__ ks,
                                                         const int32_t* __restrict__ ke, float* __restrict__ out,
@@ -197,8 +198,9 @@ __global__ __launch_bounds__(kWave * logits_wg_waves(H, DP, SELECT), stage_min_w
             flush();
         }
         if constexpr (!SELECT) {
-            // -inf outside the staged span: no query of the block sees those keys.
-            for (int q = 0; q < T::QB; ++q) {
+            // -inf outside the staged span: no query of the block sees those keys
+            // (left out when only the visible logits are asked for).
+            for (int q = 0; q < T::QB && FILL; ++q) {
                 const int t = t0 + q;
                 if (t >= S) break;
                 float* row = out + row_off(t);
@@ -501,8 +503,12 @@ static hipError_t launch_v4_logits_t(const LogitsArgs& p) {
                static_cast<const uint16_t*>(p.k), (long)p.B * p.D, (long)p.D, p.D};
     const long nblk = (long)((p.S + T::QB - 1) / T::QB) * p.B;
     dim3 grid((unsigned)nblk);                 // one block per workgroup (see sched_block)
-    hipLaunchKernelGGL((v4_logits_kernel<H, DP, false>), grid, dim3(T::THREADS), 0, p.stream, L, p.w, p.B, p.S,
-                       p.Skv, p.ratio, p.ks, p.ke, p.logits, 0, nullptr, nullptr);
+    if (p.fill)
+        hipLaunchKernelGGL((v4_logits_kernel<H, DP, false, true>), grid, dim3(T::THREADS), 0, p.stream, L, p.w, p.B,
+                           p.S, p.Skv, p.ratio, p.ks, p.ke, p.logits, 0, nullptr, nullptr);
+    else
+        hipLaunchKernelGGL((v4_logits_kernel<H, DP, false, false>), grid, dim3(T::THREADS), 0, p.stream, L, p.w, p.B,
+                           p.S, p.Skv, p.ratio, p.ks, p.ke, p.logits, 0, nullptr, nullptr);
     return hipGetLastError();
 }
 

@@ -58,11 +58,15 @@ def _v4_shapes(q, k, w):
     return S, B, H, D, Skv
 
 
-def indexer_logits(q, k, weights, compress_ratio, cu_seqlen_ks=None, cu_seqlen_ke=None, out=None):
+def indexer_logits(q, k, weights, compress_ratio, cu_seqlen_ks=None, cu_seqlen_ke=None, out=None,
+                   visible_only=False):
     """lix_indexer_logits: q [S,B,H,D] bf16, k [Skv,B,D] bf16, weights [S,B,H] fp32 -> [B,S,Skv] fp32.
 
     Positions outside [ks, ke) (causal [0, (t+1)//compress_ratio) when no
-    ranges are given) hold -inf.
+    ranges are given) hold -inf.  visible_only=True calls
+    lix_indexer_logits_visible: the positions inside the ranges get the same
+    bits, the others hold -inf or keep out's previous contents (for readers of
+    the visible positions only, such as topk_from_logits).
     """
     S, B, H, D, Skv = _v4_shapes(q, k, weights)
     ks, ke = _ranges(cu_seqlen_ks, cu_seqlen_ke, S)
@@ -72,10 +76,11 @@ def indexer_logits(q, k, weights, compress_ratio, cu_seqlen_ks=None, cu_seqlen_k
         _need(out, "out", torch.float32, 3)
         if tuple(out.shape) != (B, S, Skv):
             raise ValueError("out must be [B, S, Skv]")
-    st = _lib.load().lix_indexer_logits(q.data_ptr(), k.data_ptr(), weights.data_ptr(), B, S, Skv, H, D,
-                                        int(compress_ratio), _ptr(ks), _ptr(ke), out.data_ptr(),
-                                        _stream(q.device))
-    _lib.check(st, "lix_indexer_logits")
+    lib = _lib.load()
+    fn = lib.lix_indexer_logits_visible if visible_only else lib.lix_indexer_logits
+    st = fn(q.data_ptr(), k.data_ptr(), weights.data_ptr(), B, S, Skv, H, D, int(compress_ratio), _ptr(ks),
+            _ptr(ke), out.data_ptr(), _stream(q.device))
+    _lib.check(st, "lix_indexer_logits_visible" if visible_only else "lix_indexer_logits")
     return out
 
 

@@ -93,6 +93,9 @@ int main() {
     EXPECT(logits(p, p, fp, INT_MAX, INT_MAX, INT_MAX, 128, 256, 4, nullptr, nullptr, fp), UNS);
     EXPECT(logits(p, p, fp, 131072, 8, 2, 64, 128, 4, nullptr, nullptr, fp), UNS);
     EXPECT(logits(p, p, fp, 1, 8, 2, 64, 128, 4, nullptr, nullptr, fp), DEV);
+    EXPECT(lix_indexer_logits_visible(nullptr, p, fp, 1, 8, 2, 64, 128, 4, nullptr, nullptr, fp, nullptr), NUL);
+    EXPECT(lix_indexer_logits_visible(p, p, fp, 1, 8, 2, 48, 128, 4, nullptr, nullptr, fp, nullptr), UNS);
+    EXPECT(lix_indexer_logits_visible(p, p, fp, 1, 8, 2, 64, 128, 4, nullptr, nullptr, fp, nullptr), DEV);
 
     // ---- lix_topk (fused and materialized)
     int32_t* op = P<int32_t>();

@@ -25,7 +25,8 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = lx.load()
     names = declared_functions()
-    assert set(names) == {"lix_status_string", "lix_version", "lix_indexer_logits", "lix_topk",
+    assert set(names) == {"lix_status_string", "lix_version", "lix_indexer_logits", "lix_indexer_logits_visible",
+                          "lix_topk",
                           "lix_topk_scores", "lix_indexer_scores_v41", "lix_indexer_scores_at", "lix_topk_bf16",
                           "lix_indexer_backward", "lix_indexer_backward_workspace_bytes",
                           "lix_topk_fused_supported", "lix_indexer_backward_noalloc", "lix_topk_streaming",
@@ -42,8 +43,10 @@ def test_status_strings():
     assert lx.load().lix_version() >= 100
 
 
-def logits_call(q=P, k=P, w=P, B=1, S=8, Skv=2, H=64, D=128, c=4, ks=None, ke=None, out=P):
-    return lx.load().lix_indexer_logits(q, k, w, B, S, Skv, H, D, c, ks, ke, out, None)
+def logits_call(q=P, k=P, w=P, B=1, S=8, Skv=2, H=64, D=128, c=4, ks=None, ke=None, out=P, visible=False):
+    lib = lx.load()
+    fn = lib.lix_indexer_logits_visible if visible else lib.lix_indexer_logits
+    return fn(q, k, w, B, S, Skv, H, D, c, ks, ke, out, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -57,8 +60,10 @@ def logits_call(q=P, k=P, w=P, B=1, S=8, Skv=2, H=64, D=128, c=4, ks=None, ke=No
     (dict(B=131072, S=8, D=128), UNSUP),           # key row stride B * index_dim = 2^24
     (dict(B=131071, S=8, D=128), DEVICE),          # just below: passes validation
 ])
-def test_indexer_logits_validation(kw, code):
-    assert logits_call(**kw) == code
+@pytest.mark.parametrize("visible", [False, True])
+def test_indexer_logits_validation(kw, code, visible):
+    # lix_indexer_logits_visible validates exactly as lix_indexer_logits
+    assert logits_call(**kw, visible=visible) == code
 
 
 def topk_call(q=P, k=P, w=P, logits=None, B=1, S=8, Skv=4, H=64, D=128, c=4, ks=None, ke=None, topk=2,

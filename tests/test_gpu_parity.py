@@ -112,6 +112,47 @@ def test_logits_leave_memory_around_the_output_untouched():
     assert bool((buf[:1024] == 12345.0).all()) and bool((buf[1024 + n:] == 12345.0).all())
 
 
+@pytest.mark.parametrize("H,D,B,S,Skv,c,given", [
+    (64, 128, 1, 256, 64, 4, False),
+    (64, 128, 3, 333, 100, 3, False),
+    (8, 32, 2, 40, 50, 1, False),
+    (64, 128, 2, 200, 150, 1, True),
+    (128, 256, 1, 90, 300, 1, True),
+])
+def test_visible_logits_equal_full_logits_inside_the_ranges(H, D, B, S, Skv, c, given):
+    inp, _ = v4_case(B, S, Skv, H, D, seed=31)
+    q, k, w = dev(inp["q"]), dev(inp["k"]), dev(inp["w"])
+    ks = ke = None
+    if given:
+        g = torch.Generator().manual_seed(32)
+        ks = torch.randint(-5, Skv + 10, (S,), generator=g, dtype=torch.int32)
+        ke = ks + torch.randint(-10, Skv, (S,), generator=g, dtype=torch.int32)
+        ke[::13] = 10_000
+        ks, ke = dev(ks), dev(ke)
+    full = lx.indexer_logits(q, k, w, c, ks, ke).cpu().numpy()
+    out = torch.full((B, S, Skv), 12345.0, dtype=torch.float32, device=DEV)
+    vis = lx.indexer_logits(q, k, w, c, ks, ke, out=out, visible_only=True).cpu().numpy()
+    lo, hi = ranges(S, Skv, c, ks, ke)
+    key = np.arange(Skv)
+    inside = (key[None, :] >= np.maximum(lo, 0)[:, None]) & (key[None, :] < np.minimum(hi, Skv)[:, None])
+    inside = np.broadcast_to(inside, vis.shape)
+    assert np.array_equal(vis.view(np.uint32)[inside], full.view(np.uint32)[inside])
+    rest = vis[~inside]
+    assert bool(np.all((rest == 12345.0) | (rest == -np.inf)))
+
+
+def test_topk_over_visible_logits_equals_the_full_route():
+    cfg = synth.WORKLOADS["4k"]
+    log("4k top-k over visible logits")
+    B, S, Skv, tk = cfg["batch"], cfg["seqlen"], cfg["seqlen_kv"], cfg["topk"]
+    inp, _ = v4_case(B, S, Skv, 64, 128, cfg["seed"])
+    q, k, w = dev(inp["q"]), dev(inp["k"]), dev(inp["w"])
+    sc_f, ix_f = lx.topk_from_logits(lx.indexer_logits(q, k, w, 4), 4, tk)
+    out = torch.full((B, S, Skv), float("nan"), dtype=torch.float32, device=DEV)
+    sc_v, ix_v = lx.topk_from_logits(lx.indexer_logits(q, k, w, 4, out=out, visible_only=True), 4, tk)
+    assert torch.equal(ix_v, ix_f) and torch.equal(sc_v.view(torch.int32), sc_f.view(torch.int32))
+
+
 # ------------------------------------------------------------------ top-k
 
 def _check_topk_vs_oracle(sc, ix, nb, b, rows, ks, ke, topk, tag):
@@ -208,6 +249,11 @@ def test_topk_causal_long_rows_across_the_kernel_split():
     sc_m, ix_m = lx.topk_from_logits(logits, c, tk)
     sc_f, ix_f = lx.topk(q, k, w, c, tk)
     assert torch.equal(ix_m, ix_f) and torch.equal(sc_m, sc_f)
+    # the same selection over logits that leave the hidden positions unwritten
+    vis = lx.indexer_logits(q, k, w, c, out=torch.full_like(logits, float("nan")), visible_only=True)
+    sc_v, ix_v = lx.topk_from_logits(vis, c, tk)
+    del vis
+    assert torch.equal(ix_v, ix_m) and torch.equal(sc_v.view(torch.int32), sc_m.view(torch.int32))
     ks, ke = oracle.causal_ranges(S, Skv, c)
     rows = np.array([0, 999, 1000, 8191, 8192, 16382, 16383, 16384, 16385, S - 1])
     lg = logits[0][torch.from_numpy(rows).to(DEV)].cpu().numpy().astype(np.float64)
