@@ -158,14 +158,14 @@ def select_topk(q, k, weights, compress_ratio, topk):
     """Top-k of the causal indexer scores by the route the library offers for these sizes without a
     [B,S,Skv] buffer where it can: the streaming kernel (lix_topk_streaming) for seqlen_kv <= 8192,
     else the fused kernel (lix_topk with no logits) where it holds the candidates on chip, else the
-    materialized route (lix_indexer_logits into a [B,S,Skv] fp32 buffer, then lix_topk over it).
-    Every route selects the same keys and returns the same bits."""
+    materialized route (lix_indexer_logits_visible into a [B,S,Skv] fp32 buffer, then lix_topk over
+    it). Every route selects the same keys and returns the same bits."""
     S, B, H, D, Skv = _v4_shapes(q, k, weights)
     if Skv <= STREAMING_MAX_SEQLEN_KV:
         return topk_streaming(q, k, weights, compress_ratio, topk)
     if fused_topk_supported(Skv, H, D, topk):
         return globals()["topk"](q, k, weights, compress_ratio, topk)
-    logits = indexer_logits(q, k, weights, compress_ratio)
+    logits = indexer_logits(q, k, weights, compress_ratio, visible_only=True)
     return topk_from_logits(logits, compress_ratio, topk)
 
 
