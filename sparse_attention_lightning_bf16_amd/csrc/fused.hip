@@ -264,8 +264,10 @@ __global__ __launch_bounds__(256) void v4_fused_topk_kernel(InLayout L, const fl
             for (int cb = 0; cb < T::NCB; ++cb)
 #pragma unroll
                 for (int j = 0; j < T::QW; ++j) part[cb][j] = 0.0f;
-            // same accumulation order as the materialized logits kernel
-            rolling_stage<T>(a, stage, lane, [&](int cb, const f32x16 (&acc)[T::NRT], int r, int i) {
+            // same accumulation order as the materialized logits kernel; column
+            // blocks past the wave's last visible key are left out
+            const int ncb = __builtin_amdgcn_readfirstlane(min(T::NCB, (wave_hi - s0 + 31) >> 5));
+            rolling_stage_first<T>(a, stage, lane, ncb, [&](int cb, const f32x16 (&acc)[T::NRT], int r, int i) {
                 part[cb][T::slot(r, i)] = fmaf(wr[r][i], relu(acc[r][i]), part[cb][T::slot(r, i)]);
             });
 #pragma unroll

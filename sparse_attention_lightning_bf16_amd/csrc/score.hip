@@ -183,7 +183,9 @@ __global__ __launch_bounds__(kWave * logits_wg_waves(H, DP, SELECT), stage_min_w
 #pragma unroll
                     for (int q = 0; q < T::QW; ++q) pend[cb][q] = 0.0f;
                 if (active) {
-                    rolling_stage<T>(a, stage, lane, [&](int cb, const f32x16 (&acc)[T::NRT], int r, int i) {
+                    // column blocks up to the wave's last visible key
+                    const int ncb = __builtin_amdgcn_readfirstlane(min(T::NCB, (wave_hi - s0 + 31) >> 5));
+                    rolling_stage_first<T>(a, stage, lane, ncb, [&](int cb, const f32x16 (&acc)[T::NRT], int r, int i) {
                         pend[cb][T::slot(r, i)] = fmaf(wr[r][i], relu(acc[r][i]), pend[cb][T::slot(r, i)]);
                     });
                     if constexpr (H >= 8) {

@@ -205,6 +205,33 @@ __device__ __forceinline__ void rolling_stage(const bf16x8 (&a)[T::NRT][T::NSTEP
             for (int i = st * PER; i < (st + 1) * PER; ++i) epi(T::NCB - 1, accp, r, i);
 }
 
+// The first NC column blocks of a T stage (same fragment layout).
+template <class T, int NC>
+struct FirstBlocks {
+    static constexpr int NRT = T::NRT;
+    static constexpr int NSTEP = T::NSTEP;
+    static constexpr int NCB = NC;
+};
+
+// rolling_stage over the stage's first ncb column blocks only (ncb wave-uniform,
+// 1 <= ncb): the blocks past it hold keys no query of the wave sees, so their
+// MFMAs and epilogue are left out.  Same element order within each block.
+template <class T, class Epi>
+__device__ __forceinline__ void rolling_stage_first(const bf16x8 (&a)[T::NRT][T::NSTEP], const uint8_t* stage,
+                                                    int lane, int ncb, Epi&& epi) {
+    static_assert(T::NCB <= 4, "partial stages are instantiated for up to three blocks");
+    if (ncb >= T::NCB) {
+        rolling_stage<T>(a, stage, lane, epi);
+    } else if constexpr (T::NCB > 1) {
+        if (ncb == 1) {
+            rolling_stage<FirstBlocks<T, 1>>(a, stage, lane, epi);
+        } else if constexpr (T::NCB > 2) {
+            if (ncb == 2) rolling_stage<FirstBlocks<T, 2>>(a, stage, lane, epi);
+            else if constexpr (T::NCB > 3) rolling_stage<FirstBlocks<T, 3>>(a, stage, lane, epi);
+        }
+    }
+}
+
 // One stage block by block: each 32-key column block's MFMA chains (B
 // fragments read one k-step ahead), then that block's epilogue, with no
 // second set of accumulators.  For kernels run at three or more waves per
