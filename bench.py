@@ -13,7 +13,9 @@ over the logits) and the same over the visible logits only
 (lix_indexer_logits_visible, which leaves the hidden positions unwritten);
 the step is the fastest, named in config.path.  Each timing is the median
 of K launches bracketed by HIP events on the stream the library launches on,
-after W untimed warm-ups; inputs are resident in HBM before timing starts.
+after about 60 ms of untimed calls (the clock's recovery from the host work
+between timings) and W untimed warm-ups; inputs are resident in HBM before
+timing starts.
 
 The same run also times, in `parts`: both routes cold (L2 and MALL flushed by
 a 1 GiB write before each call, outside the timed region); the gather at the
@@ -67,15 +69,41 @@ def causal_valid_pairs(S, Skv, c):
     return int(np.minimum((p + 1) // c, Skv).sum())
 
 
+SETTLE_MS = 60.0      # untimed calls before each timing (see time_calls)
+_MARK = []
+
+
+def _mark():
+    """A one-element bitwise_not on the stream: brackets the timed calls in kernel traces."""
+    if not _MARK:
+        _MARK.append(torch.zeros(1, dtype=torch.int32, device="cuda"))
+    _MARK[0].bitwise_not_()
+
+
 def time_calls(fn, steps, warmup, between=None):
     """Median and mean duration (ms) of `steps` calls of fn, each bracketed by HIP events on torch's
-    current stream (the stream the library launches on); `between` runs untimed before each call."""
+    current stream (the stream the library launches on); `between` runs untimed before each call.
+
+    Before the `warmup` calls, fn runs untimed for about SETTLE_MS: after the host work between two
+    timings leaves the GPU idle, its clock needs some tens of milliseconds of load to come back (the
+    first ten or so calls of a route run up to 30% slower), longer than a few warm-up calls of a
+    2 ms step.  The timed calls are bracketed by two _mark() kernels for trace summaries."""
+    t0 = time.perf_counter()
+    for n in range(1, 4001):
+        if between is not None:
+            between()
+        fn()
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+            if (time.perf_counter() - t0) * 1e3 >= SETTLE_MS:
+                break
     for _ in range(warmup):
         if between is not None:
             between()
         fn()
     torch.cuda.synchronize()
     pairs = []
+    _mark()
     for _ in range(steps):
         if between is not None:
             between()
@@ -85,6 +113,7 @@ def time_calls(fn, steps, warmup, between=None):
         fn()
         e.record()
         pairs.append((s, e))
+    _mark()
     torch.cuda.synchronize()
     ms = np.array([s.elapsed_time(e) for s, e in pairs])
     return float(np.median(ms)), float(np.mean(ms))
