@@ -116,6 +116,8 @@ def test_logits_leave_memory_around_the_output_untouched():
     (64, 128, 1, 256, 64, 4, False),
     (64, 128, 3, 333, 100, 3, False),
     (8, 32, 2, 40, 50, 1, False),
+    (4, 16, 1, 61, 70, 1, False),       # heads < 8: per-slot stores of the lane halves
+    (1, 128, 2, 70, 66, 1, True),
     (64, 128, 2, 200, 150, 1, True),
     (128, 256, 1, 90, 300, 1, True),
 ])
