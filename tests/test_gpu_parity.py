@@ -131,16 +131,23 @@ def test_visible_logits_equal_full_logits_inside_the_ranges(H, D, B, S, Skv, c, 
         ke = ks + torch.randint(-10, Skv, (S,), generator=g, dtype=torch.int32)
         ke[::13] = 10_000
         ks, ke = dev(ks), dev(ke)
-    full = lx.indexer_logits(q, k, w, c, ks, ke).cpu().numpy()
-    out = torch.full((B, S, Skv), 12345.0, dtype=torch.float32, device=DEV)
-    vis = lx.indexer_logits(q, k, w, c, ks, ke, out=out, visible_only=True).cpu().numpy()
+    full_d = lx.indexer_logits(q, k, w, c, ks, ke)
+    # NaN where nothing is written: a reader of a hidden position would see it
+    out = torch.full((B, S, Skv), float("nan"), dtype=torch.float32, device=DEV)
+    vis_d = lx.indexer_logits(q, k, w, c, ks, ke, out=out, visible_only=True)
+    full, vis = full_d.cpu().numpy(), vis_d.cpu().numpy()
     lo, hi = ranges(S, Skv, c, ks, ke)
     key = np.arange(Skv)
     inside = (key[None, :] >= np.maximum(lo, 0)[:, None]) & (key[None, :] < np.minimum(hi, Skv)[:, None])
     inside = np.broadcast_to(inside, vis.shape)
     assert np.array_equal(vis.view(np.uint32)[inside], full.view(np.uint32)[inside])
     rest = vis[~inside]
-    assert bool(np.all((rest == 12345.0) | (rest == -np.inf)))
+    assert bool(np.all(np.isnan(rest) | (rest == -np.inf)))
+    # the row top-k over either buffer, with the same ranges
+    tk = min(16, Skv)
+    sc_f, ix_f = lx.topk_from_logits(full_d, c, tk, ks, ke)
+    sc_v, ix_v = lx.topk_from_logits(vis_d, c, tk, ks, ke)
+    assert torch.equal(ix_v, ix_f) and torch.equal(sc_v.view(torch.int32), sc_f.view(torch.int32))
 
 
 def test_topk_over_visible_logits_equals_the_full_route():
