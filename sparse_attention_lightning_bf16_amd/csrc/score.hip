@@ -8,9 +8,12 @@
 //     out[b,t,s] = bf16( sum_h bf16( w[b,t,h] * max(0, bf16(q[b,t,h,:] . k[b,s,:])) ) )
 // where allowed[b,t,s], bf16 -inf elsewhere; the head sum is fp32.
 //
-// One workgroup = 4 waves = QB consecutive queries of one batch element.
-// Key stages [s0, s0+KT) that lie outside every range of the workgroup are
-// never computed (causal tile skip); their logits are filled with -inf.
+// One workgroup = 4 or 8 waves (logits_wg_waves, v41_waves) = QB consecutive
+// queries of one batch element.  Key stages [s0, s0+KT) that lie outside
+// every range of the workgroup are never computed (causal tile skip); their
+// logits are filled with -inf, except by lix_indexer_logits_visible.  In the
+// stage holding a wave's last visible key, the 32-key column blocks past it
+// are left out as well.
 #include "score_core.h"
 #include "row_select.h"
 #include "launch.h"
